@@ -1,0 +1,520 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+CPU only.  Each test checks an oracle function against something other than
+itself: values printed on the pages (tests/golden/*.json, each citing its
+passage), closed forms, invariants, scalar-loop brute force on tiny inputs,
+or central finite differences of the oracle's own forward.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- partition
+
+def test_partition_page_examples():
+    g = golden("partition_examples.json")
+    for case in g["cases"]:
+        got = [list(O.partition(case["total"], case["n"], r)) for r in range(case["n"])]
+        assert got == case["shards"], case
+
+
+@pytest.mark.parametrize("total,n", [(7, 3), (50257, 8), (16, 4), (1, 2), (0, 3)])
+def test_partition_covers_exactly(total, n):
+    pos = 0
+    for r in range(n):
+        s, c = O.partition(total, n, r)
+        assert s == pos and c >= 0
+        pos += c
+    assert pos == total
+    counts = [O.partition(total, n, r)[1] for r in range(n)]
+    assert max(counts) - min(counts) <= 1
+
+
+# ---------------------------------------------------------------- embedding
+
+def test_masking_page_example():
+    g = golden("masking_example.json")
+    mask, local = O.vocab_embed_mask(g["ids"], g["start"], g["end"] - g["start"])
+    assert local.tolist() == g["masked"]
+    assert mask.tolist() == g["mask"]
+
+
+def test_embedding_worked_example():
+    g = golden("embedding_worked_example.json")
+    V, n, toks = g["vocab"], g["shards"], g["tokens"]
+    E = rng(1).standard_normal((V, 16)) + 3.0        # no zero rows by accident
+    parts = []
+    for r in range(n):
+        s, c = O.partition(V, n, r)
+        assert [s, s + c] == g["ranges"][r]
+        Y = O.vocab_embed_forward(toks, E[s:s + c], s)
+        found = [int(np.any(Y[t] != 0)) for t in range(len(toks))]
+        assert found == g["found"][r]
+        for t, tok in enumerate(toks):
+            if found[t]:
+                assert np.array_equal(Y[t], E[tok])
+            else:
+                assert np.all(Y[t] == 0)
+        parts.append(Y)
+    total = O.shard_reduce(parts)
+    assert [int(np.any(row != 0)) for row in total] == g["sum_found"]
+    # Special case: the shard sum is an ordinary gather from the full table.
+    assert np.array_equal(total, E[toks])
+
+
+def test_embedding_out_of_range_ids_are_zero():
+    E = rng(2).standard_normal((10, 4)) + 1
+    Y = O.vocab_embed_forward([-1, 10, 12, 3], E[0:5], 0)
+    assert np.all(Y[:3] == 0) and np.array_equal(Y[3], E[3])
+
+
+def _embed_backward_loop(ids, dY, start, rows):
+    dE = [[0.0] * dY.shape[1] for _ in range(rows)]
+    for t, tok in enumerate(ids):
+        if start <= tok < start + rows:
+            for c in range(dY.shape[1]):
+                dE[tok - start][c] += float(dY[t, c])
+    return np.array(dE)
+
+
+def test_embed_backward_bruteforce_and_identity():
+    g = rng(3)
+    V, H, T, n = 23, 5, 40, 3
+    ids = g.integers(-2, V + 2, T)
+    dY = g.standard_normal((T, H))
+    col_total = np.zeros(H)
+    for r in range(n):
+        s, c = O.partition(V, n, r)
+        dE = O.vocab_embed_backward(ids, dY, s, c)
+        assert np.allclose(dE, _embed_backward_loop(ids, dY, s, c), rtol=0, atol=1e-12)
+        col_total += dE.sum(axis=0)
+    inr = (ids >= 0) & (ids < V)
+    assert np.allclose(col_total, dY[inr].sum(axis=0), atol=1e-12)
+
+
+def test_embed_backward_finite_difference():
+    g = rng(4)
+    V, H, T = 9, 3, 12
+    ids = g.integers(0, V + 3, T)
+    E = g.standard_normal((V, H))
+    R = g.standard_normal((T, H))
+    s, c = O.partition(V, 2, 1)
+    dE = O.vocab_embed_backward(ids, R, s, c)
+    h = 1e-6
+    for j in range(c):
+        for k in range(H):
+            Ep, Em = E[s:s + c].copy(), E[s:s + c].copy()
+            Ep[j, k] += h
+            Em[j, k] -= h
+            fd = (np.sum(R * O.vocab_embed_forward(ids, Ep, s)) -
+                  np.sum(R * O.vocab_embed_forward(ids, Em, s))) / (2 * h)
+            assert abs(fd - dE[j, k]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_tied_gradient_is_sum_of_both_uses():
+    """Finite differences through both uses of the shared table pin the
+    'sum of the input-side and output-side gradients' rule."""
+    g = rng(5)
+    V, H, T, n = 7, 4, 6, 2
+    ids = g.integers(0, V, T)
+    E = g.standard_normal((V, H))
+    W = g.standard_normal((H, H))
+    R = [g.standard_normal((T, O.partition(V, n, r)[1])) for r in range(n)]
+
+    def loss(Ef):
+        x = O.shard_reduce([O.vocab_embed_forward(ids, Ef[s:s + c], s)
+                            for s, c in (O.partition(V, n, r) for r in range(n))])
+        hdn = x @ W
+        return sum(np.sum(R[r] * O.tied_logits(hdn, Ef[slice(*_rng(V, n, r))]))
+                   for r in range(n))
+
+    def _rng(V_, n_, r_):
+        s, c = O.partition(V_, n_, r_)
+        return s, s + c
+
+    x = O.shard_reduce([O.vocab_embed_forward(ids, E[s:s + c], s)
+                        for s, c in (O.partition(V, n, r) for r in range(n))])
+    hdn = x @ W
+    dE = np.zeros_like(E)
+    dh = []
+    for r in range(n):
+        s, c = O.partition(V, n, r)
+        dh_r, dE_out = O.tied_logits_backward(hdn, E[s:s + c], R[r])
+        dE[s:s + c] += dE_out
+        dh.append(dh_r)
+    dx = O.shard_reduce(dh) @ W.T
+    for r in range(n):
+        s, c = O.partition(V, n, r)
+        dE[s:s + c] += O.vocab_embed_backward(ids, dx, s, c)
+    h = 1e-6
+    for j in range(V):
+        for k in range(H):
+            Ep, Em = E.copy(), E.copy()
+            Ep[j, k] += h
+            Em[j, k] -= h
+            fd = (loss(Ep) - loss(Em)) / (2 * h)
+            assert abs(fd - dE[j, k]) <= 1e-6 * max(1.0, abs(fd)), (j, k)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_param_count_page_value():
+    g = golden("param_count.json")
+    assert O.param_count(g["H"], g["L"], g["V"]) == g["total"]
+    body = (12 * g["H"] ** 2 + 4 * g["H"]) * g["L"]
+    assert abs(body - g["body_approx"]) / g["body_approx"] < 0.01
+    assert O.param_count_tied_unique(g["H"], g["L"], g["V"]) == g["total"] - g["H"] * g["V"]
+
+
+def test_bf16_epsilon_page_value():
+    g = golden("format_epsilon.json")
+    assert O.bf16_next_up(1.0) - 1.0 == g["bf16"]
+    assert O.round_to_bf16(np.array([1.0 + g["bf16"]]))[0] == 1.0 + g["bf16"]
+    # the midpoint 1 + eps/2 ties to the even neighbour 1
+    assert O.round_to_bf16(np.array([1.0 + g["bf16"] / 2]))[0] == 1.0
+    assert O.round_to_bf16(np.array([1.0 + 3 * g["bf16"] / 2]))[0] == 1.0 + 2 * g["bf16"]
+    assert abs(2.0 ** -23 - g["fp32"]) < 1e-9
+
+
+def _all_finite_bf16():
+    bits = np.arange(0, 0x10000, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        vals = (bits << 16).view(np.float32).astype(np.float64)
+    ok = np.isfinite(vals)
+    return vals[ok], bits[ok]
+
+
+def test_round_to_bf16_bruteforce_nearest():
+    vals, bits = _all_finite_bf16()
+    order = np.argsort(vals, kind="stable")
+    sv, sb = vals[order], bits[order]
+    # drop -0 duplicate of +0 (keep the +0 pattern, which is even)
+    keep = np.ones(len(sv), bool)
+    keep[(sv == 0) & (sb == 0x8000)] = False
+    sv, sb = sv[keep], sb[keep]
+    g = rng(6)
+    xs = np.concatenate([
+        g.standard_normal(4000) * 10.0 ** g.integers(-30, 30, 4000),
+        g.standard_normal(500) * 2.0 ** -130,                        # subnormal range
+        (sv[1000:1500] + sv[1001:1501]) / 2,                          # exact ties
+        sv[2000:2500],                                                 # representable
+    ])
+    got = O.round_to_bf16(xs)
+    for x, y in zip(xs, got):
+        i = np.searchsorted(sv, x)
+        cands = [k for k in (i - 1, i) if 0 <= k < len(sv)]
+        best = min(abs(sv[k] - x) for k in cands)
+        near = [k for k in cands if abs(sv[k] - x) == best]
+        if len(near) == 2:                                              # tie: even pattern
+            near = [k for k in near if sb[k] % 2 == 0]
+        assert y == sv[near[0]], (x, y, sv[near[0]])
+    assert O.round_to_bf16(np.array([3.5e38]))[0] == np.inf
+
+
+# ---------------------------------------------------------------- GELU
+
+def test_gelu_closed_forms():
+    assert O.gelu(np.array(0.0)) == 0.0
+    x = np.linspace(-6, 6, 101)
+    assert np.allclose(O.gelu(x) - O.gelu(-x), x, atol=1e-14)
+    q = 1.959963984540054          # standard normal 97.5 % quantile
+    assert abs(O.gelu(np.array(q)) / q - 0.975) < 1e-12
+    assert abs(O.gelu(np.array(30.0)) - 30.0) < 1e-12
+    assert abs(O.gelu(np.array(-30.0))) < 1e-12
+    assert O.gelu_grad(np.array(0.0)) == 0.5
+
+
+def test_gelu_grad_finite_difference():
+    x = np.linspace(-5, 5, 41)
+    h = 1e-6
+    fd = (O.gelu(x + h) - O.gelu(x - h)) / (2 * h)
+    assert np.allclose(fd, O.gelu_grad(x), atol=1e-8)
+
+
+# ---------------------------------------------------------------- MLP
+
+def _mlp_loop(X, A, B):
+    M, h = X.shape
+    f = A.shape[1]
+    Z = [[0.0] * B.shape[1] for _ in range(M)]
+    for m in range(M):
+        H = []
+        for j in range(f):
+            p = sum(X[m, k] * A[k, j] for k in range(h))
+            H.append(0.5 * p * (1 + math.erf(p / math.sqrt(2))))
+        for c in range(B.shape[1]):
+            Z[m][c] = sum(H[j] * B[j, c] for j in range(f))
+    return np.array(Z)
+
+
+def test_mlp_forward_bruteforce():
+    g = rng(7)
+    X, A, B = g.standard_normal((3, 4)), g.standard_normal((4, 8)), g.standard_normal((8, 4))
+    _, _, Z = O.mlp_forward(X, A, B)
+    assert np.allclose(Z, _mlp_loop(X, A, B), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_mlp_shards_sum_to_unsharded(n):
+    g = rng(8)
+    X, A, B = g.standard_normal((5, 6)), g.standard_normal((6, 16)), g.standard_normal((16, 6))
+    dZ = g.standard_normal((5, 6))
+    P, H, Z = O.mlp_forward(X, A, B)
+    dX, dA, dB = O.mlp_backward(X, A, B, P, dZ)
+    outs, Zs = O.tp_mlp_forward(X, A, B, n)
+    assert np.allclose(Zs, Z, rtol=1e-12, atol=1e-12)
+    res, dXs = O.tp_mlp_backward(X, A, B, dZ, n)
+    assert np.allclose(dXs, dX, rtol=1e-12, atol=1e-12)
+    for r in range(n):
+        s, c = O.partition(16, n, r)
+        assert np.allclose(res[r][1], dA[:, s:s + c], rtol=1e-12, atol=1e-12)
+        assert np.allclose(res[r][2], dB[s:s + c, :], rtol=1e-12, atol=1e-12)
+        assert np.allclose(outs[r][1], H[:, s:s + c], rtol=1e-12, atol=1e-12)
+
+
+def _fd_check(f, args, grads, h=1e-6, tol=1e-6):
+    """Central differences of scalar f w.r.t. every entry of every array in args."""
+    for a, gr in zip(args, grads):
+        it = np.nditer(a, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = a[i]
+            a[i] = old + h
+            fp = f()
+            a[i] = old - h
+            fm = f()
+            a[i] = old
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - gr[i]) <= tol * max(1.0, abs(fd)), (i, fd, gr[i])
+
+
+def test_mlp_backward_finite_difference():
+    g = rng(9)
+    X, A, B = g.standard_normal((3, 4)), g.standard_normal((4, 8)), g.standard_normal((8, 4))
+    R = g.standard_normal((3, 4))
+    P, _, _ = O.mlp_forward(X, A, B)
+    dX, dA, dB = O.mlp_backward(X, A, B, P, R)
+    _fd_check(lambda: np.sum(R * O.mlp_forward(X, A, B)[2]), [X, A, B], [dX, dA, dB])
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_single_position_returns_v():
+    g = rng(10)
+    Q, K, V = g.standard_normal((1, 4)), g.standard_normal((1, 4)), g.standard_normal((1, 4))
+    Ot, lse = O.attention_head_forward(Q, K, V, causal=True)
+    assert np.allclose(Ot, V, atol=1e-15)
+    assert np.allclose(lse, (Q @ K.T)[0] / 2.0, atol=1e-15)
+
+
+def test_attention_zero_query_is_running_mean():
+    g = rng(11)
+    s, d = 7, 3
+    K, V = g.standard_normal((s, d)), g.standard_normal((s, d))
+    Ot, lse = O.attention_head_forward(np.zeros((s, d)), K, V, causal=True)
+    for i in range(s):
+        assert np.allclose(Ot[i], V[:i + 1].mean(axis=0), atol=1e-14)
+        assert abs(lse[i] - math.log(i + 1)) < 1e-14
+    On, _ = O.attention_head_forward(np.zeros((s, d)), K, V, causal=False)
+    assert np.allclose(On, np.tile(V.mean(axis=0), (s, 1)), atol=1e-14)
+
+
+def _attn_loop(Q, K, V, causal):
+    s, d = Q.shape
+    out = np.zeros_like(V)
+    for i in range(s):
+        lim = i + 1 if causal else K.shape[0]
+        sc = [sum(Q[i, c] * K[j, c] for c in range(d)) / math.sqrt(d) for j in range(lim)]
+        mx = max(sc)
+        w = [math.exp(v - mx) for v in sc]
+        tot = sum(w)
+        for c in range(d):
+            out[i, c] = sum(w[j] * V[j, c] for j in range(lim)) / tot
+    return out
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_bruteforce(causal):
+    g = rng(12)
+    Q, K, V = (g.standard_normal((5, 4)) * 2 for _ in range(3))
+    Ot, _ = O.attention_head_forward(Q, K, V, causal)
+    assert np.allclose(Ot, _attn_loop(Q, K, V, causal), atol=1e-13)
+    assert np.allclose(Ot[0], V[0], atol=1e-15) if causal else True
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_head_backward_finite_difference(causal):
+    g = rng(13)
+    Q, K, V = g.standard_normal((4, 3)), g.standard_normal((4, 3)), g.standard_normal((4, 3))
+    R = g.standard_normal((4, 3))
+    Ot, _ = O.attention_head_forward(Q, K, V, causal)
+    dQ, dK, dV = O.attention_head_backward(Q, K, V, Ot, R, causal)
+    _fd_check(lambda: np.sum(R * O.attention_head_forward(Q, K, V, causal)[0]),
+              [Q, K, V], [dQ, dK, dV])
+
+
+def _attn_full(X, WQ, WK, WV, WO, b, s, nh, d):
+    return O.attention_layer_forward(X, np.concatenate([WQ, WK, WV], axis=1), WO, b, s, nh, d)
+
+
+def test_attention_layer_shards_sum_to_unsharded_and_heads_permute():
+    g = rng(14)
+    b, s, h, nh, d, n = 2, 5, 6, 4, 3, 2
+    X = g.standard_normal((b * s, h))
+    WQ, WK, WV = (g.standard_normal((h, nh * d)) for _ in range(3))
+    WO = g.standard_normal((nh * d, h))
+    dZ = g.standard_normal((b * s, h))
+    QKV, Ob, lse, Z = _attn_full(X, WQ, WK, WV, WO, b, s, nh, d)
+    _, Zs = O.tp_attention_forward(X, WQ, WK, WV, WO, b, s, nh, d, n)
+    assert np.allclose(Zs, Z, atol=1e-12)
+    Wqkv = np.concatenate([WQ, WK, WV], axis=1)
+    dX, dWqkv, dWo = O.attention_layer_backward(X, Wqkv, WO, QKV, Ob, dZ, b, s, nh, d)
+    res, dXs = O.tp_attention_backward(X, WQ, WK, WV, WO, dZ, b, s, nh, d, n)
+    assert np.allclose(dXs, dX, atol=1e-12)
+    hs, w = nh // n, nh * d
+    for r in range(n):
+        c = slice(r * hs * d, (r + 1) * hs * d)
+        got = res[r][1]
+        assert np.allclose(got[:, :hs * d], dWqkv[:, c], atol=1e-12)
+        assert np.allclose(got[:, hs * d:2 * hs * d], dWqkv[:, w:][:, c], atol=1e-12)
+        assert np.allclose(got[:, 2 * hs * d:], dWqkv[:, 2 * w:][:, c], atol=1e-12)
+        assert np.allclose(res[r][2], dWo[c, :], atol=1e-12)
+    # a consistent permutation of the heads leaves Z unchanged
+    perm = [2, 0, 3, 1]
+    cols = np.concatenate([np.arange(p * d, (p + 1) * d) for p in perm])
+    _, _, _, Zp = _attn_full(X, WQ[:, cols], WK[:, cols], WV[:, cols], WO[cols, :], b, s, nh, d)
+    assert np.allclose(Zp, Z, atol=1e-12)
+
+
+def test_attention_layer_backward_finite_difference():
+    g = rng(15)
+    b, s, h, nh, d = 1, 3, 4, 2, 2
+    X = g.standard_normal((b * s, h))
+    Wqkv = g.standard_normal((h, 3 * nh * d))
+    Wo = g.standard_normal((nh * d, h))
+    R = g.standard_normal((b * s, h))
+    QKV, Ob, _, _ = O.attention_layer_forward(X, Wqkv, Wo, b, s, nh, d)
+    dX, dWqkv, dWo = O.attention_layer_backward(X, Wqkv, Wo, QKV, Ob, R, b, s, nh, d)
+    _fd_check(lambda: np.sum(R * O.attention_layer_forward(X, Wqkv, Wo, b, s, nh, d)[3]),
+              [X, Wqkv, Wo], [dX, dWqkv, dWo])
+
+
+# ---------------------------------------------------------------- shard_reduce
+
+def test_shard_reduce_exact_and_ordered():
+    g = rng(16)
+    parts = [g.integers(-1000, 1000, (4, 5)).astype(np.float64) for _ in range(5)]
+    tot = np.zeros((4, 5))
+    for p in parts:
+        for i in range(4):
+            for j in range(5):
+                tot[i, j] += p[i, j]
+    assert np.array_equal(O.shard_reduce(parts), tot)
+
+
+def test_shard_reduce_two_bf16_parts_round_once():
+    """For two bf16 parts the fp64 sum rounded once equals the correctly
+    rounded bf16 sum found by brute force (nearest representable, ties even)."""
+    vals, bits = _all_finite_bf16()
+    g = rng(17)
+    a = vals[g.integers(0, len(vals), 3000)]
+    b = vals[g.integers(0, len(vals), 3000)]
+    ok = np.abs(a) < 1e37
+    a, b = a[ok], b[ok]
+    got = O.round_to_bf16(O.shard_reduce([a, b]))
+    order = np.argsort(vals)
+    sv, sb = vals[order], bits[order]
+    for x, y in zip(a + b, got):
+        i = np.searchsorted(sv, x)
+        cands = [k for k in (i - 1, i) if 0 <= k < len(sv)]
+        best = min(abs(sv[k] - x) for k in cands)
+        near = [k for k in cands if abs(sv[k] - x) == best]
+        if len(near) == 2 and sv[near[0]] != sv[near[1]]:
+            near = [k for k in near if sb[k] % 2 == 0]
+        assert y == sv[near[0]]
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+def test_layernorm_invariants_and_loop():
+    g = rng(18)
+    x = g.standard_normal((4, 9)) * 3 + 1
+    gam, bet = np.ones(9), np.zeros(9)
+    y, mu, rs = O.layernorm_forward(x, gam, bet, 1e-5)
+    assert np.allclose(y.mean(axis=1), 0, atol=1e-13)
+    var = x.var(axis=1)
+    assert np.allclose(y.var(axis=1), var / (var + 1e-5), atol=1e-12)
+    gam, bet = g.standard_normal(9), g.standard_normal(9)
+    y, _, _ = O.layernorm_forward(x, gam, bet, 1e-5)
+    for i in range(4):
+        m = sum(x[i]) / 9
+        v = sum((t - m) ** 2 for t in x[i]) / 9
+        for j in range(9):
+            ref = (x[i, j] - m) / math.sqrt(v + 1e-5) * gam[j] + bet[j]
+            assert abs(ref - y[i, j]) < 1e-12
+
+
+def test_layernorm_backward_finite_difference():
+    g = rng(19)
+    x = g.standard_normal((3, 5))
+    gam, bet = g.standard_normal(5), g.standard_normal(5)
+    R = g.standard_normal((3, 5))
+    _, mu, rs = O.layernorm_forward(x, gam, bet)
+    dx, dg, db = O.layernorm_backward(x, gam, mu, rs, R)
+    _fd_check(lambda: np.sum(R * O.layernorm_forward(x, gam, bet)[0]), [x, gam, bet], [dx, dg, db])
+
+
+# ---------------------------------------------------------------- stacked model
+
+def test_gpt_backward_finite_difference():
+    g = rng(20)
+    V, H, nh, d, L, b, s, n = 11, 8, 2, 4, 2, 1, 3, 2
+    ids = g.integers(0, V, b * s)
+    E = g.standard_normal((V, H)) * 0.5
+    layers = []
+    for _ in range(L):
+        layers.append({k: g.standard_normal(sh) * 0.3 for k, sh in
+                       [("WQ", (H, H)), ("WK", (H, H)), ("WV", (H, H)), ("WO", (H, H)),
+                        ("A", (H, 4 * H)), ("B", (4 * H, H))]})
+        layers[-1].update(g1=1 + 0.1 * g.standard_normal(H), b1=0.1 * g.standard_normal(H),
+                          g2=1 + 0.1 * g.standard_normal(H), b2=0.1 * g.standard_normal(H))
+    R = [g.standard_normal((b * s, O.partition(V, n, r)[1])) for r in range(n)]
+
+    def loss():
+        lg, _ = O.gpt_forward(ids, E, layers, b, s, nh, d, n)
+        return sum(np.sum(R[r] * lg[r]) for r in range(n))
+
+    lg, cache = O.gpt_forward(ids, E, layers, b, s, nh, d, n)
+    dE, grads = O.gpt_backward(ids, E, layers, cache, R, b, s, nh, d, n)
+    # spot-check a subset of entries of every parameter (all of E)
+    _fd_check(loss, [E], [dE], tol=2e-6)
+    for li in range(L):
+        for key in ("WQ", "WO", "A", "B", "g1", "b2"):
+            a, gr = layers[li][key], grads[li][key]
+            for idx in [tuple(0 for _ in a.shape), tuple(x - 1 for x in a.shape)]:
+                old = a[idx]
+                a[idx] = old + 1e-6
+                fp = loss()
+                a[idx] = old - 1e-6
+                fm = loss()
+                a[idx] = old
+                fd = (fp - fm) / 2e-6
+                assert abs(fd - gr[idx]) <= 2e-6 * max(1.0, abs(fd)), (li, key, idx)
