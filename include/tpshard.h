@@ -1,0 +1,233 @@
+/*
+ * tpshard.h -- C ABI of the tensor-parallel transformer-shard library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call executes ONE tensor-parallel shard of one operation at that
+ * shard's real per-shard shape; the shard-partial sum that a multi-GPU run
+ * would obtain from an all-reduce is the separate call shard_reduce().
+ * Sources for what each call computes (pages cited by title and section):
+ *   "5-megatron"  formulaic.cloudchewie.com .../distributed-training/5-megatron
+ *   "Megtron张量/模型并行"  amentiraz.github.io .../Megtron张量/模型并行/
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Matrices are dense and row-major in the mathematical layout (a linear
+ *   layer is Y = X W with W of shape in x out), i.e. the layout of page
+ *   "Megtron张量/模型并行", section 切分权重; the leading dimension of every
+ *   matrix equals its column count unless an explicit ld argument exists.
+ * - Element type: TPS_BF16 (bfloat16 storage, fp32 accumulation, every store
+ *   rounded to nearest even) or TPS_F32 (fp32 throughout).  Accumulators that
+ *   the caller keeps (dE_r, LayerNorm statistics and parameter gradients) are
+ *   always fp32.
+ * - Token rows are batch-major: row = batch * seq_len + position.
+ * - Pointers are device pointers (caller-owned, e.g. from PyTorch), 16-byte
+ *   aligned.  Column counts of matrices read with vector loads (h, f_i, H,
+ *   hs*d, ldl) must be multiples of 8 elements (bf16) or 4 (fp32).  Row
+ *   counts (M, T, v_rows, sq) are arbitrary.
+ * - All calls are asynchronous on `stream` (a hipStream_t; 0 = the default
+ *   stream).  Inputs must stay alive until the stream reaches the work.
+ * - The library never allocates device memory.  Scratch memory is passed in
+ *   as `ws` of at least the size returned by the matching *_workspace() query.
+ * - Outputs must not alias inputs (exception: shard_reduce's out may equal
+ *   parts[0]).
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   on failure the call returns TPS_EINVAL (or TPS_EUNSUPPORTED /
+ *   TPS_EWORKSPACE), enqueues nothing and leaves outputs untouched.  A failed
+ *   launch returns TPS_EHIP.  tps_last_error() gives a thread-local message.
+ * - Results are deterministic: no floating-point atomics are used, so two runs
+ *   on the same inputs give identical bits.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* tps_stream_t;
+
+typedef enum {
+  TPS_OK = 0,
+  TPS_EINVAL = 1,        /* bad argument (null pointer, size, alignment, ld) */
+  TPS_EUNSUPPORTED = 2,  /* valid request this build does not implement      */
+  TPS_EWORKSPACE = 3,    /* ws_bytes smaller than the workspace query        */
+  TPS_EHIP = 4           /* a HIP launch or runtime call failed              */
+} tps_status;
+
+typedef enum { TPS_F32 = 0, TPS_BF16 = 1 } tps_dtype;
+
+const char* tps_status_string(tps_status s);
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* tps_last_error(void);
+/* Library version string. */
+const char* tps_version(void);
+
+/*
+ * Split `total` rows into `n` contiguous shards; shard r starts at *start and
+ * holds *count rows.  The first (total mod n) shards hold one extra row.
+ * Page "5-megatron", section VocabParallelEmbedding (each rank keeps a
+ * contiguous vocabulary range [start, end), example [0,5) and [5,10) for 10
+ * words); page "Megtron张量/模型并行", section 输入层Embedding (300 words split
+ * at 150).  Host-only.  EINVAL if n < 1, r outside [0, n), total < 0 or a
+ * null output pointer.
+ */
+tps_status tps_partition(int64_t total, int n, int r, int64_t* start, int64_t* count);
+
+/* ------------------------------------------------------------------------
+ * (1) MLP shard: Z = GELU(X A) B with A column-parallel and B row-parallel.
+ * Page "Megtron张量/模型并行", section MLP层 (A split by columns so GELU needs
+ * no communication, B split by rows); page "5-megatron", sections
+ * ColumnParallelLinear and RowParallelLinear (f = copy, g = all-reduce).
+ *
+ * tp_mlp_fwd:  P_i = X A_i,  H_i = gelu(P_i) (exact erf),  Z_i = H_i B_i.
+ *   X   [M x h]     activations (replicated on every shard)
+ *   A_i [h x f_i]   column shard of A
+ *   B_i [f_i x h]   row shard of B
+ *   P_i, H_i [M x f_i]  outputs, kept for the backward pass
+ *   Z_i [M x h]     output: this shard's partial (sum over shards = Z)
+ * ------------------------------------------------------------------------ */
+tps_status tp_mlp_fwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i,
+                      const void* X, const void* A_i, const void* B_i,
+                      void* P_i, void* H_i, void* Z_i, tps_stream_t stream);
+
+/* Bytes of scratch tp_mlp_bwd needs (holds dP_i, M x f_i elements). */
+size_t tp_mlp_bwd_workspace(tps_dtype dt, int64_t M, int64_t h, int64_t f_i);
+
+/*
+ * tp_mlp_bwd: with dZ the full upstream gradient (g's backward is identity):
+ *   dB_i = H_i^T dZ                      [f_i x h]
+ *   dP_i = (dZ B_i^T) * gelu'(P_i)       (scratch)
+ *   dA_i = X^T dP_i                      [h x f_i]
+ *   dX_i = dP_i A_i^T                    [M x h]  partial; f's backward sums them
+ */
+tps_status tp_mlp_bwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i,
+                      const void* X, const void* A_i, const void* B_i,
+                      const void* P_i, const void* H_i, const void* dZ,
+                      void* dX_i, void* dA_i, void* dB_i,
+                      void* ws, size_t ws_bytes, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * (2) Attention shard: Q/K/V column-parallel by heads, per-head softmax
+ * attention, output projection row-parallel.  Page "Megtron张量/模型并行",
+ * section Self-Attention层 (each head computed independently, several heads
+ * may share a GPU, output linear split by rows); page "5-megatron", section
+ * ParallelSelfAttention.  Per head: S = Q K^T / sqrt(d), keys after the query
+ * masked when `causal` != 0, P = softmax(S), O = P V.
+ *
+ *   X      [b*sq x h]
+ *   Wqkv_i [h x 3*hs*d]   = [W_Q | W_K | W_V] of this shard's hs heads; head j
+ *                           occupies columns j*d..(j+1)*d inside each block
+ *   Wo_i   [hs*d x h]     row shard of the output projection
+ *   QKV_i  [b*sq x 3*hs*d] output (kept for backward)
+ *   O_i    [b*sq x hs*d]  output (kept), head j at columns j*d..(j+1)*d
+ *   lse_i  [b x hs x sq]  fp32 output (kept): log of each softmax row's sum
+ *   Z_i    [b*sq x h]     output: this shard's partial
+ * Supported: dt = TPS_BF16, d in {64, 128, 256, 512}; TPS_EUNSUPPORTED otherwise.
+ * ------------------------------------------------------------------------ */
+tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d,
+                       int causal, const void* X, const void* Wqkv_i, const void* Wo_i,
+                       void* QKV_i, void* O_i, float* lse_i, void* Z_i, tps_stream_t stream);
+
+size_t tp_attn_bwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d);
+
+/*
+ * tp_attn_bwd: dWo_i = O_i^T dZ; dO = dZ Wo_i^T; per head dQ, dK, dV of the
+ * softmax attention; dWqkv_i = X^T dQKV; dX_i = dQKV Wqkv_i^T (partial).
+ * dZ [b*sq x h] is the full upstream gradient.  Outputs dX_i [b*sq x h],
+ * dWqkv_i [h x 3*hs*d], dWo_i [hs*d x h].
+ */
+tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d,
+                       int causal, const void* X, const void* Wqkv_i, const void* Wo_i,
+                       const void* QKV_i, const void* O_i, const float* lse_i, const void* dZ,
+                       void* dX_i, void* dWqkv_i, void* dWo_i,
+                       void* ws, size_t ws_bytes, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * (3) 'g' forward / 'f' backward: the shard-partial sum.
+ * Page "5-megatron", sections ColumnParallelLinear (_CopyToModelParallelRegion
+ * all-reduces the gradient) and RowParallelLinear
+ * (_ReduceFromModelParallelRegion all-reduces the output).
+ *   out[i] = round(sum_{r=0}^{n_parts-1} parts[r][i]) for i < n, summed in
+ *   fp32 in shard order 0..n_parts-1 and rounded once to out_dt.
+ *   parts: HOST array of n_parts device pointers (1 <= n_parts <= 8), each of
+ *   in_dt.  out may equal parts[0].
+ * ------------------------------------------------------------------------ */
+tps_status shard_reduce(tps_dtype in_dt, tps_dtype out_dt, int n_parts,
+                        const void* const* parts, void* out, int64_t n, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * (4) Vocab-parallel word embedding and the tied output projection.
+ * Page "5-megatron", section VocabParallelEmbedding: ids outside this shard's
+ * range [v_start, v_start + v_rows) are masked, the rest index row
+ * id - v_start, and masked rows of the result are set to 0 before the sum.
+ * Page "Megtron张量/模型并行", sections 输入层Embedding and 输出层Embedding:
+ * the output layer reuses the same table, and the table's update must use the
+ * sum of the output-side and input-side gradients.
+ *
+ * vocab_embed_fwd: Y_r[t] = E_r[ids[t] - v_start] if in range, else +0.
+ *   ids [T] int32 (any value; out-of-vocabulary ids simply give zero rows),
+ *   E_r [v_rows x H], Y_r [T x H] (every row written).  Bit-exact copy.
+ * ------------------------------------------------------------------------ */
+tps_status vocab_embed_fwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
+                           const int32_t* ids, const void* E_r, void* Y_r, tps_stream_t stream);
+
+size_t vocab_embed_bwd_workspace(int64_t T, int64_t v_rows);
+
+/*
+ * vocab_embed_bwd (input side): dE_r[j] += sum over t with ids[t] = v_start + j
+ * of dY[t], added in increasing t order in fp32 (deterministic, no atomics).
+ *   dY [T x H] of dt; dE_r [v_rows x H] fp32, accumulated into (rows no
+ *   token hits are not touched).  Requires T < 2^31.
+ * Tied-gradient order: call tied_logits_bwd (which overwrites dE_r with the
+ * output-side gradient) first, then vocab_embed_bwd.
+ */
+tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
+                           const int32_t* ids, const void* dY, float* dE_r,
+                           void* ws, size_t ws_bytes, tps_stream_t stream);
+
+/*
+ * tied_logits: L_r = X E_r^T.
+ *   X [T x H], E_r [v_rows x H], L_r [T x v_rows] with row stride ldl
+ *   (ldl >= v_rows, multiple of 8 for bf16 / 4 for fp32; columns v_rows..ldl-1
+ *   are not written).
+ */
+tps_status tied_logits(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, int64_t ldl,
+                       const void* X, const void* E_r, void* L_r, tps_stream_t stream);
+
+/*
+ * tied_logits_bwd: dX_r = dL_r E_r (partial, [T x H]) and
+ * dE_r = dL_r^T X ([v_rows x H] fp32, OVERWRITTEN with the output-side gradient).
+ * dL_r [T x v_rows] with row stride ldl; padding columns are ignored.
+ */
+tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, int64_t ldl,
+                           const void* X, const void* E_r, const void* dL_r,
+                           void* dX_r, float* dE_r, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * LayerNorm (replicated on every shard), for stacking layers.  Page
+ * "5-megatron", section 训练一般流程 counts two LayerNorms of 2H parameters
+ * per layer; the formula is the standard one with biased variance:
+ *   y = (x - mean) / sqrt(var + eps) * gamma + beta   (per row of H)
+ * layernorm_fwd: x, y [M x H] of dt; gamma, beta [H] fp32; mean, rstd [M] fp32
+ * outputs kept for the backward pass.
+ * layernorm_bwd: dx [M x H] of dt; dgamma, dbeta [H] fp32 OVERWRITTEN.
+ * ------------------------------------------------------------------------ */
+tps_status layernorm_fwd(tps_dtype dt, int64_t M, int64_t H, float eps, const void* x,
+                         const float* gamma, const float* beta, void* y, float* mean,
+                         float* rstd, tps_stream_t stream);
+
+size_t layernorm_bwd_workspace(int64_t M, int64_t H);
+
+tps_status layernorm_bwd(tps_dtype dt, int64_t M, int64_t H, const void* x, const float* gamma,
+                         const float* mean, const float* rstd, const void* dy, void* dx,
+                         float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
+                         tps_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -1,0 +1,18 @@
+"""Tensor-parallel transformer shards on AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libtpshard.so`` (HIP kernels behind the C ABI in
+``include/tpshard.h``); ``binding`` exposes the same entry points to Python
+for torch tensors.  Importing the package loads the library and raises if it
+has not been built.
+"""
+
+from .binding import (  # noqa: F401
+    TPS_BF16, TPS_F32, TpsError, LIB_PATH, lib,
+    tps_partition, tps_version,
+    tp_mlp_fwd, tp_mlp_bwd, tp_mlp_bwd_workspace,
+    tp_attn_fwd, tp_attn_bwd, tp_attn_bwd_workspace,
+    shard_reduce,
+    vocab_embed_fwd, vocab_embed_bwd, vocab_embed_bwd_workspace,
+    tied_logits, tied_logits_bwd,
+    layernorm_fwd, layernorm_bwd, layernorm_bwd_workspace,
+)

@@ -1,0 +1,121 @@
+// Shared device helpers for the gfx950 kernels: bf16 storage conversion,
+// 16-byte vector types, and host-side error plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/tpshard.h"
+
+namespace tps {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element-type traits: storage type and conversions to/from fp32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static float to_f32(float v) { return v; }
+  __device__ static float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  __device__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// Store 4 consecutive values (fp32 in registers) to T storage, bounds-checked
+// element-wise when `nvalid` < 4.  Aligned vector store when complete.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float v[4], int nvalid);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float v[4], int nvalid) {
+  if (nvalid >= 4) {
+    f32x4_t x = {v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4_t*>(p) = x;
+  } else {
+    for (int i = 0; i < nvalid; ++i) p[i] = v[i];
+  }
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float v[4], int nvalid) {
+  if (nvalid >= 4) {
+    u32x2_t x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2_t*>(p) = x;
+  } else {
+    for (int i = 0; i < nvalid; ++i) p[i] = f32_to_bf16(v[i]);
+  }
+}
+
+// Load 4 consecutive elements as fp32 (element-wise when incomplete).
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float v[4], int nvalid);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float v[4], int nvalid) {
+  if (nvalid >= 4) {
+    f32x4_t x = *reinterpret_cast<const f32x4_t*>(p);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  } else {
+    for (int i = 0; i < 4; ++i) v[i] = i < nvalid ? p[i] : 0.f;
+  }
+}
+template <>
+__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float v[4], int nvalid) {
+  if (nvalid >= 4) {
+    u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    v[0] = bf16lo(x[0]); v[1] = bf16hi(x[0]); v[2] = bf16lo(x[1]); v[3] = bf16hi(x[1]);
+  } else {
+    for (int i = 0; i < 4; ++i) v[i] = i < nvalid ? bf16_to_f32(p[i]) : 0.f;
+  }
+}
+
+// GELU with the exact erf form and its derivative (fp32).
+__device__ __forceinline__ float gelu_f(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
+  const float pdf = 0.39894228040143268f * __expf(-0.5f * x * x);
+  return cdf + x * pdf;
+}
+
+// ---------------------------------------------------------------- host side
+
+// Records a thread-local error message and returns `s`.
+tps_status set_error(tps_status s, const std::string& msg);
+tps_status check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t elem_bytes(tps_dtype dt) { return dt == TPS_BF16 ? 2 : 4; }
+inline int64_t vec_elems(tps_dtype dt) { return dt == TPS_BF16 ? 8 : 4; }
+
+}  // namespace tps

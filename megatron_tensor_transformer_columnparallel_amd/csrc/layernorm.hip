@@ -1,0 +1,232 @@
+// LayerNorm forward/backward (replicated on every shard; used between the
+// attention and MLP sublayers of a stacked model).  One workgroup per row in
+// the forward pass with the row held in registers (H <= 8192); the backward
+// pass gives each workgroup 8 rows and writes per-workgroup partial column
+// sums of dgamma/dbeta to the workspace, which a second kernel reduces in a
+// fixed order (deterministic, no atomics).
+#include <string>
+
+#include "common.hpp"
+
+namespace tps {
+
+constexpr int kLnMaxH = 8192;
+constexpr int kLnRowsPerBlock = 8;
+
+template <typename T> struct LnVec;
+template <> struct LnVec<bf16_t> {
+  static constexpr int V = 8;
+  __device__ static void load(const bf16_t* p, float* v) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { v[2 * w] = bf16lo(x[w]); v[2 * w + 1] = bf16hi(x[w]); }
+  }
+  __device__ static void store(bf16_t* p, const float* v) {
+    u32x4_t x;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) x[w] = pack_bf16x2(v[2 * w], v[2 * w + 1]);
+    *reinterpret_cast<u32x4_t*>(p) = x;
+  }
+};
+template <> struct LnVec<float> {
+  static constexpr int V = 4;
+  __device__ static void load(const float* p, float* v) {
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  }
+  __device__ static void store(float* p, const float* v) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+  }
+};
+
+// Sum over the 256 threads of a workgroup; `red` is 8 floats of LDS.
+__device__ __forceinline__ float block_sum(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) ln_fwd_kernel(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                     const float* __restrict__ beta, T* __restrict__ y,
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int64_t H,
+                                                     float eps) {
+  constexpr int V = LnVec<T>::V;
+  constexpr int NCH = kLnMaxH / V / 256;
+  __shared__ float red[8];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * H;
+  float v[NCH][V];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+    if (c < H) {
+      LnVec<T>::load(xr + c, v[i]);
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += v[i][e];
+    }
+  }
+  const float mu = block_sum(s, red) / (float)H;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+    if (c < H) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) { const float d = v[i][e] - mu; q += d * d; }
+    }
+  }
+  const float var = block_sum(q, red) / (float)H;
+  const float rs = rsqrtf(var + eps);
+  T* yr = y + row * H;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+    if (c < H) {
+      float o[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = (v[i][e] - mu) * rs * gamma[c + e] + beta[c + e];
+      LnVec<T>::store(yr + c, o);
+    }
+  }
+  if (threadIdx.x == 0) { mean[row] = mu; rstd[row] = rs; }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ x, const float* __restrict__ gamma,
+                                                     const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                     const T* __restrict__ dy, T* __restrict__ dx,
+                                                     float* __restrict__ part, int64_t M, int64_t H) {
+  constexpr int V = LnVec<T>::V;
+  constexpr int NCH = kLnMaxH / V / 256;
+  __shared__ float red[8];
+  float pg[NCH][V], pb[NCH][V];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e = 0; e < V; ++e) { pg[i][e] = 0.f; pb[i][e] = 0.f; }
+  const int64_t r0 = (int64_t)blockIdx.x * kLnRowsPerBlock;
+  for (int rr = 0; rr < kLnRowsPerBlock; ++rr) {
+    const int64_t row = r0 + rr;
+    if (row >= M) break;
+    const float mu = mean[row], rs = rstd[row];
+    float xh[NCH][V], gv[NCH][V];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+      if (c < H) {
+        float xv[V], dv[V];
+        LnVec<T>::load(x + row * H + c, xv);
+        LnVec<T>::load(dy + row * H + c, dv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          xh[i][e] = (xv[e] - mu) * rs;
+          gv[i][e] = dv[e] * gamma[c + e];
+          s1 += gv[i][e];
+          s2 += gv[i][e] * xh[i][e];
+          pg[i][e] += dv[e] * xh[i][e];
+          pb[i][e] += dv[e];
+        }
+      }
+    }
+    const float m1 = block_sum(s1, red) / (float)H;
+    const float m2 = block_sum(s2, red) / (float)H;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+      if (c < H) {
+        float o[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] = rs * (gv[i][e] - m1 - xh[i][e] * m2);
+        LnVec<T>::store(dx + row * H + c, o);
+      }
+    }
+  }
+  float* pr = part + (int64_t)blockIdx.x * 2 * H;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+    if (c < H) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) { pr[c + e] = pg[i][e]; pr[H + c + e] = pb[i][e]; }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) ln_param_reduce_kernel(const float* __restrict__ part, float* __restrict__ dgamma,
+                                                              float* __restrict__ dbeta, int64_t nblk, int64_t H) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= H) return;
+  float g = 0.f, b = 0.f;
+  for (int64_t k = 0; k < nblk; ++k) {
+    g += part[k * 2 * H + c];
+    b += part[k * 2 * H + H + c];
+  }
+  dgamma[c] = g;
+  dbeta[c] = b;
+}
+
+static tps_status ln_checks(const char* fn, tps_dtype dt, int64_t M, int64_t H,
+                            std::initializer_list<const void*> ptrs) {
+  if (dt != TPS_F32 && dt != TPS_BF16) return set_error(TPS_EINVAL, std::string(fn) + ": bad dtype");
+  if (M <= 0 || H <= 0 || M >= 0x7fffffffLL) return set_error(TPS_EINVAL, std::string(fn) + ": need 0 < M < 2^31, H > 0");
+  if (H % vec_elems(dt)) return set_error(TPS_EINVAL, std::string(fn) + ": H must be a multiple of 8 (bf16) / 4 (fp32)");
+  for (const void* p : ptrs) {
+    if (!p) return set_error(TPS_EINVAL, std::string(fn) + ": null pointer");
+    if (!aligned16(p)) return set_error(TPS_EINVAL, std::string(fn) + ": pointer not 16-byte aligned");
+  }
+  if (H > kLnMaxH) return set_error(TPS_EUNSUPPORTED, std::string(fn) + ": H > 8192");
+  return TPS_OK;
+}
+
+}  // namespace tps
+
+using namespace tps;
+
+extern "C" tps_status layernorm_fwd(tps_dtype dt, int64_t M, int64_t H, float eps, const void* x, const float* gamma,
+                                    const float* beta, void* y, float* mean, float* rstd, tps_stream_t stream) {
+  tps_status s = ln_checks("layernorm_fwd", dt, M, H, {x, gamma, beta, y, mean, rstd});
+  if (s != TPS_OK) return s;
+  if (!(eps >= 0.f)) return set_error(TPS_EINVAL, "layernorm_fwd: eps must be >= 0");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == TPS_BF16)
+    hipLaunchKernelGGL(ln_fwd_kernel<bf16_t>, dim3((unsigned)M), dim3(256), 0, st, (const bf16_t*)x, gamma, beta,
+                       (bf16_t*)y, mean, rstd, H, eps);
+  else
+    hipLaunchKernelGGL(ln_fwd_kernel<float>, dim3((unsigned)M), dim3(256), 0, st, (const float*)x, gamma, beta,
+                       (float*)y, mean, rstd, H, eps);
+  return check_launch("ln_fwd_kernel");
+}
+
+extern "C" size_t layernorm_bwd_workspace(int64_t M, int64_t H) {
+  if (M <= 0 || H <= 0) return 0;
+  return (size_t)ceil_div(M, kLnRowsPerBlock) * 2 * (size_t)H * sizeof(float);
+}
+
+extern "C" tps_status layernorm_bwd(tps_dtype dt, int64_t M, int64_t H, const void* x, const float* gamma,
+                                    const float* mean, const float* rstd, const void* dy, void* dx, float* dgamma,
+                                    float* dbeta, void* ws, size_t ws_bytes, tps_stream_t stream) {
+  tps_status s = ln_checks("layernorm_bwd", dt, M, H, {x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws});
+  if (s != TPS_OK) return s;
+  if (ws_bytes < layernorm_bwd_workspace(M, H)) return set_error(TPS_EWORKSPACE, "layernorm_bwd: workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
+  float* part = static_cast<float*>(ws);
+  if (dt == TPS_BF16)
+    hipLaunchKernelGGL(ln_bwd_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st, (const bf16_t*)x, gamma, mean,
+                       rstd, (const bf16_t*)dy, (bf16_t*)dx, part, M, H);
+  else
+    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st, (const float*)x, gamma, mean,
+                       rstd, (const float*)dy, (float*)dx, part, M, H);
+  s = check_launch("ln_bwd_kernel");
+  if (s != TPS_OK) return s;
+  hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(H, 256)), dim3(256), 0, st, part, dgamma, dbeta,
+                     nblk, H);
+  return check_launch("ln_param_reduce_kernel");
+}

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/tpshard.h declares, the host-only partition helper matches the pages'
+examples, and argument validation rejects bad calls before any HIP work is
+enqueued (those calls return before touching the device)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+
+def _declared():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def tp():
+    import megatron_tensor_transformer_columnparallel_amd as tp
+    return tp
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for must in ["tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "shard_reduce",
+                 "vocab_embed_fwd", "vocab_embed_bwd", "tied_logits", "tied_logits_bwd",
+                 "layernorm_fwd", "layernorm_bwd", "tps_partition"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(tp):
+    raw = ctypes.CDLL(tp.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), f"{name} declared in tpshard.h but not exported"
+    assert set(_declared()) == set(tp.binding.SIGNATURES), "binding and header disagree"
+
+
+def test_partition_matches_page_examples(tp):
+    with open(os.path.join(ROOT, "tests", "golden", "partition_examples.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        got = [list(tp.tps_partition(case["total"], case["n"], r)) for r in range(case["n"])]
+        assert got == case["shards"]
+
+
+def test_partition_rejects_bad_arguments(tp):
+    for args in [(10, 0, 0), (10, 2, 2), (10, 2, -1), (-1, 2, 0)]:
+        with pytest.raises(tp.TpsError) as e:
+            tp.tps_partition(*args)
+        assert e.value.status == tp.binding.TPS_EINVAL
+
+
+def test_status_strings(tp):
+    lib = tp.lib
+    assert lib.tps_status_string(0) == b"ok"
+    assert lib.tps_status_string(1) == b"invalid argument"
+    assert lib.tps_version().startswith(b"tpshard")
+
+
+ALIGNED = 1 << 20  # a fake, 16-byte aligned address: validation fails before any use
+
+
+@pytest.mark.parametrize("case", [
+    ("tp_mlp_fwd", (1, 0, 64, 128, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),   # M = 0
+    ("tp_mlp_fwd", (1, 8, 60, 128, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),   # h % 8
+    ("tp_mlp_fwd", (1, 8, 64, 128, None, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),      # null X
+    ("tp_mlp_fwd", (1, 8, 64, 128, ALIGNED + 2, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),  # misaligned
+    ("tp_mlp_fwd", (7, 8, 64, 128, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),   # bad dtype
+    ("tied_logits", (1, 16, 64, 150, 144, ALIGNED, ALIGNED, ALIGNED, None)),                      # ldl < v_rows
+    ("tied_logits", (1, 16, 64, 150, 154, ALIGNED, ALIGNED, ALIGNED, None)),                      # ldl % 8
+    ("vocab_embed_fwd", (1, 16, 64, 0, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # v_rows = 0
+    ("vocab_embed_fwd", (1, 16, 64, -1, 10, ALIGNED, ALIGNED, ALIGNED, None)),                    # v_start < 0
+    ("tp_attn_fwd", (1, 1, 64, 256, 2, 64, 1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, None)),
+    ("layernorm_fwd", (1, 4, 0, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),
+])
+def test_validation_rejects_before_enqueue(tp, case):
+    name, args = case
+    st = getattr(tp.lib, name)(*args)
+    assert st == tp.binding.TPS_EINVAL, (name, st, tp.lib.tps_last_error())
+    assert tp.lib.tps_last_error().startswith(name.encode())
+
+
+def test_shard_reduce_validation(tp):
+    lib = tp.lib
+    arr = (ctypes.c_void_p * 9)(*([ALIGNED] * 9))
+    assert lib.shard_reduce(1, 1, 0, arr, ALIGNED, 16, None) == tp.binding.TPS_EINVAL
+    assert lib.shard_reduce(1, 1, 9, arr, ALIGNED, 16, None) == tp.binding.TPS_EINVAL
+    arr2 = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED + 4)
+    assert lib.shard_reduce(1, 1, 2, arr2, ALIGNED, 16, None) == tp.binding.TPS_EINVAL
+    assert lib.shard_reduce(1, 1, 2, arr, ALIGNED, -1, None) == tp.binding.TPS_EINVAL
+
+
+def test_workspace_queries_and_too_small_workspace(tp):
+    lib = tp.lib
+    assert lib.tp_mlp_bwd_workspace(1, 2048, 1024, 2048) == 2048 * 2048 * 2
+    assert lib.vocab_embed_bwd_workspace(16384, 25129) == 16384 * 8
+    assert lib.vocab_embed_bwd_workspace(20000, 25129) == 32768 * 8
+    assert lib.layernorm_bwd_workspace(2048, 4096) == 256 * 2 * 4096 * 4
+    need = lib.tp_mlp_bwd_workspace(1, 8, 64, 128)
+    st = lib.tp_mlp_bwd(1, 8, 64, 128, *([ALIGNED] * 10), need - 1, None)
+    assert st == tp.binding.TPS_EWORKSPACE
+    ws = lib.tp_attn_bwd_workspace(1, 1, 2048, 4096, 4, 512)
+    assert ws >= 2048 * 4 * 512 * 2 + 4 * 2048 * 4 + 2 * 4 * 2048 * 2048 * 2 + 2048 * 3 * 2048 * 2
+    st = lib.tp_attn_bwd(1, 1, 2048, 4096, 4, 512, 1, *([ALIGNED] * 11), ws - 1, None)
+    assert st == tp.binding.TPS_EWORKSPACE
+
+
+def test_attention_fp32_is_reported_unsupported(tp):
+    st = tp.lib.tp_attn_fwd(0, 1, 16, 64, 2, 64, 1, *([ALIGNED] * 7), None)
+    assert st == tp.binding.TPS_EUNSUPPORTED

@@ -1,0 +1,189 @@
+"""GPU parity: shard_reduce and the vocab-parallel embedding (forward gather,
+input-side backward) against the fp64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpuutil import BF16_TOL, F32_TOL, empty, ids_dev, raw_bits, rel_err, say, to_dev, to_f64, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tp():
+    import megatron_tensor_transformer_columnparallel_amd as tp
+    return tp
+
+
+# ------------------------------------------------------------------ shard_reduce
+
+@pytest.mark.parametrize("n", [1, 7, 8, 4096 + 5, 1_000_003])
+def test_shard_reduce_two_bf16_parts_bit_exact(tp, n):
+    say(f"shard_reduce bf16 N=2 n={n}")
+    a = synth.make(90, 0, (n,), 3.0, "bf16")
+    b = synth.make(90, 1, (n,), 1.0, "bf16")
+    out = empty((n,), torch.bfloat16)
+    tp.shard_reduce([to_dev(a), to_dev(b)], out)
+    ref = O.round_to_bf16(O.shard_reduce([a.f64, b.f64]))
+    got = to_f64(out)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+
+
+@pytest.mark.parametrize("np_", [3, 5, 8])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_shard_reduce_many_parts(tp, np_, dt):
+    n = 100_001
+    say(f"shard_reduce {dt} N={np_} n={n}")
+    parts = [synth.make(91, i, (n,), 1.0, dt) for i in range(np_)]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = empty((n,), tdt)
+    tp.shard_reduce([to_dev(p) for p in parts], out)
+    ref = O.shard_reduce([p.f64 for p in parts])
+    assert rel_err(to_f64(out), ref) <= (BF16_TOL if dt == "bf16" else F32_TOL)
+    if dt == "f32":
+        # fp32 accumulation of fp32 inputs: within a few fp32 ulps of the exact sum
+        assert np.max(np.abs(to_f64(out) - ref)) <= 8 * np_ * 2.0 ** -23 * np.max(np.abs(ref))
+
+
+def test_shard_reduce_in_place_and_mixed_types(tp):
+    n = 12345
+    say("shard_reduce in place (out = parts[0]) and bf16 -> fp32")
+    a = synth.make(92, 0, (n,), 1.0, "bf16")
+    b = synth.make(92, 1, (n,), 1.0, "bf16")
+    da, db = to_dev(a), to_dev(b)
+    out32 = empty((n,), torch.float32)
+    tp.shard_reduce([da, db], out32)
+    assert np.array_equal(to_f64(out32), O.round_to_f32(a.f64 + b.f64))
+    tp.shard_reduce([da, db], da)
+    assert np.array_equal(to_f64(da), O.round_to_bf16(a.f64 + b.f64))
+
+
+def test_shard_reduce_propagates_nan_where_the_oracle_does(tp):
+    n = 4099
+    say("shard_reduce NaN/Inf propagation")
+    a = synth.make(93, 0, (n,), 1.0, "f32")
+    b = synth.make(93, 1, (n,), 1.0, "f32")
+    a.store[17] = np.nan
+    b.store[4098] = np.inf
+    out = empty((n,), torch.float32, fill=0.0)
+    tp.shard_reduce([to_dev(a), to_dev(b)], out)
+    ref = O.shard_reduce([a.f64, b.f64])
+    got = to_f64(out)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], O.round_to_f32(ref[fin]))
+
+
+# ------------------------------------------------------------------ embedding forward
+
+def _embed_case(tp, w, T, V, H, n, dt, worked=None, table_std=1.0, ids=None):
+    inp = synth.embed_inputs(w, T, V, H, dt, table_std, worked_ids=worked)
+    if ids is not None:
+        inp["ids"] = np.asarray(ids, dtype=np.int32)
+        T = len(ids)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    E = inp["E"]
+    dids = ids_dev(inp["ids"])
+    parts, refs = [], []
+    for r in range(n):
+        s, c = O.partition(V, n, r)
+        sub = synth.Tensor(E.store[s:s + c], dt)
+        Y = empty((T, H), tdt)
+        tp.vocab_embed_fwd(dids, to_dev(sub), Y, s)
+        parts.append(Y)
+        refs.append(O.vocab_embed_forward(inp["ids"], sub.f64, s))
+    return inp, parts, refs, tdt
+
+
+def test_embed_worked_example_fp32_bit_exact(tp):
+    cfg = synth.WORKLOADS[1]
+    say("vocab_embed_fwd workload 1 (V=300, tokens [0,212,7,9] + 60 seeded)")
+    inp, parts, refs, tdt = _embed_case(tp, 1, cfg["T"], cfg["V"], cfg["H"], cfg["n"], "f32",
+                                        worked=cfg["worked_ids"])
+    for r in range(2):
+        got = to_f64(parts[r])
+        assert np.array_equal(got, refs[r])
+        found = [int(np.any(got[t] != 0)) for t in range(4)]
+        assert found == ([1, 0, 1, 1] if r == 0 else [0, 1, 0, 0])
+    out = empty(parts[0].shape, tdt)
+    tp.shard_reduce(parts, out)
+    assert np.array_equal(to_f64(out), O.shard_reduce(refs))
+    assert np.array_equal(to_f64(out), inp["E"].f64[inp["ids"]])
+
+
+def test_embed_out_of_range_ids_write_zero_rows(tp):
+    say("vocab_embed_fwd out-of-range ids")
+    ids = [-5, 0, 299, 300, 2**31 - 1, -(2**31), 150, 149]
+    inp, parts, refs, _ = _embed_case(tp, 94, len(ids), 300, 64, 2, "bf16", ids=ids)
+    for r in range(2):
+        assert np.array_equal(to_f64(parts[r]), refs[r])
+        assert np.all(raw_bits(parts[r])[[0, 3, 4, 5]] == 0)   # +0.0 bit patterns
+
+
+def test_embed_ragged_bf16_three_shards(tp):
+    say("vocab_embed_fwd bf16 V=1001 N=3 T=777 H=136")
+    inp, parts, refs, tdt = _embed_case(tp, 95, 777, 1001, 136, 3, "bf16")
+    for r in range(3):
+        assert np.array_equal(to_f64(parts[r]), refs[r])
+    out = empty(parts[0].shape, tdt)
+    tp.shard_reduce(parts, out)
+    assert np.array_equal(to_f64(out), inp["E"].f64[inp["ids"]])
+
+
+# ------------------------------------------------------------------ embedding backward
+
+def _embed_bwd(tp, ids, dY, s, c, H, init=None):
+    dids = ids_dev(ids)
+    dE = torch.zeros((c, H), dtype=torch.float32, device="cuda") if init is None else to_dev(init).clone()
+    ws = workspace(tp.vocab_embed_bwd_workspace(len(ids), c))
+    tp.vocab_embed_bwd(dids, to_dev(dY), dE, s, ws)
+    return dE
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_embed_bwd_workload1(tp, dt):
+    cfg = synth.WORKLOADS[1]
+    say(f"vocab_embed_bwd workload-1 shapes dt={dt}")
+    inp = synth.embed_inputs(1, cfg["T"], cfg["V"], cfg["H"], dt, 1.0, worked_ids=cfg["worked_ids"])
+    for r in range(2):
+        s, c = O.partition(cfg["V"], 2, r)
+        dE = _embed_bwd(tp, inp["ids"], inp["dY"], s, c, cfg["H"])
+        ref = O.vocab_embed_backward(inp["ids"], inp["dY"].f64, s, c)
+        assert rel_err(to_f64(dE), ref) <= F32_TOL   # fp32 accumulation of exact inputs
+
+
+def test_embed_bwd_accumulates_and_handles_duplicates_and_out_of_range(tp):
+    say("vocab_embed_bwd heavy duplicates, out-of-range ids, accumulate into existing dE")
+    g = synth.rng(96, 0)
+    T, H, V = 5000, 72, 37
+    ids = g.integers(-4, V + 4, T).astype(np.int32)
+    ids[:600] = 3                       # one long segment
+    dY = synth.make(96, 1, (T, H), 1.0, "bf16")
+    for r in range(2):
+        s, c = O.partition(V, 2, r)
+        init = synth.make(96, 2 + r, (c, H), 1.0, "f32")
+        dE = _embed_bwd(tp, ids, dY, s, c, H, init=init)
+        ref = init.f64 + O.vocab_embed_backward(ids, dY.f64, s, c)
+        assert rel_err(to_f64(dE), ref) <= 1e-5
+        dE2 = _embed_bwd(tp, ids, dY, s, c, H, init=init)
+        assert np.array_equal(raw_bits(dE), raw_bits(dE2)), "not deterministic"
+
+
+@pytest.mark.parametrize("T", [1, 2, 8191, 8193, 20000])
+def test_embed_bwd_sort_sizes(tp, T):
+    """Sizes around the in-LDS sort chunk (8192) exercise the global merge passes."""
+    say(f"vocab_embed_bwd T={T}")
+    V, H = 3001, 64
+    ids = synth.uniform_ids(97, T, T, V + 50) - 25
+    dY = synth.make(97, 1, (T, H), 1.0, "bf16")
+    s, c = O.partition(V, 2, 1)
+    dE = _embed_bwd(tp, ids, dY, s, c, H)
+    ref = O.vocab_embed_backward(ids, dY.f64, s, c)
+    assert rel_err(to_f64(dE), ref) <= 1e-5
+    got = to_f64(dE)
+    untouched = np.all(ref == 0, axis=1)
+    assert np.all(got[untouched] == 0)
