@@ -42,7 +42,7 @@ def run_mlp_shard(tp, X, A_r, B_r, dZ, tdt):
 
 @pytest.mark.parametrize("w,M,h,f,n,dt", [
     (1, 8, 64, 256, 2, "f32"),          # workload 1 (fp32)
-    (81, 100, 72, 136, 2, "bf16"),      # ragged: rows and columns not tile multiples
+    (81, 100, 72, 144, 2, "bf16"),      # ragged: rows and columns not tile multiples
     (82, 333, 64, 8000, 2, "bf16"),     # 4000-wide shard: M x f_i GEMMs take the 256x256 tile
     (83, 130, 128, 384, 3, "bf16"),     # three shards
 ])
