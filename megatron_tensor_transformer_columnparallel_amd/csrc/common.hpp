@@ -97,6 +97,50 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float v[4], int n
   }
 }
 
+// 8 consecutive elements <-> fp32 (16-byte aligned for bf16, 32 for fp32),
+// element-wise when fewer than 8 are valid.
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float v[8], int nvalid) {
+  if (nvalid >= 8) {
+    store4<T>(p, v, 4);
+    store4<T>(p + 4, v + 4, 4);
+  } else {
+    store4<T>(p, v, nvalid);
+    if (nvalid > 4) store4<T>(p + 4, v + 4, nvalid - 4);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float v[8], int nvalid) {
+  if (nvalid >= 8) {
+    load4<T>(p, v, 4);
+    load4<T>(p + 4, v + 4, 4);
+  } else {
+    load4<T>(p, v, nvalid);
+    if (nvalid > 4) load4<T>(p + 4, v + 4, nvalid - 4);
+    else { v[4] = v[5] = v[6] = v[7] = 0.f; }
+  }
+}
+template <>
+__device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float v[8], int nvalid) {
+  if (nvalid >= 8) {
+    u32x4_t x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+    *reinterpret_cast<u32x4_t*>(p) = x;
+  } else {
+    for (int i = 0; i < nvalid; ++i) p[i] = f32_to_bf16(v[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8], int nvalid) {
+  if (nvalid >= 8) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { v[2 * w] = bf16lo(x[w]); v[2 * w + 1] = bf16hi(x[w]); }
+  } else {
+    for (int i = 0; i < 8; ++i) v[i] = i < nvalid ? bf16_to_f32(p[i]) : 0.f;
+  }
+}
+
 // GELU with the exact erf form and its derivative (fp32).
 __device__ __forceinline__ float gelu_f(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
