@@ -22,19 +22,121 @@
 
 namespace tps {
 
-constexpr int kFlashBQ = 64;    // queries per workgroup (4 waves x 16)
+constexpr int kFlashBQ = 64;    // queries per workgroup: 4 query groups of 16
 constexpr int kFlashBKey = 32;  // keys per LDS block
+constexpr int kFlashThreads = 512;  // 8 waves: (query group, half of the head dim)
+// The running max used as the softmax reference is only raised when a row's
+// block max exceeds it by more than this many powers of two (log2 domain):
+// numerator and denominator share the reference, so the result is exact and
+// every exp2 stays below 2^kLazyRescale.
+constexpr float kLazyRescale = 8.f;
 
+// LDS stage: one K block (keys x head dim) and one V^T block (head dim x keys).
 template <int D>
-__global__ void __launch_bounds__(256, 1)
+struct FlashStage {
+  static constexpr int KLD = D + 8;           // LDS row stride of K (elements)
+  static constexpr int VLD = kFlashBKey + 8;  // LDS row stride of V^T
+  static constexpr int K_ELEMS = kFlashBKey * KLD;
+  static constexpr int ELEMS = K_ELEMS + D * VLD;
+  static constexpr int K_CHUNKS = kFlashBKey * (D / 8);         // 16-byte chunks of K
+  static constexpr int V_BLOCKS = (kFlashBKey / 8) * (D / 8);   // 8x8 blocks of V
+  // Threads [0, V_THREADS) transpose V blocks, the others copy K chunks.
+  static constexpr int V_THREADS = V_BLOCKS < kFlashThreads / 2 ? V_BLOCKS : kFlashThreads / 2;
+  static constexpr int VB = (V_BLOCKS + V_THREADS - 1) / V_THREADS;
+  static constexpr int K_THREADS = kFlashThreads - V_THREADS;
+  static constexpr int KV = (K_CHUNKS + K_THREADS - 1) / K_THREADS;
+  static constexpr int REGS = (KV > 8 * VB ? KV : 8 * VB);
+};
+
+// Register staging of the next K/V block (global -> registers during the
+// current block's MFMAs, registers -> the other LDS stage afterwards).
+template <int D>
+struct FlashPrefetch {
+  using S = FlashStage<D>;
+  u32x4_t r[S::REGS];
+
+  __device__ __forceinline__ void load(const bf16_t* Kp, const bf16_t* Vp, int64_t ld, int k0, int sq, int tid) {
+    if (tid < S::V_THREADS) {
+#pragma unroll
+      for (int b = 0; b < S::VB; ++b) {
+        const int blk = tid + b * S::V_THREADS;
+        const int kq = blk % (kFlashBKey / 8), db = blk / (kFlashBKey / 8);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int key = k0 + kq * 8 + jj;
+          u32x4_t x = {0u, 0u, 0u, 0u};
+          if (blk < S::V_BLOCKS && key < sq) x = *reinterpret_cast<const u32x4_t*>(Vp + (int64_t)key * ld + db * 8);
+          r[b * 8 + jj] = x;
+        }
+      }
+    } else {
+      const int t = tid - S::V_THREADS;
+#pragma unroll
+      for (int i = 0; i < S::KV; ++i) {
+        const int c = t + i * S::K_THREADS;
+        const int row = c / (D / 8), cc = (c % (D / 8)) * 8;
+        const int key = k0 + row;
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (c < S::K_CHUNKS && key < sq) x = *reinterpret_cast<const u32x4_t*>(Kp + (int64_t)key * ld + cc);
+        r[i] = x;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16_t* st, int tid) const {
+    if (tid < S::V_THREADS) {
+      bf16_t* vts = st + S::K_ELEMS;
+#pragma unroll
+      for (int b = 0; b < S::VB; ++b) {
+        const int blk = tid + b * S::V_THREADS;
+        if (blk >= S::V_BLOCKS) continue;
+        const int kq = blk % (kFlashBKey / 8), db = blk / (kFlashBKey / 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int w = i >> 1;
+          const bool hi = i & 1;
+          u32x4_t o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t a = r[b * 8 + 2 * q][w], c = r[b * 8 + 2 * q + 1][w];
+            o[q] = hi ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
+          }
+          *reinterpret_cast<u32x4_t*>(vts + (db * 8 + i) * S::VLD + kq * 8) = o;
+        }
+      }
+    } else {
+      const int t = tid - S::V_THREADS;
+#pragma unroll
+      for (int i = 0; i < S::KV; ++i) {
+        const int c = t + i * S::K_THREADS;
+        if (c < S::K_CHUNKS) {
+          const int row = c / (D / 8), cc = (c % (D / 8)) * 8;
+          *reinterpret_cast<u32x4_t*>(st + row * S::KLD + cc) = r[i];
+        }
+      }
+    }
+  }
+};
+
+// One workgroup per (batch, head, 64-query block); 8 waves.  Wave w handles
+// the 16 queries of group w % 4 and accumulates the head-dim half w / 4 of
+// O^T = V^T P^T; both waves of a group compute the same S^T = K Q^T (with the
+// group's Q fragments in registers) and the same online-softmax statistics.
+// The transposed formulation makes the S^T result layout (one query per lane
+// column) directly the B operand of the PV MFMA, so P never leaves registers
+// and the per-query rescale is lane-local.  K and V^T blocks are double
+// buffered in LDS; the next block is fetched into registers while the current
+// one is consumed.  Saves lse = log(sum exp(S)) per query for the backward.
+template <int D>
+__global__ void __launch_bounds__(kFlashThreads, 1)
 flash_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int sq,
                  int hs, int causal, float scale_log2) {
-  constexpr int KLD = D + 8;             // LDS row stride of the K block
-  constexpr int VLD = kFlashBKey + 8;    // LDS row stride of the V^T block
+  using S = FlashStage<D>;
   constexpr int DK = D / 32;             // MFMA k-steps over the head dim
-  constexpr int DT = D / 16;             // 16-row tiles of O^T
-  __shared__ __attribute__((aligned(16))) bf16_t ks[kFlashBKey * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t vts[D * VLD];
+  constexpr int DH = D / 2;              // head-dim half accumulated per wave
+  constexpr int DT = DH / 16;            // 16-row tiles of this wave's O^T
+  constexpr int NCH = DK >= 2 ? 2 : 1;   // independent partial sums per S tile
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * S::ELEMS];
 
   const int64_t ld = 3LL * hs * D;       // row stride of QKV
   const int64_t ldo = (int64_t)hs * D;   // row stride of O
@@ -48,8 +150,9 @@ flash_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float
   const bf16_t* Vp = Qp + 2LL * hs * D;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qg = wave & 3, dh = wave >> 2;
   const int g = lane >> 4;                       // lane group 0..3
-  const int myq = qb * kFlashBQ + wave * 16 + (lane & 15);
+  const int myq = qb * kFlashBQ + qg * 16 + (lane & 15);
 
   // Q^T fragments (B operand): column = my query, k = head-dim slice.
   bf16x8_t qf[DK];
@@ -66,54 +169,32 @@ flash_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float
 
   const int kend = causal ? min(sq, (qb + 1) * kFlashBQ) : sq;
   const int nkb = (kend + kFlashBKey - 1) / kFlashBKey;
+  FlashPrefetch<D> pf;
+  pf.load(Kp, Vp, ld, 0, sq, tid);
+  pf.store(lds, tid);
+  __syncthreads();
+
   for (int kb = 0; kb < nkb; ++kb) {
     const int k0 = kb * kFlashBKey;
-    __syncthreads();  // previous block fully consumed
-    // K block -> LDS, rows = keys, 16-byte chunks along the head dim.
-    for (int c = tid; c < kFlashBKey * (D / 8); c += 256) {
-      const int row = c / (D / 8), cc = (c % (D / 8)) * 8;
-      const int key = k0 + row;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (key < sq) x = *reinterpret_cast<const u32x4_t*>(Kp + (int64_t)key * ld + cc);
-      *reinterpret_cast<u32x4_t*>(ks + row * KLD + cc) = x;
-    }
-    // V block -> LDS transposed (rows = head dim, columns = keys), 8x8 blocks.
-    for (int blk = tid; blk < (kFlashBKey / 8) * (D / 8); blk += 256) {
-      const int kq = blk % (kFlashBKey / 8), db = blk / (kFlashBKey / 8);
-      u32x4_t v[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int key = k0 + kq * 8 + jj;
-        v[jj] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key < sq) v[jj] = *reinterpret_cast<const u32x4_t*>(Vp + (int64_t)key * ld + db * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int w = i >> 1;
-        const bool hi = i & 1;
-        u32x4_t o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a = v[2 * q][w], c = v[2 * q + 1][w];
-          o[q] = hi ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-        }
-        *reinterpret_cast<u32x4_t*>(vts + (db * 8 + i) * VLD + kq * 8) = o;
-      }
-    }
-    __syncthreads();
+    const bf16_t* st = lds + (kb & 1) * S::ELEMS;
+    const bool more = kb + 1 < nkb;
+    if (more) pf.load(Kp, Vp, ld, k0 + kFlashBKey, sq, tid);   // lands during this block's MFMAs
 
     // S^T tiles: rows = 16 keys, column = this lane's query.
-    f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    f32x4_t sp[2][NCH];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16_t* krow = ks + (t * 16 + (lane & 15)) * KLD + g * 8;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(krow + kk * 32);
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], st[t], 0, 0, 0);
+      for (int c = 0; c < NCH; ++c) sp[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(st + (t * 16 + (lane & 15)) * S::KLD + g * 8 + kk * 32);
+        sp[t][kk % NCH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], sp[t][kk % NCH], 0, 0, 0);
       }
-    }
-    // Online softmax in the log2 domain.  Element e of st[t] is key
+    // Online softmax in the log2 domain.  Element e of tile t is key
     // k0 + 16t + 4g + e.
     float sv[8];
     float mx = -INFINITY;
@@ -121,54 +202,66 @@ flash_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x += sp[t][c][e];
         const int key = k0 + t * 16 + g * 4 + e;
-        float x = st[t][e] * scale_log2;
+        x *= scale_log2;
         if (key >= sq || (causal && key > myq)) x = -INFINITY;
         sv[t * 4 + e] = x;
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    // Raise the reference (and rescale O) only when a row's max outgrew it;
+    // the first block always raises it from -inf (key 0 is never masked).
+    const bool grow = mx > m_run + kLazyRescale;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        oacc[t][0] *= alpha; oacc[t][1] *= alpha; oacc[t][2] *= alpha; oacc[t][3] *= alpha;
+      }
+      m_run = m_new;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sv[i] = exp2f(sv[i] - m_new);
+      sv[i] = exp2f(sv[i] - m_run);
       rs += sv[i];
     }
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      oacc[t][0] *= alpha; oacc[t][1] *= alpha; oacc[t][2] *= alpha; oacc[t][3] *= alpha;
-    }
+    l_run += rs;
     // P^T as the B operand: k-slots 0..3 = keys 4g..4g+3, 4..7 = keys 16+4g..16+4g+3.
     const u32x4_t pw = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
                         pack_bf16x2(sv[6], sv[7])};
-    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-    // O^T += V^T P^T; the A fragment uses the same key order as pf.
+    const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, pw);
+    // O^T (this wave's head-dim half) += V^T P^T; A fragment in pfrag's key order.
+    const bf16_t* vts = st + S::K_ELEMS + dh * DH * S::VLD;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      const bf16_t* vrow = vts + (t * 16 + (lane & 15)) * VLD + g * 4;
+      const bf16_t* vrow = vts + (t * 16 + (lane & 15)) * S::VLD + g * 4;
       const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
       const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
       const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, oacc[t], 0, 0, 0);
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pfrag, oacc[t], 0, 0, 0);
     }
+    if (more) pf.store(lds + ((kb + 1) & 1) * S::ELEMS, tid);
+    __syncthreads();
   }
 
   if (myq < sq) {
     const float inv = 1.f / l_run;
-    bf16_t* orow = out + ((int64_t)bi * sq + myq) * ldo + (int64_t)j * D;
+    bf16_t* orow = out + ((int64_t)bi * sq + myq) * ldo + (int64_t)j * D + dh * DH;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       const float v[4] = {oacc[t][0] * inv, oacc[t][1] * inv, oacc[t][2] * inv, oacc[t][3] * inv};
       store4<bf16_t>(orow + t * 16 + g * 4, v, 4);
     }
-    if (g == 0) lse[((int64_t)bi * hs + j) * sq + myq] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    if (g == 0 && dh == 0) lse[((int64_t)bi * hs + j) * sq + myq] = (m_run + log2f(l_run)) * 0.69314718055994531f;
   }
 }
 
@@ -202,7 +295,8 @@ static tps_status launch_flash_fwd(const bf16_t* qkv, bf16_t* out, float* lse, i
                                    int causal, hipStream_t st) {
   const int64_t grid = ceil_div(sq, kFlashBQ) * hs * b;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(flash_fwd_kernel<D>, dim3((unsigned)grid), dim3(256), 0, st, qkv, out, lse, (int)sq, (int)hs,
+  hipLaunchKernelGGL(flash_fwd_kernel<D>, dim3((unsigned)grid), dim3(kFlashThreads), 0, st, qkv, out, lse, (int)sq,
+                     (int)hs,
                      causal, scale_log2);
   return check_launch("flash_fwd_kernel");
 }
