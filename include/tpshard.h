@@ -158,6 +158,21 @@ tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t h
 tps_status shard_reduce(tps_dtype in_dt, tps_dtype out_dt, int n_parts,
                         const void* const* parts, void* out, int64_t n, tps_stream_t stream);
 
+/*
+ * shard_reduce_add: the shard-partial sum fused with a residual add, for a
+ * residual stream kept in a wider type than the partials:
+ *   s      = res[i] + sum_{r=0}^{n_parts-1} parts[r][i]   (fp32, in that order)
+ *   out[i] = round_out_dt(s);  out_copy[i] = round_copy_dt(s) if out_copy != NULL
+ * res of res_dt, parts of part_dt (1 <= n_parts <= 7), out of out_dt (may equal
+ * res), optional out_copy of copy_dt (e.g. a bf16 copy that feeds the next
+ * GEMM).  The pages' layer sums the 'g' all-reduce into the residual
+ * (page "5-megatron", section RowParallelLinear: the reduce's result is the
+ * layer output the residual connection adds).
+ */
+tps_status shard_reduce_add(tps_dtype res_dt, const void* res, tps_dtype part_dt, int n_parts,
+                            const void* const* parts, tps_dtype out_dt, void* out,
+                            tps_dtype copy_dt, void* out_copy, int64_t n, tps_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * (4) Vocab-parallel word embedding and the tied output projection.
  * Page "5-megatron", section VocabParallelEmbedding: ids outside this shard's
@@ -210,21 +225,23 @@ tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, i
  * LayerNorm (replicated on every shard), for stacking layers.  Page
  * "5-megatron", section 训练一般流程 counts two LayerNorms of 2H parameters
  * per layer; the formula is the standard one with biased variance:
- *   y = (x - mean) / sqrt(var + eps) * gamma + beta   (per row of H)
- * layernorm_fwd: x, y [M x H] of dt; gamma, beta [H] fp32; mean, rstd [M] fp32
- * outputs kept for the backward pass.
- * layernorm_bwd: dx [M x H] of dt; dgamma, dbeta [H] fp32 OVERWRITTEN.
+ *   y = (x - mean) / sqrt(var + eps) * gamma + beta   (per row of H, fp32 math)
+ * layernorm_fwd: x [M x H] of x_dt, y [M x H] of y_dt (e.g. an fp32 residual
+ * stream in, bf16 GEMM input out); gamma, beta [H] fp32; mean, rstd [M] fp32
+ * outputs kept for the backward pass.  H <= 8192 (TPS_EUNSUPPORTED above).
+ * layernorm_bwd: dy of dy_dt, dx of dx_dt; dgamma, dbeta [H] fp32 OVERWRITTEN
+ * (reduced over rows in a fixed order through the workspace).
  * ------------------------------------------------------------------------ */
-tps_status layernorm_fwd(tps_dtype dt, int64_t M, int64_t H, float eps, const void* x,
+tps_status layernorm_fwd(tps_dtype x_dt, tps_dtype y_dt, int64_t M, int64_t H, float eps, const void* x,
                          const float* gamma, const float* beta, void* y, float* mean,
                          float* rstd, tps_stream_t stream);
 
 size_t layernorm_bwd_workspace(int64_t M, int64_t H);
 
-tps_status layernorm_bwd(tps_dtype dt, int64_t M, int64_t H, const void* x, const float* gamma,
-                         const float* mean, const float* rstd, const void* dy, void* dx,
-                         float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
-                         tps_stream_t stream);
+tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype dx_dt, int64_t M, int64_t H,
+                         const void* x, const float* gamma, const float* mean, const float* rstd,
+                         const void* dy, void* dx, float* dgamma, float* dbeta, void* ws,
+                         size_t ws_bytes, tps_stream_t stream);
 
 #ifdef __cplusplus
 }

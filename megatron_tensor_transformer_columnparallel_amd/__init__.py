@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     tps_partition, tps_version,
     tp_mlp_fwd, tp_mlp_bwd, tp_mlp_bwd_workspace,
     tp_attn_fwd, tp_attn_bwd, tp_attn_bwd_workspace,
-    shard_reduce,
+    shard_reduce, shard_reduce_add,
     vocab_embed_fwd, vocab_embed_bwd, vocab_embed_bwd_workspace,
     tied_logits, tied_logits_bwd,
     layernorm_fwd, layernorm_bwd, layernorm_bwd_workspace,

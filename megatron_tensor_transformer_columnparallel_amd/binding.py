@@ -34,14 +34,16 @@ SIGNATURES = {
     "tp_attn_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _sz, _vp]),
     "shard_reduce": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), _vp, _i64, _vp]),
+    "shard_reduce_add": (_i32, [_i32, _vp, _i32, _i32, ctypes.POINTER(_vp), _i32, _vp, _i32, _vp, _i64, _vp]),
     "vocab_embed_fwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "vocab_embed_bwd_workspace": (_sz, [_i64, _i64]),
     "vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tied_logits": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "layernorm_fwd": (_i32, [_i32, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "layernorm_fwd": (_i32, [_i32, _i32, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "layernorm_bwd_workspace": (_sz, [_i64, _i64]),
-    "layernorm_bwd": (_i32, [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "layernorm_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                             _vp]),
 }
 
 
@@ -197,6 +199,26 @@ def shard_reduce(parts, out, stream=None):
     _check(lib.shard_reduce(in_dt, _dt(out), len(parts), arr, _p(out), n, _stream(stream)), "shard_reduce")
 
 
+def shard_reduce_add(res, parts, out, out_copy=None, stream=None):
+    """out = res + sum(parts) in fp32 (in that order), rounded to out's dtype;
+    optionally also written rounded to out_copy's dtype."""
+    if not 1 <= len(parts) <= 7:
+        raise ValueError("1..7 parts")
+    pdt = _dt(parts[0])
+    _same(pdt, *parts)
+    _contig(res, out, *parts)
+    n = out.numel()
+    assert res.numel() == n and all(p.numel() == n for p in parts)
+    cdt = TPS_BF16
+    if out_copy is not None:
+        _contig(out_copy)
+        assert out_copy.numel() == n
+        cdt = _dt(out_copy)
+    arr = (_vp * len(parts))(*[_p(p) for p in parts])
+    _check(lib.shard_reduce_add(_dt(res), _p(res), pdt, len(parts), arr, _dt(out), _p(out), cdt, _p(out_copy), n,
+                                _stream(stream)), "shard_reduce_add")
+
+
 # ------------------------------------------------------------------ embedding
 
 def vocab_embed_fwd(ids, E_r, Y_r, v_start, stream=None):
@@ -252,10 +274,11 @@ def tied_logits_bwd(X, E_r, dL_r, dX_r, dE_r, stream=None):
 # ------------------------------------------------------------------ LayerNorm
 
 def layernorm_fwd(x, gamma, beta, y, mean, rstd, eps=1e-5, stream=None):
-    dt = _dt(x)
+    """x and y may differ in dtype (e.g. an fp32 residual stream in, bf16 out)."""
     _contig(x, gamma, beta, y, mean, rstd)
     M, H = x.shape
-    _check(lib.layernorm_fwd(dt, M, H, eps, _p(x), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd),
+    assert y.shape == (M, H)
+    _check(lib.layernorm_fwd(_dt(x), _dt(y), M, H, eps, _p(x), _p(gamma), _p(beta), _p(y), _p(mean), _p(rstd),
                              _stream(stream)), "layernorm_fwd")
 
 
@@ -264,8 +287,10 @@ def layernorm_bwd_workspace(M, H) -> int:
 
 
 def layernorm_bwd(x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws, stream=None):
-    dt = _dt(x)
+    """x, dy and dx may each be fp32 or bf16."""
     _contig(x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws)
     M, H = x.shape
-    _check(lib.layernorm_bwd(dt, M, H, _p(x), _p(gamma), _p(mean), _p(rstd), _p(dy), _p(dx), _p(dgamma),
-                             _p(dbeta), _p(ws), ws.numel() * ws.element_size(), _stream(stream)), "layernorm_bwd")
+    assert dy.shape == (M, H) and dx.shape == (M, H)
+    _check(lib.layernorm_bwd(_dt(x), _dt(dy), _dt(dx), M, H, _p(x), _p(gamma), _p(mean), _p(rstd), _p(dy), _p(dx),
+                             _p(dgamma), _p(dbeta), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "layernorm_bwd")

@@ -12,9 +12,10 @@
 //
 // Backward core: the probabilities are recomputed from lse tile by tile by
 // the GEMM kernel (epilogue exp(S*scale - lse)) and written to the workspace
-// in bf16 together with dS = P * (dO V^T - delta) * scale; dV = P^T dO,
-// dQ = dS K and dK = dS^T Q are then MFMA GEMMs whose K-loops skip the
-// causally-zero blocks.  The workspace holds O(sq^2) per head, which the
+// in bf16; dP = dO V^T is a GEMM into fp32 and a row pass forms
+// dS = P * (dP - delta) * scale with delta taken from the same P and dP;
+// dV = P^T dO, dQ = dS K and dK = dS^T Q are then MFMA GEMMs whose K-loops
+// skip the causally-zero blocks.  The workspace holds O(sq^2) per head, which the
 // 288 GB of HBM per device affords at these sequence lengths.
 #include <string>
 
@@ -265,28 +266,42 @@ flash_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float
   }
 }
 
-// delta[(b*hs + j)*sq + q] = sum_c dO[b*sq+q][j*D + c] * O[b*sq+q][j*D + c]; one wave per row/head.
-__global__ void __launch_bounds__(256) attn_delta_kernel(const bf16_t* __restrict__ dO, const bf16_t* __restrict__ O,
-                                                         float* __restrict__ delta, int64_t rows, int sq, int hs,
-                                                         int D) {
+// One wavefront per row of one (batch, head): with P the stored (bf16)
+// probabilities and dP = dO V^T (fp32), delta = sum_j P_j dP_j / sum_j P_j and
+// dS_j = P_j (dP_j - delta) * scale.  Taking delta from the same P and dP
+// makes every row of dS sum to zero (the softmax gradient of the stored P),
+// so the rounding of O and dO does not leak into dQ as a per-row bias.
+// Columns at or beyond the causal limit (and beyond sq) are written as 0.
+__global__ void __launch_bounds__(256) attn_ds_kernel(const bf16_t* __restrict__ P, const float* __restrict__ dP,
+                                                      bf16_t* __restrict__ dS, int64_t rows, int sq, int64_t ldp,
+                                                      int causal, float scale) {
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= rows * hs) return;
+  if (w >= rows) return;
   const int lane = threadIdx.x & 63;
-  const int64_t row = w / hs;
-  const int j = (int)(w % hs);
-  const int64_t off = row * (int64_t)hs * D + (int64_t)j * D;
-  float acc = 0.f;
-  for (int c = lane * 8; c < D; c += 64 * 8) {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(dO + off + c);
-    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(O + off + c);
+  const int i = (int)(w % sq);                    // query index within its head
+  const int ncol = causal ? i + 1 : sq;
+  const bf16_t* pr = P + w * ldp;
+  const float* dpr = dP + w * ldp;
+  bf16_t* dsr = dS + w * ldp;
+  float num = 0.f, den = 0.f;
+  for (int c = lane * 8; c < ncol; c += 64 * 8) {
+    float p[8], d[8];
+    load8<bf16_t>(pr + c, p, min(8, ncol - c));
+    load8<float>(dpr + c, d, min(8, ncol - c));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc += bf16lo(a[q]) * bf16lo(b[q]) + bf16hi(a[q]) * bf16hi(b[q]);
+    for (int e = 0; e < 8; ++e) { num += p[e] * d[e]; den += p[e]; }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) {
-    const int64_t bi = row / sq, q = row % sq;
-    delta[(bi * hs + j) * sq + q] = acc;
+  for (int o = 32; o >= 1; o >>= 1) { num += __shfl_xor(num, o); den += __shfl_xor(den, o); }
+  const float delta = den > 0.f ? num / den : 0.f;
+  for (int c = lane * 8; c < sq; c += 64 * 8) {
+    const int nv = min(8, sq - c);
+    float p[8], d[8], o[8];
+    load8<bf16_t>(pr + c, p, nv);
+    load8<float>(dpr + c, d, nv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (c + e < ncol) ? p[e] * (d[e] - delta) * scale : 0.f;
+    store8<bf16_t>(dsr + c, o, nv);
   }
 }
 
@@ -313,7 +328,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // of 8 elements so that every 16-byte vector access stays aligned; the
 // padding columns are never read unmasked.
 struct AttnWs {
-  size_t dO, delta, P, dS, dQKV, total;
+  size_t dO, P, dP, dS, dQKV, total;
   int64_t ldp;
 };
 static AttnWs attn_ws_layout(int64_t b, int64_t sq, int64_t hs, int64_t d) {
@@ -321,9 +336,9 @@ static AttnWs attn_ws_layout(int64_t b, int64_t sq, int64_t hs, int64_t d) {
   const size_t M = (size_t)(b * sq);
   w.ldp = (sq + 7) / 8 * 8;
   w.dO = 0;
-  w.delta = align256(w.dO + M * hs * d * 2);
-  w.P = align256(w.delta + (size_t)b * hs * sq * 4);
-  w.dS = align256(w.P + (size_t)b * hs * sq * w.ldp * 2);
+  w.P = align256(w.dO + M * hs * d * 2);
+  w.dP = align256(w.P + (size_t)b * hs * sq * w.ldp * 2);
+  w.dS = align256(w.dP + (size_t)b * hs * sq * w.ldp * 4);
   w.dQKV = align256(w.dS + (size_t)b * hs * sq * w.ldp * 2);
   w.total = align256(w.dQKV + M * 3 * hs * d * 2);
   return w;
@@ -398,8 +413,8 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   const int64_t M = b * sq, w = hs * d, w3 = 3 * w;
   char* base = static_cast<char*>(ws);
   bf16_t* dO = (bf16_t*)(base + L.dO);
-  float* delta = (float*)(base + L.delta);
   bf16_t* P = (bf16_t*)(base + L.P);
+  float* dP = (float*)(base + L.dP);
   bf16_t* dS = (bf16_t*)(base + L.dS);
   bf16_t* dQKV = (bf16_t*)(base + L.dQKV);
   const bf16_t* qkv = (const bf16_t*)QKV_i;
@@ -412,11 +427,6 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   TPS_TRY((gemm_bf16<false, false>(o, dz, shape(w, h, M, w, h), EpiStore<bf16_t>{(bf16_t*)dWo_i, h, 0, 0}, st)));
   // dO = dZ Wo_i^T                         (NT)  [M x w], K = h
   TPS_TRY((gemm_bf16<true, true>(dz, (const bf16_t*)Wo_i, shape(M, w, h, h, h), EpiStore<bf16_t>{dO, w, 0, 0}, st)));
-  // delta = rowsum(dO * O) per head
-  hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)ceil_div(M * hs, 4)), dim3(256), 0, st, dO, o, delta, M,
-                     (int)sq, (int)hs, (int)d);
-  TPS_TRY(check_launch("attn_delta_kernel"));
-
   // Per (batch, head) problems: z = bi*hs + j.
   GemmShape s = shape(sq, sq, d, w3, w3);
   s.batch = (int)(b * hs);
@@ -428,11 +438,14 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
                                  EpiAttnProb<bf16_t>{P, lse_i, ldp, sp, (int)sq, (int)hs, causal ? 1 : 0,
                                                      scale * 1.4426950408889634f},
                                  st)));
-  // dS = P * (dO V^T - delta) * scale      (NT)  [sq x sq] per head
+  // dP = dO V^T (fp32)                    (NT)  [sq x sq] per head
   GemmShape s2 = s;
   s2.lda = w; s2.sa_o = sq * w; s2.sa_i = d;
-  TPS_TRY((gemm_bf16<true, true>(dO, qkv + 2 * w, s2,
-                                 EpiAttnDS<bf16_t>{P, dS, delta, ldp, sp, (int)sq, (int)hs, scale}, st)));
+  TPS_TRY((gemm_bf16<true, true>(dO, qkv + 2 * w, s2, EpiStore<float>{dP, ldp, hs * sp, sp}, st)));
+  // dS = P * (dP - delta) * scale with delta from the same P and dP
+  hipLaunchKernelGGL(attn_ds_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, P, dP, dS,
+                     b * hs * sq, (int)sq, ldp, causal ? 1 : 0, scale);
+  TPS_TRY(check_launch("attn_ds_kernel"));
   // dV = P^T dO                            (TN)  [sq x d] per head, K = queries >= key
   GemmShape s3 = shape(sq, d, sq, ldp, w);
   s3.batch = (int)(b * hs); s3.batch_inner = (int)hs;

@@ -100,27 +100,6 @@ struct EpiAttnProb {
   }
 };
 
-// dS(m,n) = P(m,n) * (acc - delta[m]) * scale, where acc = (dO V^T)(m,n).
-template <typename T>
-struct EpiAttnDS {
-  const T* P;
-  T* dS;
-  const float* delta;
-  int64_t ldp, sp;
-  int sq, hs;
-  float scale;
-  __device__ void operator()(int zo, int zi, int m, int n, float v[8], int nv) const {
-    const int z = zo * hs + zi;
-    const int64_t o = (int64_t)z * sp + (int64_t)m * ldp + n;
-    const float dl = delta[(int64_t)z * sq + m];
-    float p[8];
-    load8<T>(P + o, p, nv);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = p[i] * (v[i] - dl) * scale;
-    store8<T>(dS + o, v, nv);
-  }
-};
-
 // ------------------------------------------------------------------ tile order
 
 // Maps a linear workgroup id to (problem z, tile row tm, tile col tn).

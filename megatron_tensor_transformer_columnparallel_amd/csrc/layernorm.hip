@@ -13,9 +13,9 @@ namespace tps {
 constexpr int kLnMaxH = 8192;
 constexpr int kLnRowsPerBlock = 8;
 
+// 8 consecutive elements <-> fp32 registers (16 bytes of bf16, 32 of fp32).
 template <typename T> struct LnVec;
 template <> struct LnVec<bf16_t> {
-  static constexpr int V = 8;
   __device__ static void load(const bf16_t* p, float* v) {
     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
@@ -29,15 +29,18 @@ template <> struct LnVec<bf16_t> {
   }
 };
 template <> struct LnVec<float> {
-  static constexpr int V = 4;
   __device__ static void load(const float* p, float* v) {
-    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p);
-    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0], b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
   }
   __device__ static void store(float* p, const float* v) {
-    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
   }
 };
+constexpr int kLnV = 8;                          // elements per thread chunk
+constexpr int kLnNCH = kLnMaxH / kLnV / 256;     // chunks per thread
 
 // Sum over the 256 threads of a workgroup; `red` is 8 floats of LDS.
 __device__ __forceinline__ float block_sum(float x, float* red) {
@@ -50,23 +53,23 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) ln_fwd_kernel(const T* __restrict__ x, const float* __restrict__ gamma,
-                                                     const float* __restrict__ beta, T* __restrict__ y,
+template <typename TX, typename TY>
+__global__ void __launch_bounds__(256) ln_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
+                                                     const float* __restrict__ beta, TY* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int64_t H,
                                                      float eps) {
-  constexpr int V = LnVec<T>::V;
-  constexpr int NCH = kLnMaxH / V / 256;
+  constexpr int V = kLnV;
+  constexpr int NCH = kLnNCH;
   __shared__ float red[8];
   const int64_t row = blockIdx.x;
-  const T* xr = x + row * H;
+  const TX* xr = x + row * H;
   float v[NCH][V];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
     if (c < H) {
-      LnVec<T>::load(xr + c, v[i]);
+      LnVec<TX>::load(xr + c, v[i]);
 #pragma unroll
       for (int e = 0; e < V; ++e) s += v[i][e];
     }
@@ -83,7 +86,7 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const T* __restrict__ x, co
   }
   const float var = block_sum(q, red) / (float)H;
   const float rs = rsqrtf(var + eps);
-  T* yr = y + row * H;
+  TY* yr = y + row * H;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
@@ -91,19 +94,19 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const T* __restrict__ x, co
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = (v[i][e] - mu) * rs * gamma[c + e] + beta[c + e];
-      LnVec<T>::store(yr + c, o);
+      LnVec<TY>::store(yr + c, o);
     }
   }
   if (threadIdx.x == 0) { mean[row] = mu; rstd[row] = rs; }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ x, const float* __restrict__ gamma,
+template <typename TX, typename TDY, typename TDX>
+__global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
-                                                     const T* __restrict__ dy, T* __restrict__ dx,
+                                                     const TDY* __restrict__ dy, TDX* __restrict__ dx,
                                                      float* __restrict__ part, int64_t M, int64_t H) {
-  constexpr int V = LnVec<T>::V;
-  constexpr int NCH = kLnMaxH / V / 256;
+  constexpr int V = kLnV;
+  constexpr int NCH = kLnNCH;
   __shared__ float red[8];
   float pg[NCH][V], pb[NCH][V];
 #pragma unroll
@@ -122,8 +125,8 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ x, co
       const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
       if (c < H) {
         float xv[V], dv[V];
-        LnVec<T>::load(x + row * H + c, xv);
-        LnVec<T>::load(dy + row * H + c, dv);
+        LnVec<TX>::load(x + row * H + c, xv);
+        LnVec<TDY>::load(dy + row * H + c, dv);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           xh[i][e] = (xv[e] - mu) * rs;
@@ -144,7 +147,7 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ x, co
         float o[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) o[e] = rs * (gv[i][e] - m1 - xh[i][e] * m2);
-        LnVec<T>::store(dx + row * H + c, o);
+        LnVec<TDX>::store(dx + row * H + c, o);
       }
     }
   }
@@ -172,11 +175,12 @@ __global__ void __launch_bounds__(256) ln_param_reduce_kernel(const float* __res
   dbeta[c] = b;
 }
 
-static tps_status ln_checks(const char* fn, tps_dtype dt, int64_t M, int64_t H,
+static tps_status ln_checks(const char* fn, std::initializer_list<tps_dtype> dts, int64_t M, int64_t H,
                             std::initializer_list<const void*> ptrs) {
-  if (dt != TPS_F32 && dt != TPS_BF16) return set_error(TPS_EINVAL, std::string(fn) + ": bad dtype");
+  for (tps_dtype d : dts)
+    if (d != TPS_F32 && d != TPS_BF16) return set_error(TPS_EINVAL, std::string(fn) + ": bad dtype");
   if (M <= 0 || H <= 0 || M >= 0x7fffffffLL) return set_error(TPS_EINVAL, std::string(fn) + ": need 0 < M < 2^31, H > 0");
-  if (H % vec_elems(dt)) return set_error(TPS_EINVAL, std::string(fn) + ": H must be a multiple of 8 (bf16) / 4 (fp32)");
+  if (H % kLnV) return set_error(TPS_EINVAL, std::string(fn) + ": H must be a multiple of 8");
   for (const void* p : ptrs) {
     if (!p) return set_error(TPS_EINVAL, std::string(fn) + ": null pointer");
     if (!aligned16(p)) return set_error(TPS_EINVAL, std::string(fn) + ": pointer not 16-byte aligned");
@@ -185,22 +189,37 @@ static tps_status ln_checks(const char* fn, tps_dtype dt, int64_t M, int64_t H,
   return TPS_OK;
 }
 
+template <typename TX, typename TY>
+static void launch_ln_fwd(int64_t M, int64_t H, float eps, const void* x, const float* g, const float* b, void* y,
+                          float* mean, float* rstd, hipStream_t st) {
+  hipLaunchKernelGGL((ln_fwd_kernel<TX, TY>), dim3((unsigned)M), dim3(256), 0, st, static_cast<const TX*>(x), g, b,
+                     static_cast<TY*>(y), mean, rstd, H, eps);
+}
+
+template <typename TX, typename TDY, typename TDX>
+static void launch_ln_bwd(int64_t M, int64_t H, const void* x, const float* g, const float* mean, const float* rstd,
+                          const void* dy, void* dx, float* part, hipStream_t st) {
+  hipLaunchKernelGGL((ln_bwd_kernel<TX, TDY, TDX>), dim3((unsigned)ceil_div(M, kLnRowsPerBlock)), dim3(256), 0, st,
+                     static_cast<const TX*>(x), g, mean, rstd, static_cast<const TDY*>(dy), static_cast<TDX*>(dx),
+                     part, M, H);
+}
+
 }  // namespace tps
 
 using namespace tps;
 
-extern "C" tps_status layernorm_fwd(tps_dtype dt, int64_t M, int64_t H, float eps, const void* x, const float* gamma,
-                                    const float* beta, void* y, float* mean, float* rstd, tps_stream_t stream) {
-  tps_status s = ln_checks("layernorm_fwd", dt, M, H, {x, gamma, beta, y, mean, rstd});
+extern "C" tps_status layernorm_fwd(tps_dtype x_dt, tps_dtype y_dt, int64_t M, int64_t H, float eps, const void* x,
+                                    const float* gamma, const float* beta, void* y, float* mean, float* rstd,
+                                    tps_stream_t stream) {
+  tps_status s = ln_checks("layernorm_fwd", {x_dt, y_dt}, M, H, {x, gamma, beta, y, mean, rstd});
   if (s != TPS_OK) return s;
   if (!(eps >= 0.f)) return set_error(TPS_EINVAL, "layernorm_fwd: eps must be >= 0");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dt == TPS_BF16)
-    hipLaunchKernelGGL(ln_fwd_kernel<bf16_t>, dim3((unsigned)M), dim3(256), 0, st, (const bf16_t*)x, gamma, beta,
-                       (bf16_t*)y, mean, rstd, H, eps);
-  else
-    hipLaunchKernelGGL(ln_fwd_kernel<float>, dim3((unsigned)M), dim3(256), 0, st, (const float*)x, gamma, beta,
-                       (float*)y, mean, rstd, H, eps);
+  const bool xb = x_dt == TPS_BF16, yb = y_dt == TPS_BF16;
+  if (xb && yb) launch_ln_fwd<bf16_t, bf16_t>(M, H, eps, x, gamma, beta, y, mean, rstd, st);
+  else if (xb) launch_ln_fwd<bf16_t, float>(M, H, eps, x, gamma, beta, y, mean, rstd, st);
+  else if (yb) launch_ln_fwd<float, bf16_t>(M, H, eps, x, gamma, beta, y, mean, rstd, st);
+  else launch_ln_fwd<float, float>(M, H, eps, x, gamma, beta, y, mean, rstd, st);
   return check_launch("ln_fwd_kernel");
 }
 
@@ -209,23 +228,29 @@ extern "C" size_t layernorm_bwd_workspace(int64_t M, int64_t H) {
   return (size_t)ceil_div(M, kLnRowsPerBlock) * 2 * (size_t)H * sizeof(float);
 }
 
-extern "C" tps_status layernorm_bwd(tps_dtype dt, int64_t M, int64_t H, const void* x, const float* gamma,
-                                    const float* mean, const float* rstd, const void* dy, void* dx, float* dgamma,
-                                    float* dbeta, void* ws, size_t ws_bytes, tps_stream_t stream) {
-  tps_status s = ln_checks("layernorm_bwd", dt, M, H, {x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws});
+extern "C" tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype dx_dt, int64_t M, int64_t H,
+                                    const void* x, const float* gamma, const float* mean, const float* rstd,
+                                    const void* dy, void* dx, float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
+                                    tps_stream_t stream) {
+  tps_status s = ln_checks("layernorm_bwd", {x_dt, dy_dt, dx_dt}, M, H, {x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws});
   if (s != TPS_OK) return s;
   if (ws_bytes < layernorm_bwd_workspace(M, H)) return set_error(TPS_EWORKSPACE, "layernorm_bwd: workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
   float* part = static_cast<float*>(ws);
-  if (dt == TPS_BF16)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16_t>, dim3((unsigned)nblk), dim3(256), 0, st, (const bf16_t*)x, gamma, mean,
-                       rstd, (const bf16_t*)dy, (bf16_t*)dx, part, M, H);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st, (const float*)x, gamma, mean,
-                       rstd, (const float*)dy, (float*)dx, part, M, H);
+  const int k = (x_dt == TPS_BF16 ? 4 : 0) | (dy_dt == TPS_BF16 ? 2 : 0) | (dx_dt == TPS_BF16 ? 1 : 0);
+  switch (k) {
+    case 7: launch_ln_bwd<bf16_t, bf16_t, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 6: launch_ln_bwd<bf16_t, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 5: launch_ln_bwd<bf16_t, float, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 4: launch_ln_bwd<bf16_t, float, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 3: launch_ln_bwd<float, bf16_t, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 2: launch_ln_bwd<float, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 1: launch_ln_bwd<float, float, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    default: launch_ln_bwd<float, float, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+  }
   s = check_launch("ln_bwd_kernel");
   if (s != TPS_OK) return s;
+  const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
   hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(H, 256)), dim3(256), 0, st, part, dgamma, dbeta,
                      nblk, H);
   return check_launch("ln_param_reduce_kernel");

@@ -59,9 +59,84 @@ __global__ void __launch_bounds__(256) shard_reduce_kernel(PartPtrs parts, int n
   }
 }
 
+// out = res + sum(parts) (fp32, in order), optional rounded copy.
+template <typename Tr, typename Tp, typename To, typename Tc>
+__global__ void __launch_bounds__(256) shard_reduce_add_kernel(const Tr* res, PartPtrs parts, int np, To* out,
+                                                               Tc* copy, int64_t n) {
+  const int64_t nvec = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+    float acc[8], x[8];
+    Vec8<Tr>::load(res + v * 8, acc);
+    for (int r = 0; r < np; ++r) {
+      Vec8<Tp>::load(static_cast<const Tp*>(parts.p[r]) + v * 8, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    }
+    Vec8<To>::store(out + v * 8, acc);
+    if (copy) Vec8<Tc>::store(copy + v * 8, acc);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int64_t i = nvec * 8; i < n; ++i) {
+      float a = Elem<Tr>::load(res + i);
+      for (int r = 0; r < np; ++r) a += Elem<Tp>::load(static_cast<const Tp*>(parts.p[r]) + i);
+      out[i] = Elem<To>::from_f32(a);
+      if (copy) copy[i] = Elem<Tc>::from_f32(a);
+    }
+  }
+}
+
+template <typename Tr, typename Tp, typename To>
+static void launch_add(tps_dtype copy_dt, const void* res, const PartPtrs& pp, int np, void* out, void* copy,
+                       int64_t n, dim3 grid, hipStream_t st) {
+  if (copy_dt == TPS_BF16)
+    hipLaunchKernelGGL((shard_reduce_add_kernel<Tr, Tp, To, bf16_t>), grid, dim3(256), 0, st,
+                       static_cast<const Tr*>(res), pp, np, static_cast<To*>(out), static_cast<bf16_t*>(copy), n);
+  else
+    hipLaunchKernelGGL((shard_reduce_add_kernel<Tr, Tp, To, float>), grid, dim3(256), 0, st,
+                       static_cast<const Tr*>(res), pp, np, static_cast<To*>(out), static_cast<float*>(copy), n);
+}
+
+template <typename Tr, typename Tp>
+static void launch_add_o(tps_dtype out_dt, tps_dtype copy_dt, const void* res, const PartPtrs& pp, int np, void* out,
+                         void* copy, int64_t n, dim3 grid, hipStream_t st) {
+  if (out_dt == TPS_BF16) launch_add<Tr, Tp, bf16_t>(copy_dt, res, pp, np, out, copy, n, grid, st);
+  else launch_add<Tr, Tp, float>(copy_dt, res, pp, np, out, copy, n, grid, st);
+}
+
 }  // namespace tps
 
 using namespace tps;
+
+static bool ok_dt(tps_dtype d) { return d == TPS_F32 || d == TPS_BF16; }
+
+extern "C" tps_status shard_reduce_add(tps_dtype res_dt, const void* res, tps_dtype part_dt, int n_parts,
+                                       const void* const* parts, tps_dtype out_dt, void* out, tps_dtype copy_dt,
+                                       void* out_copy, int64_t n, tps_stream_t stream) {
+  if (!ok_dt(res_dt) || !ok_dt(part_dt) || !ok_dt(out_dt) || !ok_dt(copy_dt))
+    return set_error(TPS_EINVAL, "shard_reduce_add: bad dtype");
+  if (n_parts < 1 || n_parts > 7) return set_error(TPS_EINVAL, "shard_reduce_add: n_parts must be in [1, 7]");
+  if (!res || !parts || !out) return set_error(TPS_EINVAL, "shard_reduce_add: null pointer");
+  if (n < 0) return set_error(TPS_EINVAL, "shard_reduce_add: n < 0");
+  PartPtrs pp{};
+  for (int r = 0; r < n_parts; ++r) {
+    if (!parts[r]) return set_error(TPS_EINVAL, "shard_reduce_add: null part pointer");
+    if (!aligned16(parts[r])) return set_error(TPS_EINVAL, "shard_reduce_add: part not 16-byte aligned");
+    pp.p[r] = parts[r];
+  }
+  if (!aligned16(res) || !aligned16(out) || (out_copy && !aligned16(out_copy)))
+    return set_error(TPS_EINVAL, "shard_reduce_add: pointers must be 16-byte aligned");
+  if (n == 0) return TPS_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int64_t blocks = ceil_div(n / 8 > 0 ? n / 8 : 1, 256);
+  if (blocks > 65536) blocks = 65536;
+  const dim3 grid((unsigned)blocks);
+  if (res_dt == TPS_F32 && part_dt == TPS_BF16) launch_add_o<float, bf16_t>(out_dt, copy_dt, res, pp, n_parts, out, out_copy, n, grid, st);
+  else if (res_dt == TPS_F32) launch_add_o<float, float>(out_dt, copy_dt, res, pp, n_parts, out, out_copy, n, grid, st);
+  else if (part_dt == TPS_BF16) launch_add_o<bf16_t, bf16_t>(out_dt, copy_dt, res, pp, n_parts, out, out_copy, n, grid, st);
+  else launch_add_o<bf16_t, float>(out_dt, copy_dt, res, pp, n_parts, out, out_copy, n, grid, st);
+  return check_launch("shard_reduce_add_kernel");
+}
 
 extern "C" tps_status shard_reduce(tps_dtype in_dt, tps_dtype out_dt, int n_parts,
                                    const void* const* parts, void* out, int64_t n,

@@ -79,7 +79,9 @@ ALIGNED = 1 << 20  # a fake, 16-byte aligned address: validation fails before an
     ("vocab_embed_fwd", (1, 16, 64, 0, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # v_rows = 0
     ("vocab_embed_fwd", (1, 16, 64, -1, 10, ALIGNED, ALIGNED, ALIGNED, None)),                    # v_start < 0
     ("tp_attn_fwd", (1, 1, 64, 256, 2, 64, 1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, None)),
-    ("layernorm_fwd", (1, 4, 0, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),
+    ("layernorm_fwd", (0, 1, 4, 0, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),
+    ("layernorm_fwd", (0, 1, 4, 12, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),  # H % 8
+    ("shard_reduce_add", (0, ALIGNED, 1, 0, None, 0, ALIGNED, 1, None, 16, None)),                  # n_parts = 0
 ])
 def test_validation_rejects_before_enqueue(tp, case):
     name, args = case

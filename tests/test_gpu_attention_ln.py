@@ -90,16 +90,19 @@ def test_attention_backward_deterministic(tp):
 
 # ------------------------------------------------------------------ LayerNorm
 
-@pytest.mark.parametrize("M,H,dt", [(5, 64, "f32"), (300, 4096, "bf16"), (33, 8192, "f32"), (17, 136, "bf16")])
-def test_layernorm_matches_oracle(tp, M, H, dt):
-    say(f"layernorm fwd+bwd M={M} H={H} {dt}")
+@pytest.mark.parametrize("M,H,dt,ydt", [(5, 64, "f32", "f32"), (300, 4096, "bf16", "bf16"), (33, 8192, "f32", "f32"),
+                                        (17, 136, "bf16", "bf16"), (64, 4096, "f32", "bf16"), (9, 72, "bf16", "f32")])
+def test_layernorm_matches_oracle(tp, M, H, dt, ydt):
+    """x and dx of dtype dt, y and dy of dtype ydt (fp32 residual stream <-> bf16 sublayer)."""
+    say(f"layernorm fwd+bwd M={M} H={H} x {dt} y {ydt}")
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    ytdt = torch.bfloat16 if ydt == "bf16" else torch.float32
+    tol = BF16_TOL if "bf16" in (dt, ydt) else F32_TOL
     x = synth.make(77, 0, (M, H), 2.0, dt)
-    dy = synth.make(77, 1, (M, H), 1.0, dt)
+    dy = synth.make(77, 1, (M, H), 1.0, ydt)
     g = synth.Tensor(1.0 + 0.1 * synth.normal(77, 2, (H,)), "f32")
     bt = synth.Tensor(0.1 * synth.normal(77, 3, (H,)), "f32")
-    y, mean, rstd = empty((M, H), tdt), empty((M,), torch.float32), empty((M,), torch.float32)
+    y, mean, rstd = empty((M, H), ytdt), empty((M,), torch.float32), empty((M,), torch.float32)
     dg, db_ = to_dev(g), to_dev(bt)
     dx_in = to_dev(x)
     tp.layernorm_fwd(dx_in, dg, db_, y, mean, rstd, 1e-5)
@@ -111,5 +114,5 @@ def test_layernorm_matches_oracle(tp, M, H, dt):
     tp.layernorm_bwd(dx_in, dg, mean, rstd, to_dev(dy), dx, dgam, dbet, ws)
     dx_ref, dg_ref, db_ref = O.layernorm_backward(x.f64, g.f64, mu_ref, rs_ref, dy.f64)
     assert rel_err(to_f64(dx), dx_ref) <= tol
-    assert rel_err(to_f64(dgam), dg_ref) <= (F32_TOL if dt == "f32" else 1e-3)
+    assert rel_err(to_f64(dgam), dg_ref) <= (F32_TOL if tol == F32_TOL else 1e-3)
     assert rel_err(to_f64(dbet), db_ref) <= 1e-5

@@ -61,6 +61,27 @@ def test_shard_reduce_in_place_and_mixed_types(tp):
     assert np.array_equal(to_f64(da), O.round_to_bf16(a.f64 + b.f64))
 
 
+@pytest.mark.parametrize("rdt,pdt,odt,cdt", [("f32", "bf16", "f32", "bf16"), ("bf16", "bf16", "bf16", None),
+                                              ("f32", "f32", "bf16", "f32")])
+def test_shard_reduce_add_residual(tp, rdt, pdt, odt, cdt):
+    n = 100_003
+    say(f"shard_reduce_add res {rdt} parts {pdt} out {odt} copy {cdt}")
+    res = synth.make(98, 0, (n,), 4.0, rdt)
+    parts = [synth.make(98, 1 + i, (n,), 1.0, pdt) for i in range(2)]
+    tt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    out = empty((n,), tt[odt])
+    copy = empty((n,), tt[cdt]) if cdt else None
+    tp.shard_reduce_add(to_dev(res), [to_dev(p) for p in parts], out, copy)
+    exact = O.shard_reduce([res.f64] + [p.f64 for p in parts])
+    rnd = {"f32": O.round_to_f32, "bf16": O.round_to_bf16}
+    # fp32 accumulation of three terms, then one rounding
+    assert np.max(np.abs(to_f64(out) - rnd[odt](exact))) <= 4 * 2.0 ** -24 * np.max(np.abs(exact)) + \
+        (0 if odt == "f32" else 2.0 ** -8 * np.max(np.abs(exact)))
+    assert rel_err(to_f64(out), exact) <= (F32_TOL if odt == "f32" else BF16_TOL)
+    if cdt:
+        assert rel_err(to_f64(copy), exact) <= (F32_TOL if cdt == "f32" else BF16_TOL)
+
+
 def test_shard_reduce_propagates_nan_where_the_oracle_does(tp):
     n = 4099
     say("shard_reduce NaN/Inf propagation")
