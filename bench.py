@@ -1,19 +1,21 @@
 """Benchmark of the tensor-parallel shard path on one MI355X.
 
-Step = one pass over one transformer layer at the page-1 model shape
-(b=1, s=2048, H=4096, 8 heads of 512, 4H MLP) split over N=2 tensor-parallel
-shards, all executed on this GPU: for each shard the attention sublayer
-(QKV column GEMM, causal flash attention, row GEMM) and the MLP sublayer
-(column GEMM + GELU, row GEMM) forward and backward, plus the four
-shard_reduce calls that stand in for the 'g' forward and 'f' backward
-all-reduces.  Inputs are seeded synthetic tensors resident in HBM.
+Step = one forward+backward pass of the 12-layer GPT at the page-1 model
+shape (H=4096, 8 heads of 512, 4H MLP, 2 LayerNorms per layer, tied vocab
+50257) on b=1 x s=2048 tokens, split over N=2 tensor-parallel shards that
+all execute on this GPU: the vocab-parallel embedding gather and its shard
+sum, per layer the LayerNorms, both shards' attention and MLP sublayers and
+the shard sums standing in for the 'g'/'f' all-reduces, the tied logits,
+and the whole backward pass including the tied table gradient (output side
+plus input side).  Inputs are seeded synthetic tensors resident in HBM;
+the logits' upstream gradient is drawn N(0,1).
 
-Prints one JSON line.  `value` = algorithmic TFLOP/s of the step (2577.0
-GFLOP: GEMMs 2MNK, causal attention s(s+1)/2 score pairs, backward = 2x
-forward).  Also reported: the roofline of the dominant kernel (the MFMA GEMM
-of the MLP shard forward), the vocab-parallel embedding kernels' HBM GB/s at
-the tied-embedding shape (V=50257, H=4096, T=16384), and the fp64 CPU oracle
-timed on a bounded sample of the same layer.
+Prints one JSON line.  `value` = algorithmic TFLOP/s of the step (33.45
+TFLOP: GEMMs 2MNK, causal attention s(s+1)/2 score pairs, backward = 2x
+forward).  Also reported: the roofline of the dominant kernel (the MFMA
+GEMM, on its single-launch call tied_logits), the single-layer step on its
+own, the vocab-parallel embedding kernels' HBM GB/s at T = 8*2048 tokens,
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -83,23 +85,15 @@ class Layer:
             self.sh.append(r)
         self.Za, self.Zm, self.dXa, self.dXm = emp((M, h)), emp((M, h)), emp((M, h)), emp((M, h))
         self.hs, self.w, self.f = hs, w, f
-        self.mlp_events = []
 
-    def step(self, record=False):
+    def step(self):
         tp, sh = self.tp, self.sh
         b, s, hs, d = self.b, self.s, self.hs, self.d
         for r in sh:
             tp.tp_attn_fwd(self.X, r["Wqkv"], r["Wo"], r["QKV"], r["O"], r["lse"], r["Za"], b, s, hs, d, True)
         tp.shard_reduce([r["Za"] for r in sh], self.Za)
         for r in sh:
-            if record:
-                e0 = self.torch.cuda.Event(enable_timing=True)
-                e1 = self.torch.cuda.Event(enable_timing=True)
-                e0.record()
             tp.tp_mlp_fwd(self.X, r["A"], r["B"], r["P"], r["H"], r["Zm"])
-            if record:
-                e1.record()
-                self.mlp_events.append((e0, e1))
         tp.shard_reduce([r["Zm"] for r in sh], self.Zm)
         for r in sh:
             tp.tp_mlp_bwd(self.X, r["A"], r["B"], r["P"], r["H"], self.dZm, r["dXm"], r["dA"], r["dB"], r["ws_mlp"])
@@ -108,6 +102,36 @@ class Layer:
             tp.tp_attn_bwd(self.X, r["Wqkv"], r["Wo"], r["QKV"], r["O"], r["lse"], self.dZa, r["dXa"], r["dWqkv"],
                            r["dWo"], r["ws_attn"], b, s, hs, d, True)
         tp.shard_reduce([r["dXa"] for r in sh], self.dXa)
+
+
+def gpt_model(tp, torch, seed=5):
+    """The 12-layer model with seeded N(0,0.02) weights, gamma=1, beta=0,
+    uniform tokens and dL ~ N(0,1), all generated on the GPU."""
+    from megatron_tensor_transformer_columnparallel_amd.gpt import GPTShape, TPGPT
+    c = GPTShape()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 * seed)
+    bf = torch.bfloat16
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std).to(bf)
+
+    E = rnd((c.V, c.H), 0.02)
+    layers = []
+    for _ in range(c.L):
+        layers.append({"WQ": rnd((c.H, c.heads * c.d), 0.02), "WK": rnd((c.H, c.heads * c.d), 0.02),
+                       "WV": rnd((c.H, c.heads * c.d), 0.02), "WO": rnd((c.heads * c.d, c.H), 0.02),
+                       "A": rnd((c.H, c.f), 0.02), "B": rnd((c.f, c.H), 0.02),
+                       "g1": torch.ones(c.H, device="cuda"), "b1": torch.zeros(c.H, device="cuda"),
+                       "g2": torch.ones(c.H, device="cuda"), "b2": torch.zeros(c.H, device="cuda")})
+    model = TPGPT(c, E, layers)
+    ids = torch.randint(0, c.V, (c.M,), generator=g, device="cuda", dtype=torch.int32)
+    dl = []
+    for r in range(c.n):
+        buf = torch.zeros((c.M, model.ldl[r]), dtype=bf, device="cuda")
+        buf[:, :model.vr[r][1]] = rnd((c.M, model.vr[r][1]), 1.0)
+        dl.append(buf[:, :model.vr[r][1]])
+    return c, model, ids, dl
 
 
 def embed_bench(tp, torch, reps=20):
@@ -164,10 +188,11 @@ def embed_bench(tp, torch, reps=20):
     return res
 
 
-def cpu_baseline(budget_s=30.0):
-    """The fp64 oracle on a bounded sample: one shard's MLP sublayer forward
-    and backward at the full layer shape (M=2048, h=4096, f_i=8192), i.e. six
-    2048x4096x8192 products plus GELU: 824.6 GFLOP algorithmic."""
+def cpu_baseline():
+    """The fp64 oracle on a bounded sample of the step: one shard of one
+    layer's MLP sublayer forward and backward at the full shape (M=2048,
+    h=4096, f_i=8192), i.e. six 2048x4096x8192 products plus GELU: 824.6
+    GFLOP algorithmic (the whole step is 33.45 TFLOP)."""
     import numpy as np
 
     import oracle as O
@@ -190,17 +215,34 @@ def cpu_baseline(budget_s=30.0):
                       f"{flops / 1e9:.1f} GFLOP in {t:.2f} s", "seconds": round(t, 2)}
 
 
+# HBM traffic of the roofline kernel from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) over `bench.py --steps 2 --warmup 1 --no-cpu
+# --no-embed --no-layer`, divided by what the same counters read for a plain
+# copy (shard_reduce with one part over 512 MiB) per byte moved.  Valid only
+# for the GEMM source it was taken on (sha256 prefix below); otherwise null.
+ROOFLINE_TRAFFIC = {"gemm_sha": None, "bytes_per_launch": None}
+
+
+def _gemm_sha():
+    import hashlib
+    p = os.path.join(ROOT, "megatron_tensor_transformer_columnparallel_amd", "csrc", "gemm.hpp")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-embed", action="store_true", help="skip the embedding kernels")
+    ap.add_argument("--no-embed", action="store_true", help="skip the embedding-kernel rates")
+    ap.add_argument("--no-layer", action="store_true", help="skip the single-layer step")
+    ap.add_argument("--calib", action="store_true", help="one 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs the whole tensor-parallel layer on ONE GPU "
-                                   "(every shard executed locally); --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs every tensor-parallel shard on ONE GPU "
+                                   "(the shard sums are local kernels); --gpus must be 1"}))
         sys.exit(2)
 
     import torch
@@ -208,42 +250,80 @@ def main():
     import megatron_tensor_transformer_columnparallel_amd as tp
 
     torch.cuda.set_device(0)
-    L = Layer(tp, torch)
-    flops = layer_flops(1, 2048, 4096, 8, 512, 16384, 2)
+    c, model, ids, dl = gpt_model(tp, torch)
+    flops = c.flops()
+
+    if args.calib:
+        # plain copy of known size for the counter calibration: 256 Mi bf16 elements in, same out
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        tp.shard_reduce([src], dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        model.forward(ids)
+        model.backward(ids, dl)
+
     for _ in range(args.warmup):
-        L.step()
+        step()
     torch.cuda.synchronize()
+    # events around each tied_logits call (one GEMM launch each) inside the timed steps
+    model.logit_events = logit_events = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
     for _ in range(args.steps):
-        L.step(record=True)
+        step()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    model.logit_events = None
     ms = t0.elapsed_time(t1) / args.steps
     value = flops / (ms * 1e-3) / 1e12
 
-    # dominant kernel: the two MFMA GEMM launches of tp_mlp_fwd (2*M*h*f_i FLOPs each)
-    mlp_ms = sorted(a.elapsed_time(b) for a, b in L.mlp_events)
-    mlp_ms = sum(mlp_ms) / len(mlp_ms)
-    per_launch_flops = 2 * 2048 * 4096 * 8192
-    achieved = per_launch_flops / (mlp_ms / 2 * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel<256,256,64,2,2> (tp_mlp_fwd: X*A_i+GELU and H_i*B_i, 2048x8192x4096)",
+    launch_ms = sum(a.elapsed_time(b) for a, b in logit_events) / len(logit_events)
+    vr = [n for _, n in model.vr]
+    per_launch_flops = sum(2 * c.M * c.H * n for n in vr) // len(vr)
+    achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
+    traffic = ROOFLINE_TRAFFIC["bytes_per_launch"] if ROOFLINE_TRAFFIC["gemm_sha"] == _gemm_sha() else None
+    roofline = {"kernel": "gemm_bf16_kernel<256,256,64,2,4,NT,EpiStore> via tied_logits "
+                          f"({c.M}x{vr[0]}x{c.H} per shard)",
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "avg_launch_us": round(mlp_ms / 2 * 1e3, 2), "flops_per_launch": per_launch_flops}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "avg_launch_us": round(launch_ms * 1e3, 2), "flops_per_launch": per_launch_flops,
+                "launches_timed": len(logit_events)}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "gpt-layer-shard-bf16: b=1 s=2048 H=4096 heads=8 d=512 4H=16384 TP N=2 "
-                                  "(attention+MLP fwd+bwd, both shards, shard_reduce)",
+           "config": {"workload": "gpt12-tp2-bf16: 12 layers, H=4096, 8 heads of 512, 4H MLP, pre-LN, tied vocab "
+                                  "50257 (25129/25128 per shard), b=1, s=2048, TP N=2 shards on one GPU, fwd+bwd",
                       "global_batch": 1, "seq_len": 2048, "parallelism": "tp2-emulated-on-1-gpu"},
            "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "gflop_per_step": round(flops / 1e9, 1), "wall_s_timed": round(wall, 3),
            "roofline": roofline}
+    del model
+    torch.cuda.empty_cache()
+    if not args.no_layer:
+        L = Layer(tp, torch)
+        for _ in range(3):
+            L.step()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(10):
+            L.step()
+        a1.record()
+        torch.cuda.synchronize()
+        lms = a0.elapsed_time(a1) / 10
+        lfl = layer_flops(1, 2048, 4096, 8, 512, 16384, 2)
+        out["layer"] = {"workload": "one layer (attention + MLP sublayers), both shards, fwd+bwd, shard sums",
+                        "ms": round(lms, 3), "TFLOP/s": round(lfl / (lms * 1e-3) / 1e12, 1),
+                        "frac_of_bf16_peak": round(lfl / (lms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del L
+        torch.cuda.empty_cache()
     if not args.no_embed:
         out["embed"] = embed_bench(tp, torch)
     if not args.no_cpu:

@@ -123,6 +123,8 @@ class TPGPT:
         self.ws_attn = _emp((tp.tp_attn_bwd_workspace(torch.bfloat16, c.b, c.s, H, self.hs, c.d),), torch.uint8)
         self.ws_ln = _emp((tp.layernorm_bwd_workspace(M, H),), torch.uint8)
         self.ws_emb = _emp((tp.vocab_embed_bwd_workspace(M, max(n for _, n in self.vr)),), torch.uint8)
+        # when a list, (start, end) torch.cuda.Events around each tied_logits call are appended to it
+        self.logit_events = None
 
     def logits_view(self, r):
         return self.logits[r][:, :self.vr[r][1]]
@@ -148,7 +150,13 @@ class TPGPT:
         self.x_out = x
         tp.shard_reduce([x], self.x_bf)                                            # round to bf16
         for r in range(cf.n):
+            if self.logit_events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
             tp.tied_logits(self.x_bf, self.E[r], self.logits_view(r))
+            if self.logit_events is not None:
+                e1.record()
+                self.logit_events.append((e0, e1))
 
     def backward(self, ids, dlogits):
         """dlogits[r]: [M x v_r] (row stride a multiple of 8) gradient of shard r's logits."""
