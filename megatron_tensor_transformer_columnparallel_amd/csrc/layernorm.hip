@@ -162,17 +162,39 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
   }
 }
 
+// dgamma/dbeta[c] = sum over row blocks k of the partials, in a fixed order.
+// A workgroup owns 64 columns (16 groups of 4) and splits the blocks into 16
+// contiguous slices, one per thread of a column group; the slice sums are then
+// added in slice order through LDS.  Deterministic, no atomics.
 __global__ void __launch_bounds__(256) ln_param_reduce_kernel(const float* __restrict__ part, float* __restrict__ dgamma,
                                                               float* __restrict__ dbeta, int64_t nblk, int64_t H) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= H) return;
-  float g = 0.f, b = 0.f;
-  for (int64_t k = 0; k < nblk; ++k) {
-    g += part[k * 2 * H + c];
-    b += part[k * 2 * H + H + c];
+  constexpr int COLS = 64, SLICES = 256 / (COLS / 4);   // 16 threads per 4 columns -> 16 slices
+  __shared__ f32x4_t red_g[SLICES][COLS / 4], red_b[SLICES][COLS / 4];
+  const int cg = threadIdx.x % (COLS / 4), sl = threadIdx.x / (COLS / 4);
+  const int64_t c = (int64_t)blockIdx.x * COLS + cg * 4;   // H is a multiple of 8
+  f32x4_t g = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+  if (c < H) {
+    const int64_t per = (nblk + SLICES - 1) / SLICES;
+    const int64_t k0 = sl * per, k1 = min(nblk, k0 + per);
+    for (int64_t k = k0; k < k1; ++k) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(part + k * 2 * H + c);
+      const f32x4_t y = *reinterpret_cast<const f32x4_t*>(part + k * 2 * H + H + c);
+      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
+      b[0] += y[0]; b[1] += y[1]; b[2] += y[2]; b[3] += y[3];
+    }
   }
-  dgamma[c] = g;
-  dbeta[c] = b;
+  red_g[sl][cg] = g;
+  red_b[sl][cg] = b;
+  __syncthreads();
+  if (sl == 0 && c < H) {
+    for (int k = 1; k < SLICES; ++k) {
+      const f32x4_t x = red_g[k][cg], y = red_b[k][cg];
+      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
+      b[0] += y[0]; b[1] += y[1]; b[2] += y[2]; b[3] += y[3];
+    }
+    *reinterpret_cast<f32x4_t*>(dgamma + c) = g;
+    *reinterpret_cast<f32x4_t*>(dbeta + c) = b;
+  }
 }
 
 static tps_status ln_checks(const char* fn, std::initializer_list<tps_dtype> dts, int64_t M, int64_t H,
@@ -251,7 +273,7 @@ extern "C" tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype d
   s = check_launch("ln_bwd_kernel");
   if (s != TPS_OK) return s;
   const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
-  hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(H, 256)), dim3(256), 0, st, part, dgamma, dbeta,
+  hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(H, 64)), dim3(256), 0, st, part, dgamma, dbeta,
                      nblk, H);
   return check_launch("ln_param_reduce_kernel");
 }
