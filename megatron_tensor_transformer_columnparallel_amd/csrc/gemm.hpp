@@ -2,10 +2,9 @@
 // result handed to a fused epilogue functor.
 //
 // bf16 path: LDS-tiled MFMA kernel (v_mfma_f32_16x16x32_bf16), double-buffered
-// LDS with register prefetch of the next K tile, XCD-aware tile order.  Both
-// operands are staged in LDS "K-contiguous" ([row][k]) so every MFMA fragment
-// is one 16-byte LDS read; an operand stored with M (or N) contiguous is
-// transposed 8x8 in registers on its way from global memory to LDS.
+// LDS fed by direct global -> LDS loads (registers only for edge tiles),
+// XCD-aware tile order.  Each operand keeps its global orientation in LDS;
+// fragments of an M/N-contiguous operand come out of the LDS transpose read.
 //
 // fp32 path: LDS-tiled SIMT kernel (4x4 outputs per thread), same epilogues.
 #pragma once
@@ -145,139 +144,151 @@ __device__ __forceinline__ u32x4_t mask_vec8(u32x4_t v, int nvalid) {
   return v;
 }
 
-// LDS layout: each operand tile is [rows][BK=64] bf16 with no padding; the
-// eight 16-byte chunks of row r are stored XOR-swizzled (chunk c at position
-// c ^ (r & 7)).  MFMA fragment reads (8 consecutive lanes = 8 consecutive rows,
-// same chunk) and the loaders' 16-byte stores then hit 8 distinct bank groups.
-__device__ __forceinline__ int lds_swizzle(int row) { return row & 7; }
+// LDS layout of one operand tile (BK = 64), as a linear array of 16-byte
+// chunks ("slots"):
+//   K-contiguous operand: [R rows][64 k], 8 chunks per row; chunk c of row r
+//     sits at position c ^ (r & 7).  An MFMA fragment (8 consecutive lanes =
+//     8 consecutive rows, same chunk) is one 16-byte read per lane spread
+//     over 8 distinct bank groups.
+//   M/N-contiguous operand: [64 k][R], R/8 chunks per k-row; chunk c of k-row
+//     k sits at position c ^ mn_swizzle<R>(k).  A fragment is read with two
+//     ds_read_b64_tr_b16 (transposing 4 k-rows x 16 columns per 16-lane
+//     group); the swizzle sends the 8 k-rows that a half-wave touches to 8
+//     distinct pairs of bank groups.
+// Slot q of either layout holds row q / CPR at position q % CPR, so a wave
+// fills 64 consecutive slots with one instruction: global_load_lds_dwordx4
+// (lane l lands at LDS base + 16 l) for interior tiles, or 16-byte register
+// stores after bounds-checked loads at the edges.
+__device__ __forceinline__ int kc_swizzle(int row) { return row & 7; }
 
-// Global -> register -> LDS loader for one operand tile of R rows (m or n)
-// by BK.  KC: the operand is K-contiguous in global memory (one 16-byte
-// vector = 8 consecutive k of one row).  Otherwise it is M/N-contiguous and
-// each thread loads an 8-row x KB-k block and transposes it in registers;
-// consecutive lanes take consecutive k-blocks so that their LDS stores land
-// in distinct banks.  Each thread walks a pointer through K; the unchecked
-// load is used for interior tiles, the checked one zero-fills past M/N/K.
-template <int R, int BK, int NT, bool KC>
-struct TileLoader {
-  static constexpr int VECS = R * BK / 8 / NT;
-  static constexpr int EPT = R * BK / NT;
-  static constexpr int KB = KC ? 8 : (EPT / 8 >= 8 ? 8 : EPT / 8);
-  static constexpr int NBLK = KC ? 0 : EPT / (8 * KB);
-  static constexpr int KBLKS = BK / KB;
-  static constexpr int ROWS_PER_PASS = NT / (BK / 8);  // KC: rows covered by one vector per thread
-  static_assert(BK == 64, "the swizzle assumes 8 chunks per row");
-  static_assert(KC || (KB == 2 || KB == 4 || KB == 8), "KB");
-  static_assert(KC || NBLK * 8 * KB == EPT, "EPT");
-  static_assert(VECS >= 1, "tile too small for the thread count");
+template <int R>
+__device__ __forceinline__ int mn_swizzle(int k) {
+  if constexpr (R >= 128) return 2 * ((k & 3) | ((k >> 1) & 4));
+  else return 2 * (((k >> 1) & 1) | ((k >> 2) & 2));
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+// Loader of one operand tile of R rows (m or n) by BK = 64.  Each thread owns
+// VECS slots (tid + i*NT); all of them share one global column offset, so a
+// single pointer walks through K.
+template <int R, int NT, bool KC>
+struct OperandLoader {
+  static constexpr int BK = 64;
+  static constexpr int CPR = KC ? BK / 8 : R / 8;   // 16-byte chunks per LDS row
+  static constexpr int VECS = R * BK / 8 / NT;      // slots per thread
+  static constexpr int RSTEP = NT / CPR;            // LDS rows between a thread's slots
+  static_assert(VECS >= 1 && NT % CPR == 0 && RSTEP % 16 == 0, "operand tile vs thread count");
+  static_assert(KC || R >= 64, "M/N-contiguous tiles need at least 8 chunks per k-row");
 
   u32x4_t v[VECS];
-  const bf16_t* ptr;  // this thread's first element of the next tile
-  int64_t step, ld;
-  int gr0, gk0;       // global row / k of this thread's first vector in tile 0
+  const bf16_t* ptr;     // global address of this thread's first slot in the next K tile
+  int64_t istep, kstep;  // elements between the thread's slots; between K tiles
+  int row0, col0;        // KC: (m/n row, k column) of the first slot; else (k row, m/n column)
 
-  __device__ __forceinline__ void init(const bf16_t* p, int64_t ld_, int r0, int k0, int tid) {
-    ld = ld_;
+  __device__ __forceinline__ void init(const bf16_t* p, int64_t ld, int r0, int k0, int tid) {
+    const int row = tid / CPR, pos = tid % CPR;
+    row0 = row;
     if constexpr (KC) {
-      gr0 = r0 + tid / (BK / 8);
-      gk0 = k0 + (tid % (BK / 8)) * 8;
-      ptr = p + (int64_t)gr0 * ld + gk0;
-      step = BK;
+      col0 = (pos ^ kc_swizzle(row)) * 8;
+      ptr = p + (int64_t)(r0 + row) * ld + k0 + col0;
+      kstep = BK;
     } else {
-      gr0 = r0 + (tid / KBLKS) * 8;
-      gk0 = k0 + (tid % KBLKS) * KB;
-      ptr = p + (int64_t)gk0 * ld + gr0;
-      step = (int64_t)BK * ld;
+      col0 = (pos ^ mn_swizzle<R>(row)) * 8;
+      ptr = p + (int64_t)(k0 + row) * ld + r0 + col0;
+      kstep = (int64_t)BK * ld;
+    }
+    istep = (int64_t)RSTEP * ld;
+  }
+
+  // Whole tile inside the operand: global -> LDS without registers.
+  __device__ __forceinline__ void issue_direct(bf16_t* region, int wave) {
+#pragma unroll
+    for (int i = 0; i < VECS; ++i)
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(ptr + i * istep),
+                                       (__attribute__((address_space(3))) void*)(region + (i * NT + wave * 64) * 8),
+                                       16, 0, 0);
+    ptr += kstep;
+  }
+
+  // Edge tile: r_rem rows (m/n) and k_rem k remain from the tile origin;
+  // elements outside are zero.
+  __device__ __forceinline__ void load_checked(int r_rem, int k_rem) {
+#pragma unroll
+    for (int i = 0; i < VECS; ++i) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if constexpr (KC) {
+        const int r = row0 + i * RSTEP;
+        if (r < r_rem && col0 < k_rem) {
+          x = *reinterpret_cast<const u32x4_t*>(ptr + i * istep);
+          if (col0 + 8 > k_rem) x = mask_vec8(x, k_rem - col0);
+        }
+      } else {
+        const int k = row0 + i * RSTEP;
+        if (k < k_rem && col0 < r_rem) {
+          x = *reinterpret_cast<const u32x4_t*>(ptr + i * istep);
+          if (col0 + 8 > r_rem) x = mask_vec8(x, r_rem - col0);
+        }
+      }
+      v[i] = x;
+    }
+    ptr += kstep;
+  }
+
+  __device__ __forceinline__ void store(bf16_t* region, int tid) const {
+#pragma unroll
+    for (int i = 0; i < VECS; ++i) *reinterpret_cast<u32x4_t*>(region + (tid + i * NT) * 8) = v[i];
+  }
+};
+
+// MFMA operand fragments of one wave: FR blocks of 16 rows starting at row
+// `base` of an R-row tile.  A fragment gives lane l row (l & 15), k = 8*(l >> 4)
+// .. +7 of the current 32-wide k-step.
+template <int R, int FR, bool KC>
+struct FragReader {
+  static constexpr int BK = 64;
+  int off[KC ? 2 : FR];  // KC: per k-step; else per fragment (element offsets)
+
+  __device__ __forceinline__ void init(int base, int lane) {
+    const int fr = lane & 15, fg = lane >> 4;
+    if constexpr (KC) {
+      const int r = base + fr;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) off[ks] = r * BK + (((ks * 4 + fg) ^ kc_swizzle(r)) * 8);
+    } else {
+      // lane j of a 16-lane group supplies k-row (j >> 2) and columns 4*(j & 3)..+3
+      // of its group's 4 x 16 block; the hardware returns column j, k-rows 0..3.
+      const int trow = 8 * fg + (fr >> 2);
+      const int f = mn_swizzle<R>(trow);   // equal for every k-row this lane reads
+#pragma unroll
+      for (int i = 0; i < FR; ++i) {
+        const int chunk = (base + 16 * i) / 8 + ((fr & 3) >> 1);
+        off[i] = trow * R + ((chunk ^ f) * 8) + (fr & 1) * 4;
+      }
     }
   }
 
-  __device__ __forceinline__ void load_fast() {
+  __device__ __forceinline__ bf16x8_t read(const bf16_t* region, int ks, int i) const {
     if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < VECS; ++i)
-        v[i] = *reinterpret_cast<const u32x4_t*>(ptr + (int64_t)i * ROWS_PER_PASS * ld);
+      return *reinterpret_cast<const bf16x8_t*>(region + off[ks] + i * 16 * BK);
     } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b)
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-          v[b * KB + j] = *reinterpret_cast<const u32x4_t*>(ptr + (int64_t)j * ld + b * (NT / KBLKS) * 8);
-    }
-    ptr += step;
-  }
-
-  // kt: index of the tile being loaded (relative to the first).
-  __device__ __forceinline__ void load_checked(int R_total, int K_total, int kt) {
-    const int dk = kt * BK;
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < VECS; ++i) {
-        const int gr = gr0 + i * ROWS_PER_PASS, gk = gk0 + dk;
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if (gr < R_total && gk < K_total) {
-          x = *reinterpret_cast<const u32x4_t*>(ptr + (int64_t)i * ROWS_PER_PASS * ld);
-          if (gk + 8 > K_total) x = mask_vec8(x, K_total - gk);
-        }
-        v[i] = x;
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int gr = gr0 + b * (NT / KBLKS) * 8;
-#pragma unroll
-        for (int j = 0; j < KB; ++j) {
-          const int gk = gk0 + dk + j;
-          u32x4_t x = {0u, 0u, 0u, 0u};
-          if (gr < R_total && gk < K_total) {
-            x = *reinterpret_cast<const u32x4_t*>(ptr + (int64_t)j * ld + b * (NT / KBLKS) * 8);
-            if (gr + 8 > R_total) x = mask_vec8(x, R_total - gr);
-          }
-          v[b * KB + j] = x;
-        }
-      }
-    }
-    ptr += step;
-  }
-
-  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < VECS; ++i) {
-        const int row = tid / (BK / 8) + i * ROWS_PER_PASS, kc = tid % (BK / 8);
-        *reinterpret_cast<u32x4_t*>(lds + row * BK + ((kc ^ lds_swizzle(row)) * 8)) = v[i];
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b) {
-        const int kb = tid % KBLKS, rb = tid / KBLKS + b * (NT / KBLKS);
-        // v[b*KB + j] holds rows rb*8..rb*8+7 at k = kb*KB + j; output row i
-        // gathers element i of each of the KB vectors.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int w = i >> 1;
-          const bool hi = i & 1;
-          uint32_t out[KB / 2];
-#pragma unroll
-          for (int q = 0; q < KB / 2; ++q) {
-            const uint32_t a = v[b * KB + 2 * q][w], c = v[b * KB + 2 * q + 1][w];
-            out[q] = hi ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-          }
-          const int row = rb * 8 + i;
-          const int e = kb * KB;
-          bf16_t* dst = lds + row * BK + (((e >> 3) ^ lds_swizzle(row)) * 8) + (e & 7);
-          if constexpr (KB == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{out[0], out[1], out[2], out[3]};
-          else if constexpr (KB == 4) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{out[0], out[1]};
-          else *reinterpret_cast<uint32_t*>(dst) = out[0];
-        }
-      }
+      const bf16_t* p = region + off[i] + ks * 32 * R;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+      const s16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p + 4 * R));
+      const s16x8_t r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8_t, r);
     }
   }
 };
 
 // One workgroup computes a BM x BN tile with WM x WN waves, each wave a
 // (BM/WM) x (BN/WN) block of 16x16 MFMA tiles, K in steps of BK = 64 through
-// two LDS stages: while the MFMAs consume stage k, the loads of tile k+1 are
-// in flight to registers and land in the other stage at the end of the step.
+// two LDS stages: while the MFMAs consume one stage, the next K tile is in
+// flight to the other.
 template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKC, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64, 1)
 gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, GemmShape s, Epi epi) {
@@ -288,6 +299,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   constexpr int STAGE = (BM + BN) * BK;                 // bf16 elements per LDS stage
   constexpr int BAND_BYTES = WTM * (BN + 4) * 4;        // fp32 epilogue band
   constexpr int LDS_BYTES = 4 * STAGE > BAND_BYTES ? 4 * STAGE : BAND_BYTES;
+  static_assert(BK == 64, "loaders and swizzles assume BK = 64");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_BYTES / 2];
@@ -307,7 +319,9 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   k_range(s, m0, BM, BK, kb, ke);
   if (s.skip_upper && n0 > m0 + BM - 1) ke = kb;
   const int nk = (ke - kb + BK - 1) / BK;
-  const bool full = (m0 + BM <= s.M) && (n0 + BN <= s.N) && ((ke - kb) % BK == 0);
+  // K tiles [0, nkd) are loaded directly (tile inside M and N, all 64 k in range)
+  const bool mn_inside = (m0 + BM <= s.M) && (n0 + BN <= s.N);
+  const int nkd = mn_inside ? (ke - kb) / BK : 0;
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -315,30 +329,49 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  TileLoader<BM, BK, NT, AK> la;
-  TileLoader<BN, BK, NT, BKC> lb;
+  OperandLoader<BM, NT, AK> la;
+  OperandLoader<BN, NT, BKC> lb;
   la.init(A + zo * s.sa_o + zi * s.sa_i, s.lda, m0, kb, tid);
   lb.init(B + zo * s.sb_o + zi * s.sb_i, s.ldb, n0, kb, tid);
+  FragReader<BM, FM, AK> fa;
+  FragReader<BN, FN, BKC> fb;
+  fa.init(wm * WTM, lane);
+  fb.init(wn * WTN, lane);
 
-  // Fragment of a 16x16x32 MFMA: lane reads row (lane & 15) of its 16-row
-  // block, chunk ks*4 + (lane >> 4) (8 consecutive k).
-  const int fr = lane & 15, fg = lane >> 4;
-  const int ra = wm * WTM + fr, rb = wn * WTN + fr;
-  int offa[KS], offb[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    offa[ks] = ra * BK + (((ks * 4 + fg) ^ lds_swizzle(ra)) * 8);
-    offb[ks] = BM * BK + rb * BK + (((ks * 4 + fg) ^ lds_swizzle(rb)) * 8);
+  const int m_rem = s.M - m0, n_rem = s.N - n0;
+  auto load = [&](int kt, bf16_t* st) {  // returns true when registers must be stored
+    if (kt < nkd) {
+      la.issue_direct(st, wave);
+      lb.issue_direct(st + BM * BK, wave);
+      return false;
+    }
+    const int k_rem = s.K - kb - kt * BK;
+    la.load_checked(m_rem, k_rem);
+    lb.load_checked(n_rem, k_rem);
+    return true;
+  };
+
+  if (nk > 0) {
+    if (load(0, lds)) {
+      la.store(lds, tid);
+      lb.store(lds + BM * BK, tid);
+    }
+    wait_vmem();
+    __syncthreads();
   }
-
-  auto compute = [&](const bf16_t* st) {
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    bf16_t* nx = lds + (cur ^ 1) * STAGE;
+    const bool more = kt + 1 < nk;
+    const bool regs = more && load(kt + 1, nx);
+    const bf16_t* st = lds + cur * STAGE;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + offa[ks] + i * 16 * BK);
+      for (int i = 0; i < FM; ++i) af[i] = fa.read(st, ks, i);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + offb[ks] + j * 16 * BK);
+      for (int j = 0; j < FN; ++j) bfr[j] = fb.read(st + BM * BK, ks, j);
       // operands swapped: the result's lane layout is C(m = lane & 15, n = 4*(lane >> 4) + e)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -346,41 +379,12 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-  };
-
-  if (nk > 0) {
-    if (full) { la.load_fast(); lb.load_fast(); }
-    else { la.load_checked(s.M, s.K, 0); lb.load_checked(s.N, s.K, 0); }
-    la.store(lds, tid);
-    lb.store(lds + BM * BK, tid);
+    if (regs) {
+      la.store(nx, tid);
+      lb.store(nx + BM * BK, tid);
+    }
+    wait_vmem();
     __syncthreads();
-  }
-  if (full) {
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) { la.load_fast(); lb.load_fast(); }
-      compute(lds + cur * STAGE);
-      if (more) {
-        bf16_t* nx = lds + (cur ^ 1) * STAGE;
-        la.store(nx, tid);
-        lb.store(nx + BM * BK, tid);
-      }
-      __syncthreads();
-    }
-  } else {
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) { la.load_checked(s.M, s.K, kt + 1); lb.load_checked(s.N, s.K, kt + 1); }
-      compute(lds + cur * STAGE);
-      if (more) {
-        bf16_t* nx = lds + (cur ^ 1) * STAGE;
-        la.store(nx, tid);
-        lb.store(nx + BM * BK, tid);
-      }
-      __syncthreads();
-    }
   }
 
   // Epilogue staged through LDS (free after the K-loop's last barrier): one
@@ -490,15 +494,17 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
   return check_launch("gemm_bf16_kernel");
 }
 
-// Tile shape by problem size (measured on MI355X): 256x256 with 8 waves
-// (2 per SIMD) when it yields at least 3/4 of a wave of workgroups per CU,
-// else 128x128 with 4 waves (two workgroups per CU), else 64x64.
+// Tile shape by problem size: 256x256 with 8 waves (one workgroup per CU) or
+// 128x128 with 4 waves (two per CU), whichever needs fewer time units for
+// its rounds of resident workgroups (a 128x128 round measured at ~0.57 of a
+// 256x256 round on MI355X); 64x64 for problems too small to fill the chip.
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             hipStream_t st) {
   const int64_t big = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
-  if (big >= 192) return launch_mfma<256, 256, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
   const int64_t mid = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
+  if (big >= 192 && ceil_div(big, 256) * 100 <= ceil_div(mid, 512) * 57)
+    return launch_mfma<256, 256, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
   if (mid >= 192) return launch_mfma<128, 128, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
   return launch_mfma<64, 64, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
 }
