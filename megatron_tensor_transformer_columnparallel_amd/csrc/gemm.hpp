@@ -204,13 +204,18 @@ struct OperandLoader {
     istep = (int64_t)RSTEP * ld;
   }
 
-  // Whole tile inside the operand: global -> LDS without registers.
+  // Whole tile inside the operand: global -> LDS without registers.  Issued
+  // as inline assembly so that the compiler does not treat the in-flight LDS
+  // writes as aliasing the LDS reads of the other stage (it would otherwise
+  // wait for them before every fragment read); completion is awaited
+  // explicitly with wait_vmem() before the barrier that publishes the stage.
   __device__ __forceinline__ void issue_direct(bf16_t* region, int wave) {
 #pragma unroll
-    for (int i = 0; i < VECS; ++i)
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(ptr + i * istep),
-                                       (__attribute__((address_space(3))) void*)(region + (i * NT + wave * 64) * 8),
-                                       16, 0, 0);
+    for (int i = 0; i < VECS; ++i) {
+      const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(region + (i * NT + wave * 64) * 8);
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(ptr + i * istep), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
+    }
     ptr += kstep;
   }
 
@@ -339,32 +344,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   fb.init(wn * WTN, lane);
 
   const int m_rem = s.M - m0, n_rem = s.N - n0;
-  auto load = [&](int kt, bf16_t* st) {  // returns true when registers must be stored
-    if (kt < nkd) {
-      la.issue_direct(st, wave);
-      lb.issue_direct(st + BM * BK, wave);
-      return false;
-    }
-    const int k_rem = s.K - kb - kt * BK;
-    la.load_checked(m_rem, k_rem);
-    lb.load_checked(n_rem, k_rem);
-    return true;
-  };
-
-  if (nk > 0) {
-    if (load(0, lds)) {
-      la.store(lds, tid);
-      lb.store(lds + BM * BK, tid);
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    bf16_t* nx = lds + (cur ^ 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    const bool regs = more && load(kt + 1, nx);
-    const bf16_t* st = lds + cur * STAGE;
+  auto compute = [&](const bf16_t* st) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8_t af[FM], bfr[FN];
@@ -379,12 +359,62 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
-    if (regs) {
-      la.store(nx, tid);
-      lb.store(nx + BM * BK, tid);
+  };
+  auto load_checked = [&](int kt) {
+    const int k_rem = s.K - kb - kt * BK;
+    la.load_checked(m_rem, k_rem);
+    lb.load_checked(n_rem, k_rem);
+  };
+  auto store_regs = [&](bf16_t* st) {
+    la.store(st, tid);
+    lb.store(st + BM * BK, tid);
+  };
+
+  if (mn_inside) {
+    // Interior tile: every full K tile goes global -> LDS directly; this
+    // loop issues no other vector-memory operation, so the only wait on the
+    // DMA is the explicit one before each barrier.
+    if (nkd > 0) {
+      la.issue_direct(lds, wave);
+      lb.issue_direct(lds + BM * BK, wave);
+      wait_vmem();
+      __syncthreads();
     }
-    wait_vmem();
-    __syncthreads();
+    for (int kt = 0; kt < nkd; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nkd) {
+        bf16_t* nx = lds + (cur ^ 1) * STAGE;
+        la.issue_direct(nx, wave);
+        lb.issue_direct(nx + BM * BK, wave);
+      }
+      compute(lds + cur * STAGE);
+      wait_vmem();
+      __syncthreads();
+    }
+    // Ragged last K tile (fewer than BK values of k left): through registers.
+    if (nk > nkd) {
+      bf16_t* st = lds + (nkd & 1) * STAGE;
+      load_checked(nkd);
+      store_regs(st);
+      __syncthreads();
+      compute(st);
+      __syncthreads();
+    }
+  } else {
+    // Edge tile: bounds-checked loads through registers, double-buffered.
+    if (nk > 0) {
+      load_checked(0);
+      store_regs(lds);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) load_checked(kt + 1);
+      compute(lds + cur * STAGE);
+      if (more) store_regs(lds + (cur ^ 1) * STAGE);
+      __syncthreads();
+    }
   }
 
   // Epilogue staged through LDS (free after the K-loop's last barrier): one
