@@ -81,7 +81,8 @@ class Layer:
             r["dXa"], r["dWqkv"], r["dWo"] = emp((M, h)), emp((h, 3 * w)), emp((w, h))
             r["dXm"], r["dA"], r["dB"] = emp((M, h)), emp((h, f)), emp((f, h))
             r["ws_mlp"] = emp((tp.tp_mlp_bwd_workspace(bf, M, h, f),), torch.uint8)
-            r["ws_attn"] = emp((tp.tp_attn_bwd_workspace(bf, b, s, h, hs, d),), torch.uint8)
+            r["ws_attn"] = emp((max(tp.tp_attn_fwd_workspace(bf, b, s, h, hs, d),
+                                    tp.tp_attn_bwd_workspace(bf, b, s, h, hs, d)),), torch.uint8)
             self.sh.append(r)
         self.Za, self.Zm, self.dXa, self.dXm = emp((M, h)), emp((M, h)), emp((M, h)), emp((M, h))
         self.hs, self.w, self.f = hs, w, f
@@ -90,7 +91,8 @@ class Layer:
         tp, sh = self.tp, self.sh
         b, s, hs, d = self.b, self.s, self.hs, self.d
         for r in sh:
-            tp.tp_attn_fwd(self.X, r["Wqkv"], r["Wo"], r["QKV"], r["O"], r["lse"], r["Za"], b, s, hs, d, True)
+            tp.tp_attn_fwd(self.X, r["Wqkv"], r["Wo"], r["QKV"], r["O"], r["lse"], r["Za"], b, s, hs, d, True,
+                           ws=r["ws_attn"])
         tp.shard_reduce([r["Za"] for r in sh], self.Za)
         for r in sh:
             tp.tp_mlp_fwd(self.X, r["A"], r["B"], r["P"], r["H"], r["Zm"])

@@ -124,12 +124,20 @@ tps_status tp_mlp_bwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i,
  *   QKV_i  [b*sq x 3*hs*d] output (kept for backward)
  *   O_i    [b*sq x hs*d]  output (kept), head j at columns j*d..(j+1)*d
  *   lse_i  [b x hs x sq]  fp32 output (kept): log of each softmax row's sum
+ *                           of exp(S), i.e. P = exp(S - lse) row by row
  *   Z_i    [b*sq x h]     output: this shard's partial
- * Supported: dt = TPS_BF16, d in {64, 128, 256, 512}; TPS_EUNSUPPORTED otherwise.
+ *   ws     caller scratch of at least tp_attn_fwd_workspace(...) bytes
+ *          (16-byte aligned); holds the scores and probabilities of every
+ *          (batch, head), b*hs*sq*round_up(sq, 8)*6 bytes, and is free again
+ *          when the stream has passed the call.
+ * Supported: dt = TPS_BF16, d a multiple of 8; TPS_EUNSUPPORTED for fp32.
+ * TPS_EWORKSPACE if ws_bytes is too small (nothing is enqueued).
  * ------------------------------------------------------------------------ */
+size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d);
 tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d,
                        int causal, const void* X, const void* Wqkv_i, const void* Wo_i,
-                       void* QKV_i, void* O_i, float* lse_i, void* Z_i, tps_stream_t stream);
+                       void* QKV_i, void* O_i, float* lse_i, void* Z_i,
+                       void* ws, size_t ws_bytes, tps_stream_t stream);
 
 size_t tp_attn_bwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d);
 

@@ -10,7 +10,7 @@ from .binding import (  # noqa: F401
     TPS_BF16, TPS_F32, TpsError, LIB_PATH, lib,
     tps_partition, tps_version,
     tp_mlp_fwd, tp_mlp_bwd, tp_mlp_bwd_workspace,
-    tp_attn_fwd, tp_attn_bwd, tp_attn_bwd_workspace,
+    tp_attn_fwd, tp_attn_fwd_workspace, tp_attn_bwd, tp_attn_bwd_workspace,
     shard_reduce, shard_reduce_add,
     vocab_embed_fwd, vocab_embed_bwd, vocab_embed_bwd_workspace,
     tied_logits, tied_logits_bwd,

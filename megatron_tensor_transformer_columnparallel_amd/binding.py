@@ -29,7 +29,9 @@ SIGNATURES = {
     "tp_mlp_fwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tp_mlp_bwd_workspace": (_sz, [_i32, _i64, _i64, _i64]),
     "tp_mlp_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "tp_attn_fwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tp_attn_fwd_workspace": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64]),
+    "tp_attn_fwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                           _vp]),
     "tp_attn_bwd_workspace": (_sz, [_i32, _i64, _i64, _i64, _i64, _i64]),
     "tp_attn_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -156,7 +158,13 @@ def tp_mlp_bwd(X, A_i, B_i, P_i, H_i, dZ, dX_i, dA_i, dB_i, ws, stream=None):
 
 # ------------------------------------------------------------------ attention
 
-def tp_attn_fwd(X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, b, sq, hs, d, causal=True, stream=None):
+def tp_attn_fwd_workspace(dtype, b, sq, h, hs, d) -> int:
+    return lib.tp_attn_fwd_workspace(TPS_BF16 if dtype == torch.bfloat16 else TPS_F32, b, sq, h, hs, d)
+
+
+def tp_attn_fwd(X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, b, sq, hs, d, causal=True, ws=None, stream=None):
+    """ws: uint8 device tensor of at least tp_attn_fwd_workspace(...) bytes;
+    when omitted, one is taken from torch's allocator for this call."""
     dt = _dt(X)
     _same(dt, Wqkv_i, Wo_i, QKV_i, O_i, Z_i)
     _contig(X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i)
@@ -164,8 +172,12 @@ def tp_attn_fwd(X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, b, sq, hs, d, causal=Tr
     assert M == b * sq and Wqkv_i.shape == (h, 3 * hs * d) and Wo_i.shape == (hs * d, h)
     assert QKV_i.shape == (M, 3 * hs * d) and O_i.shape == (M, hs * d) and Z_i.shape == (M, h)
     assert lse_i.dtype == torch.float32 and lse_i.numel() == b * hs * sq
+    if ws is None:
+        ws = torch.empty((tp_attn_fwd_workspace(X.dtype, b, sq, h, hs, d),), dtype=torch.uint8, device=X.device)
+    _contig(ws)
     _check(lib.tp_attn_fwd(dt, b, sq, h, hs, d, 1 if causal else 0, _p(X), _p(Wqkv_i), _p(Wo_i), _p(QKV_i),
-                           _p(O_i), _p(lse_i), _p(Z_i), _stream(stream)), "tp_attn_fwd")
+                           _p(O_i), _p(lse_i), _p(Z_i), _p(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)), "tp_attn_fwd")
 
 
 def tp_attn_bwd_workspace(dtype, b, sq, h, hs, d) -> int:

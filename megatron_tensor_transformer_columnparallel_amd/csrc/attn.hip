@@ -1,269 +1,99 @@
 // Attention shard: QKV column-parallel by heads, per-head softmax attention,
 // row-parallel output projection.
 //
-// Forward core: flash-style kernel, one workgroup per (batch, head, 64-query
-// block), four wavefronts of 16 queries.  Each wavefront keeps its queries'
-// Q fragments in registers and accumulates O^T (head dim x queries) in
-// registers while streaming 32-key blocks of K and V^T through LDS with an
-// online softmax.  The transposed formulation S^T = K Q^T makes the MFMA
-// result layout (one query per lane column) directly usable as the B operand
-// of O^T += V^T P^T, so P never leaves registers and the per-query softmax
-// rescale is lane-local.  Saves lse = log(sum exp(S)) per query.
+// Forward core, per (batch, head): the scores S = Q K^T are an MFMA GEMM
+// whose epilogue stores S * scale * log2(e) in fp32 (tiles wholly above the
+// causal diagonal are neither computed nor stored); a row pass takes each
+// row's max and sum of exp2, writes the normalised probabilities P in bf16
+// and saves lse = log(sum exp(S * scale)); O = P V is a second GEMM whose
+// K-loop stops at the causal limit of its row tile.  With 4 heads of 512 on
+// 2048 tokens this keeps all 256 CUs busy, where one workgroup per
+// (head, query block) would occupy at most 128 of them, and it reads K and V
+// once per 256-wide tile instead of once per 64-query block.  S and P live in
+// a caller workspace of O(sq^2) per head (96 MB for 4 heads at sq = 2048).
 //
 // Backward core: the probabilities are recomputed from lse tile by tile by
 // the GEMM kernel (epilogue exp(S*scale - lse)) and written to the workspace
 // in bf16; dP = dO V^T is a GEMM into fp32 and a row pass forms
 // dS = P * (dP - delta) * scale with delta taken from the same P and dP;
 // dV = P^T dO, dQ = dS K and dK = dS^T Q are then MFMA GEMMs whose K-loops
-// skip the causally-zero blocks.  The workspace holds O(sq^2) per head, which the
-// 288 GB of HBM per device affords at these sequence lengths.
+// skip the causally-zero blocks.
 #include <string>
 
 #include "gemm.hpp"
 
 namespace tps {
 
-constexpr int kFlashBQ = 64;    // queries per workgroup: 4 query groups of 16
-constexpr int kFlashBKey = 32;  // keys per LDS block
-constexpr int kFlashThreads = 512;  // 8 waves: (query group, half of the head dim)
-// The running max used as the softmax reference is only raised when a row's
-// block max exceeds it by more than this many powers of two (log2 domain):
-// numerator and denominator share the reference, so the result is exact and
-// every exp2 stays below 2^kLazyRescale.
-constexpr float kLazyRescale = 8.f;
-
-// LDS stage: one K block (keys x head dim) and one V^T block (head dim x keys).
-template <int D>
-struct FlashStage {
-  static constexpr int KLD = D + 8;           // LDS row stride of K (elements)
-  static constexpr int VLD = kFlashBKey + 8;  // LDS row stride of V^T
-  static constexpr int K_ELEMS = kFlashBKey * KLD;
-  static constexpr int ELEMS = K_ELEMS + D * VLD;
-  static constexpr int K_CHUNKS = kFlashBKey * (D / 8);         // 16-byte chunks of K
-  static constexpr int V_BLOCKS = (kFlashBKey / 8) * (D / 8);   // 8x8 blocks of V
-  // Threads [0, V_THREADS) transpose V blocks, the others copy K chunks.
-  static constexpr int V_THREADS = V_BLOCKS < kFlashThreads / 2 ? V_BLOCKS : kFlashThreads / 2;
-  static constexpr int VB = (V_BLOCKS + V_THREADS - 1) / V_THREADS;
-  static constexpr int K_THREADS = kFlashThreads - V_THREADS;
-  static constexpr int KV = (K_CHUNKS + K_THREADS - 1) / K_THREADS;
-  static constexpr int REGS = (KV > 8 * VB ? KV : 8 * VB);
-};
-
-// Register staging of the next K/V block (global -> registers during the
-// current block's MFMAs, registers -> the other LDS stage afterwards).
-template <int D>
-struct FlashPrefetch {
-  using S = FlashStage<D>;
-  u32x4_t r[S::REGS];
-
-  __device__ __forceinline__ void load(const bf16_t* Kp, const bf16_t* Vp, int64_t ld, int k0, int sq, int tid) {
-    if (tid < S::V_THREADS) {
+// Scores of one (batch, head) problem, stored in the log2 domain:
+// S2(m, n) = acc * scale * log2(e).  With `causal`, 8-column chunks that lie
+// entirely after the query (n > m) are not stored: no pass reads them.
+struct EpiScore {
+  float* S;
+  int64_t ld, sp;  // row stride and per-(b,head) stride of S
+  int hs, causal;
+  float scale_log2;
+  __device__ void operator()(int zo, int zi, int m, int n, float v[8], int nv) const {
+    if (causal && n > m) return;
+    float t[8];
 #pragma unroll
-      for (int b = 0; b < S::VB; ++b) {
-        const int blk = tid + b * S::V_THREADS;
-        const int kq = blk % (kFlashBKey / 8), db = blk / (kFlashBKey / 8);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int key = k0 + kq * 8 + jj;
-          u32x4_t x = {0u, 0u, 0u, 0u};
-          if (blk < S::V_BLOCKS && key < sq) x = *reinterpret_cast<const u32x4_t*>(Vp + (int64_t)key * ld + db * 8);
-          r[b * 8 + jj] = x;
-        }
-      }
-    } else {
-      const int t = tid - S::V_THREADS;
-#pragma unroll
-      for (int i = 0; i < S::KV; ++i) {
-        const int c = t + i * S::K_THREADS;
-        const int row = c / (D / 8), cc = (c % (D / 8)) * 8;
-        const int key = k0 + row;
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if (c < S::K_CHUNKS && key < sq) x = *reinterpret_cast<const u32x4_t*>(Kp + (int64_t)key * ld + cc);
-        r[i] = x;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(bf16_t* st, int tid) const {
-    if (tid < S::V_THREADS) {
-      bf16_t* vts = st + S::K_ELEMS;
-#pragma unroll
-      for (int b = 0; b < S::VB; ++b) {
-        const int blk = tid + b * S::V_THREADS;
-        if (blk >= S::V_BLOCKS) continue;
-        const int kq = blk % (kFlashBKey / 8), db = blk / (kFlashBKey / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int w = i >> 1;
-          const bool hi = i & 1;
-          u32x4_t o;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t a = r[b * 8 + 2 * q][w], c = r[b * 8 + 2 * q + 1][w];
-            o[q] = hi ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-          }
-          *reinterpret_cast<u32x4_t*>(vts + (db * 8 + i) * S::VLD + kq * 8) = o;
-        }
-      }
-    } else {
-      const int t = tid - S::V_THREADS;
-#pragma unroll
-      for (int i = 0; i < S::KV; ++i) {
-        const int c = t + i * S::K_THREADS;
-        if (c < S::K_CHUNKS) {
-          const int row = c / (D / 8), cc = (c % (D / 8)) * 8;
-          *reinterpret_cast<u32x4_t*>(st + row * S::KLD + cc) = r[i];
-        }
-      }
-    }
+    for (int i = 0; i < 8; ++i) t[i] = v[i] * scale_log2;
+    store8<float>(S + (int64_t)(zo * hs + zi) * sp + (int64_t)m * ld + n, t, nv);
   }
 };
 
-// One workgroup per (batch, head, 64-query block); 8 waves.  Wave w handles
-// the 16 queries of group w % 4 and accumulates the head-dim half w / 4 of
-// O^T = V^T P^T; both waves of a group compute the same S^T = K Q^T (with the
-// group's Q fragments in registers) and the same online-softmax statistics.
-// The transposed formulation makes the S^T result layout (one query per lane
-// column) directly the B operand of the PV MFMA, so P never leaves registers
-// and the per-query rescale is lane-local.  K and V^T blocks are double
-// buffered in LDS; the next block is fetched into registers while the current
-// one is consumed.  Saves lse = log(sum exp(S)) per query for the backward.
-template <int D>
-__global__ void __launch_bounds__(kFlashThreads, 1)
-flash_fwd_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ out, float* __restrict__ lse, int sq,
-                 int hs, int causal, float scale_log2) {
-  using S = FlashStage<D>;
-  constexpr int DK = D / 32;             // MFMA k-steps over the head dim
-  constexpr int DH = D / 2;              // head-dim half accumulated per wave
-  constexpr int DT = DH / 16;            // 16-row tiles of this wave's O^T
-  constexpr int NCH = DK >= 2 ? 2 : 1;   // independent partial sums per S tile
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * S::ELEMS];
+// Causal zero padding of P: a row i is written up to this column so that
+// the O = P V GEMM (row tiles of at most 256, K-loop ending at the tile's
+// last row) only ever reads written values.
+constexpr int kProbPad = 256;
 
-  const int64_t ld = 3LL * hs * D;       // row stride of QKV
-  const int64_t ldo = (int64_t)hs * D;   // row stride of O
-  const int nqb = (sq + kFlashBQ - 1) / kFlashBQ;
-  const int id = blockIdx.x;
-  const int qb = nqb - 1 - (id % nqb);   // heaviest (last) query blocks first
-  const int rest = id / nqb;
-  const int j = rest % hs, bi = rest / hs;
-  const bf16_t* Qp = qkv + (int64_t)bi * sq * ld + (int64_t)j * D;
-  const bf16_t* Kp = Qp + (int64_t)hs * D;
-  const bf16_t* Vp = Qp + 2LL * hs * D;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qg = wave & 3, dh = wave >> 2;
-  const int g = lane >> 4;                       // lane group 0..3
-  const int myq = qb * kFlashBQ + qg * 16 + (lane & 15);
-
-  // Q^T fragments (B operand): column = my query, k = head-dim slice.
-  bf16x8_t qf[DK];
+// One wavefront per row of one (batch, head): online max / sum of exp2 over
+// the row's unmasked scores (8 per lane per step, merged across lanes), then
+// P = exp2(S2 - max) / sum in bf16 for the unmasked columns and zeros up to
+// the padding limit; lse = (max + log2(sum)) * ln 2.
+__global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restrict__ S2, bf16_t* __restrict__ P,
+                                                           float* __restrict__ lse, int64_t rows, int sq,
+                                                           int64_t ldp, int causal) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int i = (int)(w % sq);
+  const int ncol = causal ? i + 1 : sq;
+  const int64_t zend = causal ? min(ldp, (int64_t)((i + kProbPad) / kProbPad) * kProbPad) : ldp;
+  const float* sr = S2 + w * ldp;
+  bf16_t* pr = P + w * ldp;
+  float mx = -INFINITY, sum = 0.f;
+  for (int c = lane * 8; c < ncol; c += 64 * 8) {
+    float x[8];
+    const int nv = min(8, ncol - c);
+    load8<float>(sr + c, x, nv);
+    float bm = -INFINITY;
 #pragma unroll
-  for (int kk = 0; kk < DK; ++kk) {
-    u32x4_t x = {0u, 0u, 0u, 0u};
-    if (myq < sq) x = *reinterpret_cast<const u32x4_t*>(Qp + (int64_t)myq * ld + kk * 32 + g * 8);
-    qf[kk] = __builtin_bit_cast(bf16x8_t, x);
+    for (int e = 0; e < 8; ++e) bm = fmaxf(bm, e < nv ? x[e] : -INFINITY);
+    const float nm = fmaxf(mx, bm);
+    float bs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bs += e < nv ? exp2f(x[e] - nm) : 0.f;
+    sum = sum * exp2f(mx - nm) + bs;   // exp2(-inf) = 0 on the first step
+    mx = nm;
   }
-  f32x4_t oacc[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const int kend = causal ? min(sq, (qb + 1) * kFlashBQ) : sq;
-  const int nkb = (kend + kFlashBKey - 1) / kFlashBKey;
-  FlashPrefetch<D> pf;
-  pf.load(Kp, Vp, ld, 0, sq, tid);
-  pf.store(lds, tid);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * kFlashBKey;
-    const bf16_t* st = lds + (kb & 1) * S::ELEMS;
-    const bool more = kb + 1 < nkb;
-    if (more) pf.load(Kp, Vp, ld, k0 + kFlashBKey, sq, tid);   // lands during this block's MFMAs
-
-    // S^T tiles: rows = 16 keys, column = this lane's query.
-    f32x4_t sp[2][NCH];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) sp[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(st + (t * 16 + (lane & 15)) * S::KLD + g * 8 + kk * 32);
-        sp[t][kk % NCH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], sp[t][kk % NCH], 0, 0, 0);
-      }
-    // Online softmax in the log2 domain.  Element e of tile t is key
-    // k0 + 16t + 4g + e.
-    float sv[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = 0.f;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) x += sp[t][c][e];
-        const int key = k0 + t * 16 + g * 4 + e;
-        x *= scale_log2;
-        if (key >= sq || (causal && key > myq)) x = -INFINITY;
-        sv[t * 4 + e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Raise the reference (and rescale O) only when a row's max outgrew it;
-    // the first block always raises it from -inf (key 0 is never masked).
-    const bool grow = mx > m_run + kLazyRescale;
-    if (__ballot(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        oacc[t][0] *= alpha; oacc[t][1] *= alpha; oacc[t][2] *= alpha; oacc[t][3] *= alpha;
-      }
-      m_run = m_new;
-    }
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      sv[i] = exp2f(sv[i] - m_run);
-      rs += sv[i];
-    }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    l_run += rs;
-    // P^T as the B operand: k-slots 0..3 = keys 4g..4g+3, 4..7 = keys 16+4g..16+4g+3.
-    const u32x4_t pw = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]), pack_bf16x2(sv[4], sv[5]),
-                        pack_bf16x2(sv[6], sv[7])};
-    const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, pw);
-    // O^T (this wave's head-dim half) += V^T P^T; A fragment in pfrag's key order.
-    const bf16_t* vts = st + S::K_ELEMS + dh * DH * S::VLD;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const bf16_t* vrow = vts + (t * 16 + (lane & 15)) * S::VLD + g * 4;
-      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-      const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
-      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pfrag, oacc[t], 0, 0, 0);
-    }
-    if (more) pf.store(lds + ((kb + 1) & 1) * S::ELEMS, tid);
-    __syncthreads();
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float om = __shfl_xor(mx, o), os = __shfl_xor(sum, o);
+    const float nm = fmaxf(mx, om);
+    sum = (nm == -INFINITY) ? 0.f : sum * exp2f(mx - nm) + os * exp2f(om - nm);
+    mx = nm;
   }
-
-  if (myq < sq) {
-    const float inv = 1.f / l_run;
-    bf16_t* orow = out + ((int64_t)bi * sq + myq) * ldo + (int64_t)j * D + dh * DH;
+  const float inv = 1.f / sum;
+  for (int64_t c = lane * 8; c < zend; c += 64 * 8) {
+    const int nv = (int)min((int64_t)8, zend - c);
+    float x[8];
+    load8<float>(sr + c, x, (int)max(0, min(nv, ncol - (int)c)));
+    float p[8];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const float v[4] = {oacc[t][0] * inv, oacc[t][1] * inv, oacc[t][2] * inv, oacc[t][3] * inv};
-      store4<bf16_t>(orow + t * 16 + g * 4, v, 4);
-    }
-    if (g == 0 && dh == 0) lse[((int64_t)bi * hs + j) * sq + myq] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    for (int e = 0; e < 8; ++e) p[e] = (c + e < ncol) ? exp2f(x[e] - mx) * inv : 0.f;
+    store8<bf16_t>(pr + c, p, nv);
   }
+  if (lane == 0) lse[w] = (mx + log2f(sum)) * 0.69314718055994531f;
 }
 
 // One wavefront per row of one (batch, head): with P the stored (bf16)
@@ -305,17 +135,6 @@ __global__ void __launch_bounds__(256) attn_ds_kernel(const bf16_t* __restrict__
   }
 }
 
-template <int D>
-static tps_status launch_flash_fwd(const bf16_t* qkv, bf16_t* out, float* lse, int64_t b, int64_t sq, int64_t hs,
-                                   int causal, hipStream_t st) {
-  const int64_t grid = ceil_div(sq, kFlashBQ) * hs * b;
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL(flash_fwd_kernel<D>, dim3((unsigned)grid), dim3(kFlashThreads), 0, st, qkv, out, lse, (int)sq,
-                     (int)hs,
-                     causal, scale_log2);
-  return check_launch("flash_fwd_kernel");
-}
-
 static GemmShape shape(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
   GemmShape s;
   s.M = (int)M; s.N = (int)N; s.K = (int)K; s.lda = lda; s.ldb = ldb;
@@ -344,6 +163,22 @@ static AttnWs attn_ws_layout(int64_t b, int64_t sq, int64_t hs, int64_t d) {
   return w;
 }
 
+// Forward workspace: the log2-domain scores S2 (fp32) and the probabilities
+// P (bf16), both [b][hs][sq][ldp].
+struct AttnFwdWs {
+  size_t S, P, total;
+  int64_t ldp;
+};
+static AttnFwdWs attn_fwd_ws_layout(int64_t b, int64_t sq, int64_t hs) {
+  AttnFwdWs w;
+  w.ldp = (sq + 7) / 8 * 8;
+  const size_t n = (size_t)b * hs * sq * w.ldp;
+  w.S = 0;
+  w.P = align256(n * 4);
+  w.total = align256(w.P + n * 2);
+  return w;
+}
+
 #define TPS_REQ(cond, msg) \
   do { if (!(cond)) return set_error(TPS_EINVAL, std::string(fn) + ": " + (msg)); } while (0)
 #define TPS_TRY(expr) \
@@ -360,8 +195,7 @@ static tps_status attn_checks(const char* fn, tps_dtype dt, int64_t b, int64_t s
     TPS_REQ(aligned16(p), "pointer not 16-byte aligned");
   }
   if (dt != TPS_BF16) return set_error(TPS_EUNSUPPORTED, std::string(fn) + ": attention is implemented for bf16 only");
-  if (d != 64 && d != 128 && d != 256 && d != 512)
-    return set_error(TPS_EUNSUPPORTED, std::string(fn) + ": head dim must be 64, 128, 256 or 512");
+  TPS_REQ(d % 8 == 0, "head dim must be a multiple of 8");
   return TPS_OK;
 }
 
@@ -369,26 +203,50 @@ static tps_status attn_checks(const char* fn, tps_dtype dt, int64_t b, int64_t s
 
 using namespace tps;
 
+extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d) {
+  (void)dt;
+  (void)h;
+  if (b <= 0 || sq <= 0 || hs <= 0 || d <= 0) return 0;
+  return attn_fwd_ws_layout(b, sq, hs).total;
+}
+
 extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d, int causal,
                                   const void* X, const void* Wqkv_i, const void* Wo_i, void* QKV_i, void* O_i,
-                                  float* lse_i, void* Z_i, tps_stream_t stream) {
-  TPS_TRY(attn_checks("tp_attn_fwd", dt, b, sq, h, hs, d, {X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i}));
+                                  float* lse_i, void* Z_i, void* ws, size_t ws_bytes, tps_stream_t stream) {
+  TPS_TRY(attn_checks("tp_attn_fwd", dt, b, sq, h, hs, d, {X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, ws}));
+  const AttnFwdWs L = attn_fwd_ws_layout(b, sq, hs);
+  if (ws_bytes < L.total) return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t M = b * sq, w = hs * d;
+  const int64_t M = b * sq, w = hs * d, w3 = 3 * w;
   const bf16_t* x = (const bf16_t*)X;
   bf16_t* qkv = (bf16_t*)QKV_i;
   bf16_t* o = (bf16_t*)O_i;
+  char* base = static_cast<char*>(ws);
+  float* S2 = (float*)(base + L.S);
+  bf16_t* P = (bf16_t*)(base + L.P);
+  const int64_t ldp = L.ldp, sp = sq * L.ldp;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   // QKV_i = X Wqkv_i                       (NN)
-  TPS_TRY((gemm_bf16<true, false>(x, (const bf16_t*)Wqkv_i, shape(M, 3 * w, h, h, 3 * w),
-                                  EpiStore<bf16_t>{qkv, 3 * w, 0, 0}, st)));
-  tps_status s;
-  switch (d) {
-    case 64: s = launch_flash_fwd<64>(qkv, o, lse_i, b, sq, hs, causal ? 1 : 0, st); break;
-    case 128: s = launch_flash_fwd<128>(qkv, o, lse_i, b, sq, hs, causal ? 1 : 0, st); break;
-    case 256: s = launch_flash_fwd<256>(qkv, o, lse_i, b, sq, hs, causal ? 1 : 0, st); break;
-    default: s = launch_flash_fwd<512>(qkv, o, lse_i, b, sq, hs, causal ? 1 : 0, st); break;
-  }
-  TPS_TRY(s);
+  TPS_TRY((gemm_bf16<true, false>(x, (const bf16_t*)Wqkv_i, shape(M, w3, h, h, w3),
+                                  EpiStore<bf16_t>{qkv, w3, 0, 0}, st)));
+  // Per (batch, head) problems: z = bi*hs + j.
+  // S2 = Q K^T * scale * log2(e)           (NT)  [sq x sq] per head, fp32
+  GemmShape s = shape(sq, sq, d, w3, w3);
+  s.batch = (int)(b * hs);
+  s.batch_inner = (int)hs;
+  s.sa_o = sq * w3; s.sa_i = d; s.sb_o = sq * w3; s.sb_i = d;
+  s.skip_upper = causal ? 1 : 0;
+  TPS_TRY((gemm_bf16<true, true>(qkv, qkv + w, s, EpiScore{S2, ldp, sp, (int)hs, causal ? 1 : 0, scale_log2}, st)));
+  // P = softmax rows of S (bf16), lse
+  hipLaunchKernelGGL(attn_softmax_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, S2, P, lse_i,
+                     b * hs * sq, (int)sq, ldp, causal ? 1 : 0);
+  TPS_TRY(check_launch("attn_softmax_kernel"));
+  // O = P V                                (NN)  [sq x d] per head, K = keys <= query
+  GemmShape s2 = shape(sq, d, sq, ldp, w3);
+  s2.batch = (int)(b * hs); s2.batch_inner = (int)hs;
+  s2.sa_o = hs * sp; s2.sa_i = sp; s2.sb_o = sq * w3; s2.sb_i = d;
+  s2.kmode = causal ? 1 : 0;
+  TPS_TRY((gemm_bf16<true, false>(P, qkv + 2 * w, s2, EpiStore<bf16_t>{o, w, sq * w, d}, st)));
   // Z_i = O_i Wo_i                         (NN)
   return gemm_bf16<true, false>(o, (const bf16_t*)Wo_i, shape(M, h, w, w, h), EpiStore<bf16_t>{(bf16_t*)Z_i, h, 0, 0},
                                 st);

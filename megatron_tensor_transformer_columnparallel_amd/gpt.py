@@ -120,7 +120,9 @@ class TPGPT:
         self.dln = _emp((M, H), f32)
         self.dparts = [_emp((M, H)) for _ in range(c.n)]
         self.ws_mlp = _emp((tp.tp_mlp_bwd_workspace(torch.bfloat16, M, H, self.fi),), torch.uint8)
-        self.ws_attn = _emp((tp.tp_attn_bwd_workspace(torch.bfloat16, c.b, c.s, H, self.hs, c.d),), torch.uint8)
+        # one scratch buffer serves the attention forward and backward calls
+        self.ws_attn = _emp((max(tp.tp_attn_fwd_workspace(torch.bfloat16, c.b, c.s, H, self.hs, c.d),
+                                 tp.tp_attn_bwd_workspace(torch.bfloat16, c.b, c.s, H, self.hs, c.d)),), torch.uint8)
         self.ws_ln = _emp((tp.layernorm_bwd_workspace(M, H),), torch.uint8)
         self.ws_emb = _emp((tp.vocab_embed_bwd_workspace(M, max(n for _, n in self.vr)),), torch.uint8)
         # when a list, (start, end) torch.cuda.Events around each tied_logits call are appended to it
@@ -140,7 +142,7 @@ class TPGPT:
             tp.layernorm_fwd(x, lw["g1"], lw["b1"], a["y1"], a["m1"], a["r1"], cf.eps)
             for p, sa in zip(lw["sh"], a["sh"]):
                 tp.tp_attn_fwd(a["y1"], p["Wqkv"], p["Wo"], sa["QKV"], sa["O"], sa["lse"], sa["Za"],
-                               cf.b, cf.s, c.hs, cf.d, True)
+                               cf.b, cf.s, c.hs, cf.d, True, ws=self.ws_attn)
             tp.shard_reduce_add(x, [sa["Za"] for sa in a["sh"]], a["x2"])           # residual + g
             tp.layernorm_fwd(a["x2"], lw["g2"], lw["b2"], a["y2"], a["m2"], a["r2"], cf.eps)
             for p, sa in zip(lw["sh"], a["sh"]):

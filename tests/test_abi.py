@@ -78,7 +78,10 @@ ALIGNED = 1 << 20  # a fake, 16-byte aligned address: validation fails before an
     ("tied_logits", (1, 16, 64, 150, 154, ALIGNED, ALIGNED, ALIGNED, None)),                      # ldl % 8
     ("vocab_embed_fwd", (1, 16, 64, 0, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # v_rows = 0
     ("vocab_embed_fwd", (1, 16, 64, -1, 10, ALIGNED, ALIGNED, ALIGNED, None)),                    # v_start < 0
-    ("tp_attn_fwd", (1, 1, 64, 256, 2, 64, 1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, None)),
+    ("tp_attn_fwd", (1, 1, 64, 256, 2, 64, 1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED,
+                     ALIGNED, 1 << 30, None)),                                                      # null lse
+    ("tp_attn_fwd", (1, 1, 64, 256, 2, 60, 1, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                     ALIGNED, 1 << 30, None)),                                                      # d % 8
     ("layernorm_fwd", (0, 1, 4, 0, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),
     ("layernorm_fwd", (0, 1, 4, 12, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),  # H % 8
     ("shard_reduce_add", (0, ALIGNED, 1, 0, None, 0, ALIGNED, 1, None, 16, None)),                  # n_parts = 0
@@ -113,8 +116,14 @@ def test_workspace_queries_and_too_small_workspace(tp):
     assert ws >= 2048 * 4 * 512 * 2 + 4 * 2048 * 4 + 2 * 4 * 2048 * 2048 * 2 + 2048 * 3 * 2048 * 2
     st = lib.tp_attn_bwd(1, 1, 2048, 4096, 4, 512, 1, *([ALIGNED] * 11), ws - 1, None)
     assert st == tp.binding.TPS_EWORKSPACE
+    # forward: fp32 log2-domain scores + bf16 probabilities per (batch, head)
+    wf = lib.tp_attn_fwd_workspace(1, 1, 2048, 4096, 4, 512)
+    assert wf >= 4 * 2048 * 2048 * (4 + 2)
+    assert lib.tp_attn_fwd_workspace(1, 1, 30, 64, 2, 64) >= 2 * 30 * 32 * 6
+    st = lib.tp_attn_fwd(1, 1, 2048, 4096, 4, 512, 1, *([ALIGNED] * 8), wf - 1, None)
+    assert st == tp.binding.TPS_EWORKSPACE
 
 
 def test_attention_fp32_is_reported_unsupported(tp):
-    st = tp.lib.tp_attn_fwd(0, 1, 16, 64, 2, 64, 1, *([ALIGNED] * 7), None)
+    st = tp.lib.tp_attn_fwd(0, 1, 16, 64, 2, 64, 1, *([ALIGNED] * 8), 1 << 30, None)
     assert st == tp.binding.TPS_EUNSUPPORTED

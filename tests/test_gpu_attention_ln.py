@@ -47,7 +47,9 @@ def run_attn_shard(tp, X, Wqkv, Wo, dZ, b, sq, hs, d, causal):
     (73, 1, 80, 512, 2, 512, 2, True),     # head dim 512 (the page-1 shape's head size)
     (74, 3, 33, 128, 2, 256, 1, True),     # single shard, batch 3
     (75, 1, 1, 128, 2, 64, 2, True),       # one position: O = V
-    (78, 1, 300, 128, 2, 64, 2, True),     # peaked softmax (weights x 8): the running max moves a lot
+    (78, 1, 300, 128, 2, 64, 2, True),     # peaked softmax (weights x 8): large score range per row
+    (79, 1, 520, 256, 4, 96, 2, True),     # head dim 96; rows past two 256-wide probability pads
+    (80, 2, 261, 128, 2, 40, 1, True),     # head dim 40, sq not a multiple of 8 (padded score rows)
 ])
 def test_attention_shards_match_oracle(tp, w, b, sq, h, heads, d, n, causal):
     say(f"tp_attn fwd+bwd b={b} sq={sq} h={h} heads={heads} d={d} N={n} causal={causal}")
