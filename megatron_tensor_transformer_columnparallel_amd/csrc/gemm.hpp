@@ -159,7 +159,13 @@ __device__ __forceinline__ u32x4_t mask_vec8(u32x4_t v, int nvalid) {
 // fills 64 consecutive slots with one instruction: global_load_lds_dwordx4
 // (lane l lands at LDS base + 16 l) for interior tiles, or 16-byte register
 // stores after bounds-checked loads at the edges.
-__device__ __forceinline__ int kc_swizzle(int row) { return row & 7; }
+// K-contiguous rows of CPR chunks: 8 consecutive rows reading the same chunk
+// land in 8 distinct 16-byte slots of a 128-byte bank window.
+template <int CPR>
+__device__ __forceinline__ int kc_swizzle(int row) {
+  if constexpr (CPR == 8) return row & 7;
+  else return (row >> 1) & 3;   // two 64-byte rows per window
+}
 
 template <int R>
 __device__ __forceinline__ int mn_swizzle(int k) {
@@ -172,75 +178,102 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
-// Loader of one operand tile of R rows (m or n) by BK = 64.  Each thread owns
-// VECS slots (tid + i*NT); all of them share one global column offset, so a
-// single pointer walks through K.
-template <int R, int NT, bool KC>
+// Loader of one operand tile of R rows (m or n) by BK (32 or 64).  Each
+// thread owns VECS slots (tid + i*NT); all of them share one global column
+// offset, so a single pointer walks through K.
+template <int R, int NT, bool KC, int BK>
 struct OperandLoader {
-  static constexpr int BK = 64;
   static constexpr int CPR = KC ? BK / 8 : R / 8;   // 16-byte chunks per LDS row
   static constexpr int VECS = R * BK / 8 / NT;      // slots per thread
   static constexpr int RSTEP = NT / CPR;            // LDS rows between a thread's slots
-  static_assert(VECS >= 1 && NT % CPR == 0 && RSTEP % 16 == 0, "operand tile vs thread count");
+  static constexpr int PERIOD = KC ? 8 : 16;        // rows after which the swizzle repeats
+  // A thread's slots sit RSTEP rows apart: either all at one swizzled column
+  // (RSTEP a multiple of the period) or alternating between two (half of it).
+  static constexpr bool ALT = RSTEP % PERIOD != 0;
+  static_assert(VECS >= 1 && NT % CPR == 0 && (2 * RSTEP) % PERIOD == 0, "operand tile vs thread count");
   static_assert(KC || R >= 64, "M/N-contiguous tiles need at least 8 chunks per k-row");
 
   u32x4_t v[VECS];
-  const bf16_t* ptr;     // global address of this thread's first slot in the next K tile
-  int64_t istep, kstep;  // elements between the thread's slots; between K tiles
-  int row0, col0;        // KC: (m/n row, k column) of the first slot; else (k row, m/n column)
+  const bf16_t* base;    // tile origin (row r0, current K tile) -- the same for every lane
+  uint32_t voff;         // bytes from `base` to this thread's first slot
+  uint32_t istep;        // bytes between the thread's slots
+  int64_t kstep;         // elements between K tiles
+  int row0;              // KC: m/n row of the first slot; else its k row
+  int col[2];            // KC: k column, else m/n column, of even and odd slots
 
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (KC) return kc_swizzle<CPR>(row);
+    else return mn_swizzle<R>(row);
+  }
+  __device__ __forceinline__ int slot_col(int i) const { return (ALT && (i & 1)) ? col[1] : col[0]; }
+  // byte offset of slot i from `base`
+  __device__ __forceinline__ uint32_t slot_off(int i) const {
+    return voff + (uint32_t)i * istep + ((ALT && (i & 1)) ? (uint32_t)(col[1] - col[0]) * 2u : 0u);
+  }
+
+  // ld * rows of the tile * 2 bytes must stay below 2^32 (checked on the host).
   __device__ __forceinline__ void init(const bf16_t* p, int64_t ld, int r0, int k0, int tid) {
     const int row = tid / CPR, pos = tid % CPR;
     row0 = row;
+    col[0] = (pos ^ swz(row)) * 8;
+    col[1] = (pos ^ swz(row + RSTEP)) * 8;
     if constexpr (KC) {
-      col0 = (pos ^ kc_swizzle(row)) * 8;
-      ptr = p + (int64_t)(r0 + row) * ld + k0 + col0;
+      base = p + (int64_t)r0 * ld + k0;
       kstep = BK;
     } else {
-      col0 = (pos ^ mn_swizzle<R>(row)) * 8;
-      ptr = p + (int64_t)(k0 + row) * ld + r0 + col0;
+      base = p + (int64_t)k0 * ld + r0;
       kstep = (int64_t)BK * ld;
     }
-    istep = (int64_t)RSTEP * ld;
+    voff = (uint32_t)(((int64_t)row * ld + col[0]) * 2);
+    istep = (uint32_t)(RSTEP * ld * 2);
   }
 
-  // Whole tile inside the operand: global -> LDS without registers.  Issued
-  // as inline assembly so that the compiler does not treat the in-flight LDS
-  // writes as aliasing the LDS reads of the other stage (it would otherwise
-  // wait for them before every fragment read); completion is awaited
-  // explicitly with wait_vmem() before the barrier that publishes the stage.
+  // Whole tile inside the operand: global -> LDS without registers, as
+  // global_load_lds_dwordx4 with the wave-uniform base in scalar registers
+  // and a 32-bit per-lane offset.  Issued as inline assembly so that the
+  // compiler does not treat the in-flight LDS writes as aliasing the LDS
+  // reads of the other stages (it would otherwise wait for them before every
+  // fragment read); completion is awaited explicitly with a vmcnt wait before
+  // the barrier that publishes the stage.
   __device__ __forceinline__ void issue_direct(bf16_t* region, int wave) {
+    // readfirstlane yields a signed int: each half goes through uint32_t so
+    // that the low half is zero-extended, not sign-extended, into 64 bits.
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
       const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(region + (i * NT + wave * 64) * 8);
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                   :: "v"(ptr + i * istep), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(slot_off(i)), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
     }
-    ptr += kstep;
+    base += kstep;
   }
 
   // Edge tile: r_rem rows (m/n) and k_rem k remain from the tile origin;
   // elements outside are zero.
   __device__ __forceinline__ void load_checked(int r_rem, int k_rem) {
+    const char* b = reinterpret_cast<const char*>(base);
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
       u32x4_t x = {0u, 0u, 0u, 0u};
+      const int rr = row0 + i * RSTEP, cc = slot_col(i);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b + slot_off(i));
       if constexpr (KC) {
-        const int r = row0 + i * RSTEP;
-        if (r < r_rem && col0 < k_rem) {
-          x = *reinterpret_cast<const u32x4_t*>(ptr + i * istep);
-          if (col0 + 8 > k_rem) x = mask_vec8(x, k_rem - col0);
+        if (rr < r_rem && cc < k_rem) {
+          x = *src;
+          if (cc + 8 > k_rem) x = mask_vec8(x, k_rem - cc);
         }
       } else {
-        const int k = row0 + i * RSTEP;
-        if (k < k_rem && col0 < r_rem) {
-          x = *reinterpret_cast<const u32x4_t*>(ptr + i * istep);
-          if (col0 + 8 > r_rem) x = mask_vec8(x, r_rem - col0);
+        if (rr < k_rem && cc < r_rem) {
+          x = *src;
+          if (cc + 8 > r_rem) x = mask_vec8(x, r_rem - cc);
         }
       }
       v[i] = x;
     }
-    ptr += kstep;
+    base += kstep;
   }
 
   __device__ __forceinline__ void store(bf16_t* region, int tid) const {
@@ -252,17 +285,17 @@ struct OperandLoader {
 // MFMA operand fragments of one wave: FR blocks of 16 rows starting at row
 // `base` of an R-row tile.  A fragment gives lane l row (l & 15), k = 8*(l >> 4)
 // .. +7 of the current 32-wide k-step.
-template <int R, int FR, bool KC>
+template <int R, int FR, bool KC, int BK>
 struct FragReader {
-  static constexpr int BK = 64;
-  int off[KC ? 2 : FR];  // KC: per k-step; else per fragment (element offsets)
+  static constexpr int KS = BK / 32;
+  int off[KC ? KS : FR];  // KC: per k-step; else per fragment (element offsets)
 
   __device__ __forceinline__ void init(int base, int lane) {
     const int fr = lane & 15, fg = lane >> 4;
     if constexpr (KC) {
       const int r = base + fr;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) off[ks] = r * BK + (((ks * 4 + fg) ^ kc_swizzle(r)) * 8);
+      for (int ks = 0; ks < KS; ++ks) off[ks] = r * BK + (((ks * 4 + fg) ^ kc_swizzle<BK / 8>(r)) * 8);
     } else {
       // lane j of a 16-lane group supplies k-row (j >> 2) and columns 4*(j & 3)..+3
       // of its group's 4 x 16 block; the hardware returns column j, k-rows 0..3.
@@ -291,9 +324,11 @@ struct FragReader {
 };
 
 // One workgroup computes a BM x BN tile with WM x WN waves, each wave a
-// (BM/WM) x (BN/WN) block of 16x16 MFMA tiles, K in steps of BK = 64 through
-// two LDS stages: while the MFMAs consume one stage, the next K tile is in
-// flight to the other.
+// (BM/WM) x (BN/WN) block of 16x16 MFMA tiles.  K advances in tiles of BK
+// through two LDS stages.  Interior tiles (the whole BM x BN block inside
+// the matrix) load the next K tile from global memory straight into LDS
+// while the MFMAs consume the current one; edge tiles go through
+// bounds-checked register loads.  The epilogue runs from the accumulators.
 template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKC, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64, 1)
 gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, GemmShape s, Epi epi) {
@@ -302,9 +337,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int KS = BK / 32;
   constexpr int STAGE = (BM + BN) * BK;                 // bf16 elements per LDS stage
-  constexpr int BAND_BYTES = WTM * (BN + 4) * 4;        // fp32 epilogue band
-  constexpr int LDS_BYTES = 4 * STAGE > BAND_BYTES ? 4 * STAGE : BAND_BYTES;
-  static_assert(BK == 64, "loaders and swizzles assume BK = 64");
+  constexpr int LDS_BYTES = 2 * 2 * STAGE;             // two stages
+  static_assert(BK == 32 || BK == 64, "loaders and swizzles support BK = 32 or 64");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_BYTES / 2];
@@ -324,7 +358,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   k_range(s, m0, BM, BK, kb, ke);
   if (s.skip_upper && n0 > m0 + BM - 1) ke = kb;
   const int nk = (ke - kb + BK - 1) / BK;
-  // K tiles [0, nkd) are loaded directly (tile inside M and N, all 64 k in range)
+  // K tiles [0, nkd) are loaded directly (tile inside M and N, all BK k in range)
   const bool mn_inside = (m0 + BM <= s.M) && (n0 + BN <= s.N);
   const int nkd = mn_inside ? (ke - kb) / BK : 0;
 
@@ -334,12 +368,14 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  OperandLoader<BM, NT, AK> la;
-  OperandLoader<BN, NT, BKC> lb;
+  using LoaderA = OperandLoader<BM, NT, AK, BK>;
+  using LoaderB = OperandLoader<BN, NT, BKC, BK>;
+  LoaderA la;
+  LoaderB lb;
   la.init(A + zo * s.sa_o + zi * s.sa_i, s.lda, m0, kb, tid);
   lb.init(B + zo * s.sb_o + zi * s.sb_i, s.ldb, n0, kb, tid);
-  FragReader<BM, FM, AK> fa;
-  FragReader<BN, FN, BKC> fb;
+  FragReader<BM, FM, AK, BK> fa;
+  FragReader<BN, FN, BKC, BK> fb;
   fa.init(wm * WTM, lane);
   fb.init(wn * WTN, lane);
 
@@ -347,18 +383,42 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   auto compute = [&](const bf16_t* st) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8_t af[FM], bfr[FN];
+      if constexpr (FM * FN <= 32) {
+        bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = fa.read(st, ks, i);
+        for (int i = 0; i < FM; ++i) af[i] = fa.read(st, ks, i);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = fb.read(st + BM * BK, ks, j);
-      // operands swapped: the result's lane layout is C(m = lane & 15, n = 4*(lane >> 4) + e)
+        for (int j = 0; j < FN; ++j) bfr[j] = fb.read(st + BM * BK, ks, j);
+        // operands swapped: the result's lane layout is C(m = lane & 15, n = 4*(lane >> 4) + e)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      } else {
+        // Large wave tile: all B fragments, A fragments one block row at a
+        // time with the next one in flight (bounded register footprint).
+        bf16x8_t bfr[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[j] = fb.read(st + BM * BK, ks, j);
+        bf16x8_t an = fa.read(st, ks, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const bf16x8_t a = an;
+          if (i + 1 < FM) an = fa.read(st, ks, i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], a, acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
+  };
+  auto issue = [&](int kt) {
+    bf16_t* st = lds + (kt & 1) * STAGE;
+    la.issue_direct(st, wave);
+    lb.issue_direct(st + BM * BK, wave);
   };
   auto load_checked = [&](int kt) {
     const int k_rem = s.K - kb - kt * BK;
@@ -371,81 +431,70 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   };
 
   if (mn_inside) {
-    // Interior tile: every full K tile goes global -> LDS directly; this
-    // loop issues no other vector-memory operation, so the only wait on the
-    // DMA is the explicit one before each barrier.
+    // Interior tile: every full K tile goes global -> LDS directly; the DMA
+    // of tile kt+1 is in flight while tile kt's fragments are read and
+    // multiplied.  No other vector-memory operation is issued in this loop,
+    // so the vmcnt wait covers exactly that DMA.
     if (nkd > 0) {
-      la.issue_direct(lds, wave);
-      lb.issue_direct(lds + BM * BK, wave);
+      issue(0);
       wait_vmem();
       __syncthreads();
     }
     for (int kt = 0; kt < nkd; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nkd) {
-        bf16_t* nx = lds + (cur ^ 1) * STAGE;
-        la.issue_direct(nx, wave);
-        lb.issue_direct(nx + BM * BK, wave);
-      }
-      compute(lds + cur * STAGE);
+      if (kt + 1 < nkd) issue(kt + 1);
+      compute(lds + (kt & 1) * STAGE);
       wait_vmem();
-      __syncthreads();
+      __syncthreads();   // tile kt+1 visible; tile kt's stage consumed by every wave
     }
-    // Ragged last K tile (fewer than BK values of k left): through registers.
     if (nk > nkd) {
       bf16_t* st = lds + (nkd & 1) * STAGE;
       load_checked(nkd);
       store_regs(st);
       __syncthreads();
       compute(st);
-      __syncthreads();
     }
   } else {
-    // Edge tile: bounds-checked loads through registers, double-buffered.
-    if (nk > 0) {
-      load_checked(0);
-      store_regs(lds);
-      __syncthreads();
-    }
+    // Edge tile: bounds-checked loads through registers into alternating
+    // stages (no register double-buffering: the loaded values are dead once
+    // stored, which keeps them out of the MFMA loop's register budget).
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) load_checked(kt + 1);
-      compute(lds + cur * STAGE);
-      if (more) store_regs(lds + (cur ^ 1) * STAGE);
-      __syncthreads();
+      bf16_t* st = lds + (kt & 1) * STAGE;
+      load_checked(kt);
+      store_regs(st);
+      __syncthreads();   // stage kt & 1 written; everyone is past tile kt-1
+      compute(st);
     }
   }
 
-  // Epilogue staged through LDS (free after the K-loop's last barrier): one
-  // band of wave-rows at a time writes its accumulators as fp32, then the
-  // whole workgroup applies the epilogue to 8 consecutive columns per thread
-  // with 16-byte accesses.
-  float* band_buf = reinterpret_cast<float*>(lds);
-  constexpr int SLD = BN + 4;
-  const int em = lane & 15, en = (lane >> 4) * 4;
+  // Epilogue straight from the accumulators.  Fragment j of block row i gives
+  // lane l the row m = 16 i + (l & 15) and the columns 16 j + 4 g .. +3,
+  // g = l >> 4.  For a pair of fragments (j0, j1) the lanes of groups g and
+  // g ^ 1 (lanes l and l ^ 16) trade four values, after which each lane holds
+  // 8 consecutive columns: j0's 8 g' .. +7 for even g, j1's for odd g, with
+  // g' = g >> 1.  Each lane then applies the epilogue to its 8 columns with
+  // 16-byte accesses; no LDS and no barrier are involved, so waves leave
+  // the K-loop independently.
+  static_assert(FN % 2 == 0, "fragments are paired along n");
+  const int g = lane >> 4;
+  const bool odd = g & 1;
 #pragma unroll
-  for (int band = 0; band < WM; ++band) {
-    if (wm == band) {
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 16 + (lane & 15);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int jp = 0; jp < FN; jp += 2) {
+      const f32x4_t& a0 = acc[i][jp];
+      const f32x4_t& a1 = acc[i][jp + 1];
+      float v[8];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          *reinterpret_cast<f32x4_t*>(band_buf + (i * 16 + em) * SLD + wn * WTN + j * 16 + en) = acc[i][j];
-    }
-    __syncthreads();
-    constexpr int CHUNKS = WTM * BN / 8;
-    for (int c = tid; c < CHUNKS; c += NT) {
-      const int r = c / (BN / 8), cc = (c % (BN / 8)) * 8;
-      const int m = m0 + band * WTM + r, n = n0 + cc;
-      if (m < s.M && n < s.N) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(band_buf + r * SLD + cc);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(band_buf + r * SLD + cc + 4);
-        float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        epi(zo, zi, m, n, v, min(8, s.N - n));
+      for (int e = 0; e < 4; ++e) {
+        const float send = odd ? a0[e] : a1[e];
+        const float recv = __shfl_xor(send, 16);
+        v[e] = odd ? recv : a0[e];
+        v[4 + e] = odd ? a1[e] : recv;
       }
+      const int n = n0 + wn * WTN + (jp + (odd ? 1 : 0)) * 16 + (g >> 1) * 8;
+      if (m < s.M && n < s.N) epi(zo, zi, m, n, v, min(8, s.N - n));
     }
-    __syncthreads();
   }
 }
 
@@ -519,23 +568,27 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
   const int64_t tiles = ceil_div(s.M, BM) * ceil_div(s.N, BN) * (int64_t)s.batch;
   if (tiles == 0) return TPS_OK;
   if (tiles > 0x7fffffff) return set_error(TPS_EINVAL, "gemm: too many tiles");
+  // per-lane operand offsets inside a tile are 32-bit byte offsets
+  const int64_t span_a = (AK ? BM : BK) * s.lda * 2, span_b = (BKC ? BN : BK) * s.ldb * 2;
+  if (span_a >= (1LL << 32) || span_b >= (1LL << 32))
+    return set_error(TPS_EINVAL, "gemm: leading dimension too large for 32-bit tile offsets");
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, AK, BKC, Epi>), dim3((unsigned)tiles),
                      dim3(WM * WN * 64), 0, st, A, B, s, epi);
   return check_launch("gemm_bf16_kernel");
 }
 
-// Tile shape by problem size: 256x256 with 8 waves (one workgroup per CU) or
-// 128x128 with 4 waves (two per CU), whichever needs fewer time units for
-// its rounds of resident workgroups (a 128x128 round measured at ~0.57 of a
-// 256x256 round on MI355X); 64x64 for problems too small to fill the chip.
+// Tile shape by problem size, from cold-cache timings of these kernels on
+// MI355X: 256x256 (one 8-wave workgroup per CU) whenever it yields at least
+// 192 tiles; otherwise 128x128 (4 waves, two workgroups per CU), which beat
+// 256x256 and 128x256 on every M = 2048, N <= 4096 shape of the layer; 64x64
+// for problems too small for 64 tiles of 128x128.
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             hipStream_t st) {
   const int64_t big = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
   const int64_t mid = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
-  if (big >= 192 && ceil_div(big, 256) * 100 <= ceil_div(mid, 512) * 57)
-    return launch_mfma<256, 256, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
-  if (mid >= 192) return launch_mfma<128, 128, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
+  if (big >= 192) return launch_mfma<256, 256, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
+  if (mid >= 64) return launch_mfma<128, 128, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
   return launch_mfma<64, 64, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
 }
 
