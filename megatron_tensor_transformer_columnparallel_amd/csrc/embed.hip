@@ -9,17 +9,21 @@
 // Deterministic and free of atomics: the composite keys (local_row << 32 | t)
 // are unique, so sorting them (bitonic network) yields one fixed order, with
 // each row's tokens contiguous and ascending in t.  One wavefront per segment
-// head then sums that row's dY rows in fp32 in that order and adds the sum to
-// dE_r with a plain read-modify-write (each row has exactly one owner).
+// head then adds that row's dY rows, in that order, to the row of dE_r in
+// fp32 with a plain read-modify-write (each row has exactly one owner).
 #include "common.hpp"
 
 namespace tps {
 
+// One wavefront per token.  Every lane issues all of its 16-byte loads for
+// a slab of 64 x 8 chunks before any store, so a whole 8 KiB bf16 row is in
+// flight at once.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restrict__ ids,
                                                          const T* __restrict__ E, T* __restrict__ Y,
                                                          int64_t ntok, int64_t H, int64_t v_start,
                                                          int64_t v_rows) {
+  constexpr int U = 8;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= ntok) return;
   const int lane = threadIdx.x & 63;
@@ -27,12 +31,20 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restric
   const bool inr = local >= 0 && local < v_rows;
   const int64_t nch = H * (int64_t)sizeof(T) / 16;  // 16-byte chunks per row
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(Y + t * H);
-  if (inr) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(E + local * H);
-    for (int64_t c = lane; c < nch; c += 64) dst[c] = src[c];
-  } else {
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    for (int64_t c = lane; c < nch; c += 64) dst[c] = z;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(E + (inr ? local : 0) * H);
+  for (int64_t c0 = lane; c0 < nch; c0 += 64 * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * 64;
+      v[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (inr && c < nch) v[u] = src[c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * 64;
+      if (c < nch) dst[c] = v[u];
+    }
   }
 }
 
@@ -68,7 +80,7 @@ __global__ void __launch_bounds__(1024) bitonic_local_kernel(uint64_t* keys, int
   for (int64_t k = kfirst; k <= klast; k <<= 1) {
     for (int j = (int)((kouter ? chunk : k) >> 1); j >= 1; j >>= 1) {
       for (int q = threadIdx.x; q < half; q += 1024) {
-        const int i = 2 * j * (q / j) + (q % j);
+        const int i = ((q & ~(j - 1)) << 1) | (q & (j - 1));   // j is a power of two
         const int l = i + j;
         const bool asc = ((base + i) & k) == 0;
         const uint64_t a = s[i], b = s[l];
@@ -80,23 +92,155 @@ __global__ void __launch_bounds__(1024) bitonic_local_kernel(uint64_t* keys, int
   for (int i = threadIdx.x; i < chunk; i += 1024) keys[base + i] = s[i];
 }
 
+// Single-workgroup stable sort by row for T <= kRadixMax tokens: the
+// 32-bit keys (row << tbits | t) start in token order, so a stable LSD radix
+// sort on the row bits (8 bits per pass) leaves each row's tokens ascending
+// in t.  Out-of-range tokens get row = v_rows and sort last.  Per pass, each
+// of the 16 waves owns a contiguous run of the keys and its own 256 digit
+// counters; lanes with equal digits are found with eight ballots, so a
+// block's count per digit and a lane's rank among earlier lanes with its
+// digit need no atomics.  One exclusive scan over (digit, wave) in
+// digit-major order gives every wave its starting position per digit.  The
+// result is written as the 64-bit keys (row << 32 | t, or kNoKey) the
+// accumulation kernel reads.
+constexpr int kRadixMax = 16384;
+constexpr int kRadixThreads = 1024;
+constexpr int kRadixWaves = kRadixThreads / 64;
+
+// Lanes of the wave holding the same 8-bit digit as this lane (among valid lanes).
+__device__ __forceinline__ uint64_t same_digit_lanes(uint32_t d, bool valid) {
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t bal = __ballot(valid && ((d >> bit) & 1u));
+    same &= ((d >> bit) & 1u) ? bal : ~bal;
+  }
+  return same;
+}
+
+__global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const int32_t* __restrict__ ids,
+                                                                          uint64_t* __restrict__ keys_out,
+                                                                          int ntok, int64_t v_start,
+                                                                          int v_rows, int tbits, int rbits) {
+  __shared__ uint32_t kb[2][kRadixMax];
+  __shared__ uint32_t off[kRadixWaves * 256];   // [wave][digit]: a wave's counters are contiguous
+  __shared__ uint32_t wsum[kRadixWaves];
+  static_assert(256 * kRadixWaves == 4 * kRadixThreads, "scan: four entries per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t tmask = (1u << tbits) - 1u;
+  {
+    // all id loads in flight at once, then the keys
+    constexpr int PER = kRadixMax / kRadixThreads;
+    int32_t idv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = tid + i * kRadixThreads;
+      idv[i] = t < ntok ? ids[t] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = tid + i * kRadixThreads;
+      if (t < ntok) {
+        const int64_t local = (int64_t)idv[i] - v_start;
+        const uint32_t row = (local >= 0 && local < v_rows) ? (uint32_t)local : (uint32_t)v_rows;
+        kb[0][t] = (row << tbits) | (uint32_t)t;
+      }
+    }
+  }
+  __syncthreads();
+  const int per = (ntok + kRadixWaves - 1) / kRadixWaves;   // keys per wave
+  const int lo = min(ntok, wave * per), hi = min(ntok, lo + per);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t* my = off + wave * 256;
+  int cur = 0;
+  for (int shift = 0; shift < rbits; shift += 8) {
+    for (int i = lane; i < 256; i += 64) my[i] = 0u;
+    // counts per (wave, digit): the first lane of each digit group adds the
+    // group's size (only this wave touches its counters)
+    for (int b = lo; b < hi; b += 64) {
+      const int q = b + lane;
+      const bool valid = q < hi;
+      const uint32_t d = valid ? (kb[cur][q] >> tbits >> shift) & 255u : 0u;
+      const uint64_t same = same_digit_lanes(d, valid);
+      if (valid && (same & lt_mask) == 0) my[d] += (uint32_t)__popcll(same);
+    }
+    __syncthreads();
+    // exclusive scan over (digit, wave) in digit-major order: entry e is
+    // (digit e / 16, wave e % 16); 4 consecutive entries per thread, a
+    // shuffle scan per wave, then the 16 wave totals
+    {
+      uint32_t c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        c[i] = off[(e % kRadixWaves) * 256 + e / kRadixWaves];
+      }
+      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+      uint32_t x = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[wave] = x;
+      __syncthreads();
+      uint32_t run = x - mine;
+      for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        off[(e % kRadixWaves) * 256 + e / kRadixWaves] = run;
+        run += c[i];
+      }
+    }
+    __syncthreads();
+    // stable scatter: rank among earlier lanes of the block with the same digit
+    for (int b = lo; b < hi; b += 64) {
+      const int q = b + lane;
+      const bool valid = q < hi;
+      const uint32_t key = valid ? kb[cur][q] : 0u;
+      const uint32_t d = (key >> tbits >> shift) & 255u;
+      const uint64_t same = same_digit_lanes(d, valid);
+      const uint32_t rank = (uint32_t)__popcll(same & lt_mask);
+      const uint32_t base = valid ? my[d] : 0u;
+      if (valid) kb[cur ^ 1][base + rank] = key;
+      // every lane of a digit group read the same base; the group's first lane advances it
+      if (valid && rank == 0) my[d] = base + (uint32_t)__popcll(same);
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  for (int t = tid; t < ntok; t += kRadixThreads) {
+    const uint32_t key = kb[cur][t];
+    const uint32_t row = key >> tbits;
+    keys_out[t] = (row >= (uint32_t)v_rows) ? kNoKey : (((uint64_t)row << 32) | (uint64_t)(key & tmask));
+  }
+}
+
 __global__ void __launch_bounds__(256) bitonic_global_kernel(uint64_t* keys, int64_t n, int64_t k, int64_t j) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= n / 2) return;
-  const int64_t i = 2 * j * (q / j) + (q % j);
+  const int64_t i = ((q & ~(j - 1)) << 1) | (q & (j - 1));   // j is a power of two
   const int64_t l = i + j;
   const bool asc = (i & k) == 0;
   const uint64_t a = keys[i], b = keys[l];
   if ((a > b) == asc) { keys[i] = b; keys[l] = a; }
 }
 
-// One wavefront per sorted position; positions that start a row's segment sum
-// that segment.  Columns are processed in slabs of 64 lanes x VEC elements.
+// One wavefront per sorted position; a position that starts a row's segment
+// owns that row.  The wave takes the segment's tokens 64 at a time (one key
+// per lane; the segment ends at the first key of another row -- kNoKey sorts
+// last and matches no row), then, for SL slabs of 64 lanes x VEC columns at a
+// time, starts from the row's current dE (the output-side gradient) and adds
+// the segment's dY rows in increasing token order in fp32.  Token indices
+// are read from the keys' lanes into scalar registers, so no load waits on
+// another; each lane keeps SL x VEC fp32 partial sums.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_bwd_accum_kernel(const uint64_t* __restrict__ keys,
-                                                               const T* __restrict__ dY, float* dE,
+                                                               const T* __restrict__ dY, float* __restrict__ dE,
                                                                int64_t ntok, int64_t H) {
   constexpr int VEC = 16 / sizeof(T);
+  constexpr int SL = 4;
   const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= ntok) return;
   const uint64_t key = keys[p];
@@ -104,34 +248,64 @@ __global__ void __launch_bounds__(256) embed_bwd_accum_kernel(const uint64_t* __
   const uint64_t row = key >> 32;
   if (p > 0 && (keys[p - 1] >> 32) == row) return;  // not the head of its segment
   const int lane = threadIdx.x & 63;
-  int64_t end = p + 1;
-  while (end < ntok && keys[end] != kNoKey && (keys[end] >> 32) == row) ++end;
   float* drow = dE + (int64_t)row * H;
-  for (int64_t c0 = 0; c0 < H; c0 += 64 * VEC) {
-    const int64_t c = c0 + lane * VEC;
-    if (c >= H) continue;
-    float acc[VEC];
+  for (int64_t b = p; b < ntok; b += 64) {
+    const int64_t q = b + lane;
+    const uint64_t kq = q < ntok ? keys[q] : kNoKey;
+    const uint64_t in_seg = __ballot(kq != kNoKey && (kq >> 32) == row);
+    // positions b .. b + n - 1 belong to the segment (a contiguous prefix)
+    const int n = in_seg == ~0ull ? 64 : (int)__builtin_ctzll(~in_seg);
+    if (n == 0) break;
+    const int tl = (int)(kq & 0xffffffffu);
+    for (int64_t c0 = (int64_t)lane * VEC; c0 < H; c0 += 64 * VEC * SL) {
+      float acc[SL][VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int64_t q = p; q < end; ++q) {
-      const int64_t t = (int64_t)(keys[q] & 0xffffffffu);
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(dY + t * H + c);
-      if constexpr (VEC == 8) {
+      for (int sl = 0; sl < SL; ++sl) {
+        const int64_t c = c0 + (int64_t)sl * 64 * VEC;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) { acc[2 * w] += bf16lo(x[w]); acc[2 * w + 1] += bf16hi(x[w]); }
-      } else {
+        for (int i = 0; i < VEC; i += 4) {
+          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+          if (c < H) d = *reinterpret_cast<const f32x4_t*>(drow + c + i);
+          acc[sl][i] = d[0]; acc[sl][i + 1] = d[1]; acc[sl][i + 2] = d[2]; acc[sl][i + 3] = d[3];
+        }
+      }
+      for (int u = 0; u < n; ++u) {
+        const int64_t t = __builtin_amdgcn_readlane(tl, u);
+        const T* src = dY + t * H;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[w] += __uint_as_float(x[w]);
+        for (int sl = 0; sl < SL; ++sl) {
+          const int64_t c = c0 + (int64_t)sl * 64 * VEC;
+          if (c < H) {
+            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + c);
+            if constexpr (VEC == 8) {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) { acc[sl][2 * w] += bf16lo(x[w]); acc[sl][2 * w + 1] += bf16hi(x[w]); }
+            } else {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) acc[sl][w] += __uint_as_float(x[w]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) {
+        const int64_t c = c0 + (int64_t)sl * 64 * VEC;
+        if (c < H) {
+#pragma unroll
+          for (int i = 0; i < VEC; i += 4)
+            *reinterpret_cast<f32x4_t*>(drow + c + i) =
+                f32x4_t{acc[sl][i], acc[sl][i + 1], acc[sl][i + 2], acc[sl][i + 3]};
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < VEC; i += 4) {
-      f32x4_t* d = reinterpret_cast<f32x4_t*>(drow + c + i);
-      f32x4_t o = *d;
-      o[0] += acc[i]; o[1] += acc[i + 1]; o[2] += acc[i + 2]; o[3] += acc[i + 3];
-      *d = o;
-    }
+    if (n < 64) break;
   }
+}
+
+static int ceil_log2(int64_t x) {   // smallest b with 2^b >= x (x >= 1)
+  int b = 0;
+  while ((int64_t{1} << b) < x) ++b;
+  return b;
 }
 
 static int64_t next_pow2(int64_t x) {
@@ -207,12 +381,19 @@ extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_
     return set_error(TPS_EWORKSPACE, "vocab_embed_bwd: workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint64_t* keys = static_cast<uint64_t*>(ws);
-  const int64_t npad = next_pow2(T);
-  hipLaunchKernelGGL(embed_keys_kernel, dim3((unsigned)ceil_div(npad, 256)), dim3(256), 0, st, ids, keys, T, npad,
-                     v_start, v_rows);
-  s = check_launch("embed_keys_kernel");
-  if (s != TPS_OK) return s;
-  s = sort_keys(keys, npad, st);
+  const int tbits = ceil_log2(T), rbits = ceil_log2(v_rows + 1);
+  if (T <= kRadixMax && tbits + rbits <= 32) {
+    hipLaunchKernelGGL(embed_radix_sort_kernel, dim3(1), dim3(kRadixThreads), 0, st, ids, keys, (int)T, v_start,
+                       (int)v_rows, tbits, rbits);
+    s = check_launch("embed_radix_sort_kernel");
+  } else {
+    const int64_t npad = next_pow2(T);
+    hipLaunchKernelGGL(embed_keys_kernel, dim3((unsigned)ceil_div(npad, 256)), dim3(256), 0, st, ids, keys, T,
+                       npad, v_start, v_rows);
+    s = check_launch("embed_keys_kernel");
+    if (s != TPS_OK) return s;
+    s = sort_keys(keys, npad, st);
+  }
   if (s != TPS_OK) return s;
   const dim3 grid((unsigned)ceil_div(T, 4));
   if (dt == TPS_BF16)
