@@ -41,15 +41,36 @@ struct EpiScore {
   }
 };
 
-// Causal zero padding of P: a row i is written up to this column so that
-// the O = P V GEMM (row tiles of at most 256, K-loop ending at the tile's
-// last row) only ever reads written values.
+// Rows of S2, P, dP and dS are ldp elements apart with ldp a multiple of 8,
+// so every 8-element chunk that starts inside a row lies inside it: the row
+// passes below always move whole 16- or 32-byte vectors and mask columns
+// past the row's limit arithmetically (values beyond it are never used).
+__device__ __forceinline__ void ld_f32x8(const float* p, float v[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3]; v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+__device__ __forceinline__ void ld_bf16x8(const bf16_t* p, float v[8]) {
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) { v[2 * w] = bf16lo(x[w]); v[2 * w + 1] = bf16hi(x[w]); }
+}
+__device__ __forceinline__ void st_bf16x8(bf16_t* p, const float v[8]) {
+  *reinterpret_cast<u32x4_t*>(p) =
+      u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
+
+// Causal zero padding of P and dS: a row i is written up to this column so
+// that the GEMMs that read them (row tiles of at most 256; K-loops ending at
+// the tile's last row, or starting at its first) only ever read written
+// values.
 constexpr int kProbPad = 256;
+constexpr int kRowUnroll = 4;   // 8-element chunks in flight per lane
 
 // One wavefront per row of one (batch, head): online max / sum of exp2 over
-// the row's unmasked scores (8 per lane per step, merged across lanes), then
-// P = exp2(S2 - max) / sum in bf16 for the unmasked columns and zeros up to
-// the padding limit; lse = (max + log2(sum)) * ln 2.
+// the row's unmasked scores (8 per lane per chunk, merged across lanes),
+// then P = exp2(S2 - max) / sum in bf16 for the unmasked columns and zeros
+// up to the padding limit; lse = (max + log2(sum)) * ln 2.
 __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restrict__ S2, bf16_t* __restrict__ P,
                                                            float* __restrict__ lse, int64_t rows, int sq,
                                                            int64_t ldp, int causal) {
@@ -58,23 +79,32 @@ __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int i = (int)(w % sq);
   const int ncol = causal ? i + 1 : sq;
-  const int64_t zend = causal ? min(ldp, (int64_t)((i + kProbPad) / kProbPad) * kProbPad) : ldp;
+  const int zend = causal ? (int)min(ldp, (int64_t)((i + kProbPad) / kProbPad) * kProbPad) : (int)ldp;
   const float* sr = S2 + w * ldp;
   bf16_t* pr = P + w * ldp;
   float mx = -INFINITY, sum = 0.f;
-  for (int c = lane * 8; c < ncol; c += 64 * 8) {
-    float x[8];
-    const int nv = min(8, ncol - c);
-    load8<float>(sr + c, x, nv);
-    float bm = -INFINITY;
+  for (int c0 = lane * 8; c0 < ncol; c0 += 64 * 8 * kRowUnroll) {
+    float x[kRowUnroll][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bm = fmaxf(bm, e < nv ? x[e] : -INFINITY);
-    const float nm = fmaxf(mx, bm);
-    float bs = 0.f;
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < ncol) ld_f32x8(sr + c, x[u]);
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bs += e < nv ? exp2f(x[e] - nm) : 0.f;
-    sum = sum * exp2f(mx - nm) + bs;   // exp2(-inf) = 0 on the first step
-    mx = nm;
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < ncol) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bm = fmaxf(bm, c + e < ncol ? x[u][e] : -INFINITY);
+        const float nm = fmaxf(mx, bm);
+        float bs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bs += c + e < ncol ? exp2f(x[u][e] - nm) : 0.f;
+        sum = sum * exp2f(mx - nm) + bs;   // exp2(-inf) = 0 on the first chunk
+        mx = nm;
+      }
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -84,14 +114,27 @@ __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restri
     mx = nm;
   }
   const float inv = 1.f / sum;
-  for (int64_t c = lane * 8; c < zend; c += 64 * 8) {
-    const int nv = (int)min((int64_t)8, zend - c);
-    float x[8];
-    load8<float>(sr + c, x, (int)max(0, min(nv, ncol - (int)c)));
-    float p[8];
+  for (int c0 = lane * 8; c0 < zend; c0 += 64 * 8 * kRowUnroll) {
+    float x[kRowUnroll][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = (c + e < ncol) ? exp2f(x[e] - mx) * inv : 0.f;
-    store8<bf16_t>(pr + c, p, nv);
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < ncol) ld_f32x8(sr + c, x[u]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < zend) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = (c + e < ncol) ? exp2f(x[u][e] - mx) * inv : 0.f;
+        st_bf16x8(pr + c, p);
+      }
+    }
   }
   if (lane == 0) lse[w] = (mx + log2f(sum)) * 0.69314718055994531f;
 }
@@ -101,7 +144,8 @@ __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restri
 // dS_j = P_j (dP_j - delta) * scale.  Taking delta from the same P and dP
 // makes every row of dS sum to zero (the softmax gradient of the stored P),
 // so the rounding of O and dO does not leak into dQ as a per-row bias.
-// Columns at or beyond the causal limit (and beyond sq) are written as 0.
+// Columns at or beyond the causal limit are written as 0 up to the padding
+// limit (the whole row without the causal mask).
 __global__ void __launch_bounds__(256) attn_ds_kernel(const bf16_t* __restrict__ P, const float* __restrict__ dP,
                                                       bf16_t* __restrict__ dS, int64_t rows, int sq, int64_t ldp,
                                                       int causal, float scale) {
@@ -110,28 +154,52 @@ __global__ void __launch_bounds__(256) attn_ds_kernel(const bf16_t* __restrict__
   const int lane = threadIdx.x & 63;
   const int i = (int)(w % sq);                    // query index within its head
   const int ncol = causal ? i + 1 : sq;
+  const int zend = causal ? (int)min(ldp, (int64_t)((i + kProbPad) / kProbPad) * kProbPad) : (int)ldp;
   const bf16_t* pr = P + w * ldp;
   const float* dpr = dP + w * ldp;
   bf16_t* dsr = dS + w * ldp;
   float num = 0.f, den = 0.f;
-  for (int c = lane * 8; c < ncol; c += 64 * 8) {
-    float p[8], d[8];
-    load8<bf16_t>(pr + c, p, min(8, ncol - c));
-    load8<float>(dpr + c, d, min(8, ncol - c));
+  for (int c0 = lane * 8; c0 < ncol; c0 += 64 * 8 * kRowUnroll) {
+    float p[kRowUnroll][8], d[kRowUnroll][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { num += p[e] * d[e]; den += p[e]; }
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < ncol) { ld_bf16x8(pr + c, p[u]); ld_f32x8(dpr + c, d[u]); }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < ncol) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c + e < ncol) { num += p[u][e] * d[u][e]; den += p[u][e]; }
+      }
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) { num += __shfl_xor(num, o); den += __shfl_xor(den, o); }
   const float delta = den > 0.f ? num / den : 0.f;
-  for (int c = lane * 8; c < sq; c += 64 * 8) {
-    const int nv = min(8, sq - c);
-    float p[8], d[8], o[8];
-    load8<bf16_t>(pr + c, p, nv);
-    load8<float>(dpr + c, d, nv);
+  for (int c0 = lane * 8; c0 < zend; c0 += 64 * 8 * kRowUnroll) {
+    float p[kRowUnroll][8], d[kRowUnroll][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (c + e < ncol) ? p[e] * (d[e] - delta) * scale : 0.f;
-    store8<bf16_t>(dsr + c, o, nv);
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < ncol) { ld_bf16x8(pr + c, p[u]); ld_f32x8(dpr + c, d[u]); }
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { p[u][e] = 0.f; d[u][e] = 0.f; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + u * 64 * 8;
+      if (c < zend) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (c + e < ncol) ? p[u][e] * (d[u][e] - delta) * scale : 0.f;
+        st_bf16x8(dsr + c, o);
+      }
+    }
   }
 }
 

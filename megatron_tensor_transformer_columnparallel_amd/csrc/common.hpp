@@ -62,7 +62,9 @@ __device__ __forceinline__ void store4<float>(float* p, const float v[4], int nv
     f32x4_t x = {v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4_t*>(p) = x;
   } else {
-    for (int i = 0; i < nvalid; ++i) p[i] = v[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < nvalid) p[i] = v[i];
   }
 }
 template <>
@@ -71,7 +73,9 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float v[4], int 
     u32x2_t x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     *reinterpret_cast<u32x2_t*>(p) = x;
   } else {
-    for (int i = 0; i < nvalid; ++i) p[i] = f32_to_bf16(v[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < nvalid) p[i] = f32_to_bf16(v[i]);
   }
 }
 
@@ -84,6 +88,7 @@ __device__ __forceinline__ void load4<float>(const float* p, float v[4], int nva
     f32x4_t x = *reinterpret_cast<const f32x4_t*>(p);
     v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
   } else {
+#pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = i < nvalid ? p[i] : 0.f;
   }
 }
@@ -93,6 +98,7 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float v[4], int n
     u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
     v[0] = bf16lo(x[0]); v[1] = bf16hi(x[0]); v[2] = bf16lo(x[1]); v[3] = bf16hi(x[1]);
   } else {
+#pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = i < nvalid ? bf16_to_f32(p[i]) : 0.f;
   }
 }
@@ -127,7 +133,9 @@ __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float v[8], int 
                  pack_bf16x2(v[6], v[7])};
     *reinterpret_cast<u32x4_t*>(p) = x;
   } else {
-    for (int i = 0; i < nvalid; ++i) p[i] = f32_to_bf16(v[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nvalid) p[i] = f32_to_bf16(v[i]);
   }
 }
 template <>
@@ -137,6 +145,7 @@ __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8], int n
 #pragma unroll
     for (int w = 0; w < 4; ++w) { v[2 * w] = bf16lo(x[w]); v[2 * w + 1] = bf16hi(x[w]); }
   } else {
+#pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = i < nvalid ? bf16_to_f32(p[i]) : 0.f;
   }
 }

@@ -579,16 +579,16 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
 
 // Tile shape by problem size, from cold-cache timings of these kernels on
 // MI355X: 256x256 (one 8-wave workgroup per CU) whenever it yields at least
-// 192 tiles; otherwise 128x128 (4 waves, two workgroups per CU), which beat
-// 256x256 and 128x256 on every M = 2048, N <= 4096 shape of the layer; 64x64
-// for problems too small for 64 tiles of 128x128.
+// 192 tiles; otherwise 128x128 with 8 waves of 64x32, which beat 256x256,
+// 256x128, 128x256 and the 4-wave 128x128 on every M = 2048, N <= 4096 shape
+// of the layer; 64x64 for problems too small for 64 tiles of 128x128.
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             hipStream_t st) {
   const int64_t big = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
   const int64_t mid = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
   if (big >= 192) return launch_mfma<256, 256, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
-  if (mid >= 64) return launch_mfma<128, 128, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
+  if (mid >= 64) return launch_mfma<128, 128, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
   return launch_mfma<64, 64, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
 }
 
