@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * 64;
-      if (c < nch) dst[c] = v[u];
+      if (c < nch) __builtin_nontemporal_store(v[u], dst + c);
     }
   }
 }

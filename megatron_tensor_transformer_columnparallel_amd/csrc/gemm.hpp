@@ -174,6 +174,9 @@ __device__ __forceinline__ int mn_swizzle(int k) {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -325,11 +328,12 @@ struct FragReader {
 
 // One workgroup computes a BM x BN tile with WM x WN waves, each wave a
 // (BM/WM) x (BN/WN) block of 16x16 MFMA tiles.  K advances in tiles of BK
-// through two LDS stages.  Interior tiles (the whole BM x BN block inside
-// the matrix) load the next K tile from global memory straight into LDS
-// while the MFMAs consume the current one; edge tiles go through
-// bounds-checked register loads.  The epilogue runs from the accumulators.
-template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKC, class Epi>
+// through NS LDS stages.  Interior tiles (the whole BM x BN block inside
+// the matrix) keep NS-1 K tiles in flight from global memory straight into
+// LDS while the MFMAs consume the current one; edge tiles go through
+// bounds-checked register loads (two of the stages).  The epilogue runs
+// from the accumulators.
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool AK, bool BKC, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64, 1)
 gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, GemmShape s, Epi epi) {
   constexpr int NT = WM * WN * 64;
@@ -337,8 +341,9 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   constexpr int FM = WTM / 16, FN = WTN / 16;
   constexpr int KS = BK / 32;
   constexpr int STAGE = (BM + BN) * BK;                 // bf16 elements per LDS stage
-  constexpr int LDS_BYTES = 2 * 2 * STAGE;             // two stages
+  constexpr int LDS_BYTES = NS * 2 * STAGE;
   static_assert(BK == 32 || BK == 64, "loaders and swizzles support BK = 32 or 64");
+  static_assert(NS >= 2, "at least two stages");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_BYTES / 2];
@@ -415,8 +420,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
       }
     }
   };
-  auto issue = [&](int kt) {
-    bf16_t* st = lds + (kt & 1) * STAGE;
+  auto issue = [&](int /*kt*/, int stage) {   // K tiles are issued in order
+    bf16_t* st = lds + stage * STAGE;
     la.issue_direct(st, wave);
     lb.issue_direct(st + BM * BK, wave);
   };
@@ -431,23 +436,29 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   };
 
   if (mn_inside) {
-    // Interior tile: every full K tile goes global -> LDS directly; the DMA
-    // of tile kt+1 is in flight while tile kt's fragments are read and
-    // multiplied.  No other vector-memory operation is issued in this loop,
-    // so the vmcnt wait covers exactly that DMA.
-    if (nkd > 0) {
-      issue(0);
-      wait_vmem();
-      __syncthreads();
-    }
+    // Interior tile: every full K tile goes global -> LDS directly, NS-1 of
+    // them in flight while tile kt's fragments are read and multiplied.  No
+    // other vector-memory operation is issued in this loop, so the vmcnt
+    // count is exactly the DMA instructions of the tiles after kt.
+    constexpr int VPT = LoaderA::VECS + LoaderB::VECS;   // DMA instructions per wave per K tile
+    const int pre = min(NS - 1, nkd);
+    for (int p = 0; p < pre; ++p) issue(p, p);
+    int cs = 0, is = pre % NS;   // stage of tile kt; stage of the next tile to issue
     for (int kt = 0; kt < nkd; ++kt) {
-      if (kt + 1 < nkd) issue(kt + 1);
-      compute(lds + (kt & 1) * STAGE);
-      wait_vmem();
-      __syncthreads();   // tile kt+1 visible; tile kt's stage consumed by every wave
+      if (kt + NS - 1 <= nkd) wait_vmem_n<(NS - 2) * VPT>();   // NS-2 later tiles may stay in flight
+      else wait_vmem();
+      __syncthreads();   // tile kt visible; every wave is past tile kt-1, whose stage is reused next
+      if (kt + NS - 1 < nkd) {
+        issue(kt + NS - 1, is);
+        is = (is + 1 == NS) ? 0 : is + 1;
+      }
+      compute(lds + cs * STAGE);
+      cs = (cs + 1 == NS) ? 0 : cs + 1;
     }
     if (nk > nkd) {
-      bf16_t* st = lds + (nkd & 1) * STAGE;
+      // the stage after the last direct tile: its last reader finished before
+      // the final loop barrier, and every DMA has been waited for
+      bf16_t* st = lds + (nkd % NS) * STAGE;
       load_checked(nkd);
       store_regs(st);
       __syncthreads();
@@ -562,7 +573,7 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B, GemmSh
 
 // ------------------------------------------------------------------ dispatch
 
-template <int BM, int BN, int BK, int WM, int WN, bool AK, bool BKC, class Epi>
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool AK, bool BKC, class Epi>
 inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                               hipStream_t st) {
   const int64_t tiles = ceil_div(s.M, BM) * ceil_div(s.N, BN) * (int64_t)s.batch;
@@ -572,24 +583,29 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
   const int64_t span_a = (AK ? BM : BK) * s.lda * 2, span_b = (BKC ? BN : BK) * s.ldb * 2;
   if (span_a >= (1LL << 32) || span_b >= (1LL << 32))
     return set_error(TPS_EINVAL, "gemm: leading dimension too large for 32-bit tile offsets");
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, AK, BKC, Epi>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, NS, AK, BKC, Epi>), dim3((unsigned)tiles),
                      dim3(WM * WN * 64), 0, st, A, B, s, epi);
   return check_launch("gemm_bf16_kernel");
 }
 
 // Tile shape by problem size, from cold-cache timings of these kernels on
-// MI355X: 256x256 (one 8-wave workgroup per CU) whenever it yields at least
-// 192 tiles; otherwise 128x128 with 8 waves of 64x32, which beat 256x256,
-// 256x128, 128x256 and the 4-wave 128x128 on every M = 2048, N <= 4096 shape
-// of the layer; 64x64 for problems too small for 64 tiles of 128x128.
+// MI355X: 256x256 (one 8-wave workgroup per CU, two stages) whenever it
+// yields at least 192 tiles; otherwise 128x128 with 8 waves of 64x32, which
+// beat 256x256, 256x128, 128x256 and the 4-wave 128x128 on every M = 2048,
+// N <= 4096 shape of the layer; 64x64 for problems too small for 64 tiles
+// of 128x128.  A 128x128 grid of at most 256 tiles (one per CU) is bound by
+// the DMA latency of a single K tile in flight and takes three stages
+// (2048x2048x4096: 62 -> 47 us); larger grids keep two stages (64 KB), so
+// that two workgroups share a CU and cover each other's waits.
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             hipStream_t st) {
   const int64_t big = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
   const int64_t mid = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
-  if (big >= 192) return launch_mfma<256, 256, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
-  if (mid >= 64) return launch_mfma<128, 128, 64, 2, 4, AK, BKC>(A, B, s, epi, st);
-  return launch_mfma<64, 64, 64, 2, 2, AK, BKC>(A, B, s, epi, st);
+  if (big >= 192) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
+  if (mid > 256) return launch_mfma<128, 128, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
+  if (mid >= 64) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);
+  return launch_mfma<64, 64, 64, 2, 2, 2, AK, BKC>(A, B, s, epi, st);
 }
 
 template <bool AK, bool BKC, class Epi>
