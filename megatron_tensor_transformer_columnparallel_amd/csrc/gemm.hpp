@@ -589,22 +589,30 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
 }
 
 // Tile shape by problem size, from cold-cache timings of these kernels on
-// MI355X: 256x256 (one 8-wave workgroup per CU, two stages) whenever it
-// yields at least 192 tiles; otherwise 128x128 with 8 waves of 64x32, which
-// beat 256x256, 256x128, 128x256 and the 4-wave 128x128 on every M = 2048,
-// N <= 4096 shape of the layer; 64x64 for problems too small for 64 tiles
-// of 128x128.  A 128x128 grid of at most 256 tiles (one per CU) is bound by
-// the DMA latency of a single K tile in flight and takes three stages
-// (2048x2048x4096: 62 -> 47 us); larger grids keep two stages (64 KB), so
-// that two workgroups share a CU and cover each other's waits.
+// MI355X (M = 2048 and the layer's N, K):
+//   256x256, 8 waves, two stages, when it yields at least 192 tiles, unless
+//     the grid would end with a partly filled second round (257..511 tiles
+//     that are not a multiple of 256: 4096x6144x2048 TN takes 132 us at
+//     256x256, 120 us at 128x128);
+//   128x256, 8 waves of 64x64, three stages, when that fills one round of
+//     192..256 tiles (2048x4096x8192 NN: 151 -> 135 us against 128x128;
+//     2048x4096x6144 NT: 116 -> 108 us);
+//   128x128, 8 waves of 64x32: two stages (64 KB, so two workgroups share a
+//     CU and cover each other's waits) above 256 tiles, three stages at most
+//     256 tiles, where one K tile in flight leaves the DMA latency exposed
+//     (2048x2048x4096: 62 -> 47 us);
+//   64x64 for problems too small for 64 tiles of 128x128.
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             hipStream_t st) {
-  const int64_t big = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
-  const int64_t mid = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
-  if (big >= 192) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
-  if (mid > 256) return launch_mfma<128, 128, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
-  if (mid >= 64) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);
+  const int64_t t256 = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
+  const int64_t t128x256 = ceil_div(s.M, 128) * ceil_div(s.N, 256) * (int64_t)s.batch;
+  const int64_t t128 = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
+  const bool partial_round = t256 > 256 && t256 < 512 && t256 % 256 != 0;
+  if (t256 >= 192 && !partial_round) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
+  if (t128x256 >= 192 && t128x256 <= 256) return launch_mfma<128, 256, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);
+  if (t128 > 256) return launch_mfma<128, 128, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
+  if (t128 >= 64) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);
   return launch_mfma<64, 64, 64, 2, 2, 2, AK, BKC>(A, B, s, epi, st);
 }
 
