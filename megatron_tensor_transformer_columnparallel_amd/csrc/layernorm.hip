@@ -1,9 +1,10 @@
 // LayerNorm forward/backward (replicated on every shard; used between the
 // attention and MLP sublayers of a stacked model).  One workgroup per row in
 // the forward pass with the row held in registers (H <= 8192); the backward
-// pass gives each workgroup 8 rows and writes per-workgroup partial column
-// sums of dgamma/dbeta to the workspace, which a second kernel reduces in a
-// fixed order (deterministic, no atomics).
+// pass gives each workgroup 8 rows (prefetching one row ahead when H is 4096)
+// and writes per-workgroup partial column sums of dgamma/dbeta to
+// the workspace, which a second kernel reduces in a fixed order
+// (deterministic, no atomics).
 #include <string>
 
 #include "common.hpp"
@@ -162,38 +163,149 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
   }
 }
 
-// dgamma/dbeta[c] = sum over row blocks k of the partials, in a fixed order.
-// A workgroup owns 64 columns (16 groups of 4) and splits the blocks into 16
-// contiguous slices, one per thread of a column group; the slice sums are then
-// added in slice order through LDS.  Deterministic, no atomics.
+// Backward for H = NCH * 4096 (launched for H = 4096, the layer width; with
+// NCH = 2 the two row buffers no longer fit in registers): 512 threads,
+// every thread owns NCH full chunks, so no load or store is conditional and
+// the compiler counts them exactly.  The loads of row r+1 are issued before row r is
+// processed, into the other of two register buffers, so they stay in flight
+// across row r's barrier and stores: the barrier waits only for LDS
+// operations, and the wait before row r+1 counts only row r+1's loads.  The two row sums
+// travel together through a double-buffered LDS exchange: one barrier per
+// row.  Same partial-sum layout as ln_bwd_kernel.
+constexpr int kLnBwdThreads = 512;
+
+template <int NCH, typename TX, typename TDY, typename TDX>
+__global__ void __launch_bounds__(kLnBwdThreads) ln_bwd_rows_kernel(const TX* __restrict__ x,
+                                                                    const float* __restrict__ gamma,
+                                                                    const float* __restrict__ mean,
+                                                                    const float* __restrict__ rstd,
+                                                                    const TDY* __restrict__ dy, TDX* __restrict__ dx,
+                                                                    float* __restrict__ part, int64_t M) {
+  constexpr int V = kLnV;
+  constexpr int NW = kLnBwdThreads / 64;
+  constexpr int64_t H = (int64_t)NCH * kLnBwdThreads * V;
+  __shared__ float red[2][NW][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float pg[NCH][V], pb[NCH][V], gm[NCH][V];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = ((int64_t)i * kLnBwdThreads + threadIdx.x) * V;
+    LnVec<float>::load(gamma + c, gm[i]);
+#pragma unroll
+    for (int e = 0; e < V; ++e) { pg[i][e] = 0.f; pb[i][e] = 0.f; }
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * kLnRowsPerBlock;
+  const int nr = (int)min((int64_t)kLnRowsPerBlock, M - r0);
+  auto load_row = [&](int64_t row, float (&xv)[NCH][V], float (&dv)[NCH][V]) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = ((int64_t)i * kLnBwdThreads + threadIdx.x) * V;
+      LnVec<TX>::load(x + row * H + c, xv[i]);
+      LnVec<TDY>::load(dy + row * H + c, dv[i]);
+    }
+  };
+  // One row: sums, the shared row means, dx, and the dgamma/dbeta partials.
+  auto row_pass = [&](int rr, const float (&xv)[NCH][V], const float (&dv)[NCH][V]) {
+    const int64_t row = r0 + rr;
+    const float mu = mean[row], rs = rstd[row];
+    float xh[NCH][V], gv[NCH][V];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        xh[i][e] = (xv[i][e] - mu) * rs;
+        gv[i][e] = dv[i][e] * gm[i][e];
+        s1 += gv[i][e];
+        s2 += gv[i][e] * xh[i][e];
+        pg[i][e] += dv[i][e] * xh[i][e];
+        pb[i][e] += dv[i][e];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      s1 += __shfl_xor(s1, o);
+      s2 += __shfl_xor(s2, o);
+    }
+    // buffer rr & 1 was last read in row rr-2, before every wave reached
+    // row rr-1's barrier
+    if (lane == 0) { red[rr & 1][wave][0] = s1; red[rr & 1][wave][1] = s2; }
+    __syncthreads();
+    float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { t1 += red[rr & 1][w][0]; t2 += red[rr & 1][w][1]; }
+    const float m1 = t1 / (float)H, m2 = t2 / (float)H;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t c = ((int64_t)i * kLnBwdThreads + threadIdx.x) * V;
+      float o[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = rs * (gv[i][e] - m1 - xh[i][e] * m2);
+      LnVec<TDX>::store(dx + row * H + c, o);
+    }
+  };
+  if (nr == kLnRowsPerBlock) {
+    // full block: unrolled, rows alternate between two register buffers
+    float xs[2][NCH][V], ds[2][NCH][V];
+    load_row(r0, xs[0], ds[0]);
+#pragma unroll
+    for (int rr = 0; rr < kLnRowsPerBlock; ++rr) {
+      if (rr + 1 < kLnRowsPerBlock) load_row(r0 + rr + 1, xs[(rr + 1) & 1], ds[(rr + 1) & 1]);
+      row_pass(rr, xs[rr & 1], ds[rr & 1]);
+    }
+  } else {
+    // last, partial block: one buffer plus a copy per row
+    float xa[NCH][V], da[NCH][V];
+    load_row(r0, xa, da);
+    for (int rr = 0; rr < nr; ++rr) {
+      float xb[NCH][V], db[NCH][V];
+      load_row(rr + 1 < nr ? r0 + rr + 1 : r0 + rr, xb, db);
+      row_pass(rr, xa, da);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int e = 0; e < V; ++e) { xa[i][e] = xb[i][e]; da[i][e] = db[i][e]; }
+    }
+  }
+  float* pr = part + (int64_t)blockIdx.x * 2 * H;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t c = ((int64_t)i * kLnBwdThreads + threadIdx.x) * V;
+    LnVec<float>::store(pr + c, pg[i]);
+    LnVec<float>::store(pr + H + c, pb[i]);
+  }
+}
+
+// [dgamma | dbeta][j] = sum over row blocks k of part[k][j], j < 2H, in a
+// fixed order.  A workgroup owns 8 quads of columns and splits the blocks
+// into 32 contiguous slices, one per thread of a quad; the slice sums are
+// then added in slice order through LDS.  Deterministic, no atomics.
 __global__ void __launch_bounds__(256) ln_param_reduce_kernel(const float* __restrict__ part, float* __restrict__ dgamma,
                                                               float* __restrict__ dbeta, int64_t nblk, int64_t H) {
-  constexpr int COLS = 64, SLICES = 256 / (COLS / 4);   // 16 threads per 4 columns -> 16 slices
-  __shared__ f32x4_t red_g[SLICES][COLS / 4], red_b[SLICES][COLS / 4];
-  const int cg = threadIdx.x % (COLS / 4), sl = threadIdx.x / (COLS / 4);
-  const int64_t c = (int64_t)blockIdx.x * COLS + cg * 4;   // H is a multiple of 8
-  f32x4_t g = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-  if (c < H) {
+  constexpr int CQ = 8, SLICES = 256 / CQ;
+  __shared__ f32x4_t red[SLICES][CQ];
+  const int cq = threadIdx.x % CQ, sl = threadIdx.x / CQ;
+  const int64_t W = 2 * H;
+  const int64_t j = ((int64_t)blockIdx.x * CQ + cq) * 4;   // H is a multiple of 8: a quad never straddles H
+  f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+  if (j < W) {
     const int64_t per = (nblk + SLICES - 1) / SLICES;
     const int64_t k0 = sl * per, k1 = min(nblk, k0 + per);
     for (int64_t k = k0; k < k1; ++k) {
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(part + k * 2 * H + c);
-      const f32x4_t y = *reinterpret_cast<const f32x4_t*>(part + k * 2 * H + H + c);
-      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
-      b[0] += y[0]; b[1] += y[1]; b[2] += y[2]; b[3] += y[3];
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(part + k * W + j);
+      a[0] += x[0]; a[1] += x[1]; a[2] += x[2]; a[3] += x[3];
     }
   }
-  red_g[sl][cg] = g;
-  red_b[sl][cg] = b;
+  red[sl][cq] = a;
   __syncthreads();
-  if (sl == 0 && c < H) {
+  if (sl == 0 && j < W) {
+#pragma unroll 8
     for (int k = 1; k < SLICES; ++k) {
-      const f32x4_t x = red_g[k][cg], y = red_b[k][cg];
-      g[0] += x[0]; g[1] += x[1]; g[2] += x[2]; g[3] += x[3];
-      b[0] += y[0]; b[1] += y[1]; b[2] += y[2]; b[3] += y[3];
+      const f32x4_t x = red[k][cq];
+      a[0] += x[0]; a[1] += x[1]; a[2] += x[2]; a[3] += x[3];
     }
-    *reinterpret_cast<f32x4_t*>(dgamma + c) = g;
-    *reinterpret_cast<f32x4_t*>(dbeta + c) = b;
+    float* dst = j < H ? dgamma + j : dbeta + (j - H);
+    *reinterpret_cast<f32x4_t*>(dst) = a;
   }
 }
 
@@ -221,9 +333,17 @@ static void launch_ln_fwd(int64_t M, int64_t H, float eps, const void* x, const 
 template <typename TX, typename TDY, typename TDX>
 static void launch_ln_bwd(int64_t M, int64_t H, const void* x, const float* g, const float* mean, const float* rstd,
                           const void* dy, void* dx, float* part, hipStream_t st) {
-  hipLaunchKernelGGL((ln_bwd_kernel<TX, TDY, TDX>), dim3((unsigned)ceil_div(M, kLnRowsPerBlock)), dim3(256), 0, st,
-                     static_cast<const TX*>(x), g, mean, rstd, static_cast<const TDY*>(dy), static_cast<TDX*>(dx),
-                     part, M, H);
+  const dim3 grid((unsigned)ceil_div(M, kLnRowsPerBlock));
+  const TX* xp = static_cast<const TX*>(x);
+  const TDY* dyp = static_cast<const TDY*>(dy);
+  TDX* dxp = static_cast<TDX*>(dx);
+  constexpr int64_t W1 = (int64_t)kLnBwdThreads * kLnV;   // 4096
+  if (H == W1)
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<1, TX, TDY, TDX>), grid, dim3(kLnBwdThreads), 0, st, xp, g, mean, rstd,
+                       dyp, dxp, part, M);
+  else
+    hipLaunchKernelGGL((ln_bwd_kernel<TX, TDY, TDX>), grid, dim3(256), 0, st, xp, g, mean, rstd, dyp, dxp, part, M,
+                       H);
 }
 
 }  // namespace tps
@@ -273,7 +393,7 @@ extern "C" tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype d
   s = check_launch("ln_bwd_kernel");
   if (s != TPS_OK) return s;
   const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
-  hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(H, 64)), dim3(256), 0, st, part, dgamma, dbeta,
-                     nblk, H);
+  hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(2 * H, 32)), dim3(256), 0, st, part, dgamma,
+                     dbeta, nblk, H);
   return check_launch("ln_param_reduce_kernel");
 }

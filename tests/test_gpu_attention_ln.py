@@ -93,7 +93,8 @@ def test_attention_backward_deterministic(tp):
 # ------------------------------------------------------------------ LayerNorm
 
 @pytest.mark.parametrize("M,H,dt,ydt", [(5, 64, "f32", "f32"), (300, 4096, "bf16", "bf16"), (33, 8192, "f32", "f32"),
-                                        (17, 136, "bf16", "bf16"), (64, 4096, "f32", "bf16"), (9, 72, "bf16", "f32")])
+                                        (17, 136, "bf16", "bf16"), (64, 4096, "f32", "bf16"), (9, 72, "bf16", "f32"),
+                                        (2048, 4096, "f32", "f32"), (13, 4096, "f32", "f32"), (3, 4096, "bf16", "f32")])
 def test_layernorm_matches_oracle(tp, M, H, dt, ydt):
     """x and dx of dtype dt, y and dy of dtype ydt (fp32 residual stream <-> bf16 sublayer)."""
     say(f"layernorm fwd+bwd M={M} H={H} x {dt} y {ydt}")
