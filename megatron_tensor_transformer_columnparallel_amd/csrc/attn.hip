@@ -70,7 +70,8 @@ constexpr int kRowUnroll = 4;   // 8-element chunks in flight per lane
 // One wavefront per row of one (batch, head): online max / sum of exp2 over
 // the row's unmasked scores (8 per lane per chunk, merged across lanes),
 // then P = exp2(S2 - max) / sum in bf16 for the unmasked columns and zeros
-// up to the padding limit; lse = (max + log2(sum)) * ln 2.
+// up to the padding limit; lse = (max + log2(sum)) * ln 2.  Rows of at most
+// 64 x 8 x kRowUnroll written columns take one pass (S read once).
 __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restrict__ S2, bf16_t* __restrict__ P,
                                                            float* __restrict__ lse, int64_t rows, int sq,
                                                            int64_t ldp, int causal) {
@@ -83,6 +84,47 @@ __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restri
   const float* sr = S2 + w * ldp;
   bf16_t* pr = P + w * ldp;
   float mx = -INFINITY, sum = 0.f;
+  if (zend <= 64 * 8 * kRowUnroll) {
+    // the whole row is one pass of kRowUnroll chunks per lane: S is read
+    // once; row max, then exp2 once per score, row sum, scaled store
+    float x[kRowUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = lane * 8 + u * 64 * 8;
+      if (c < ncol) ld_f32x8(sr + c, x[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e >= ncol) x[u][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[u][e]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[u][e] = exp2f(x[u][e] - mx);   // masked: exp2(-inf) = 0
+        sum += x[u][e];
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = lane * 8 + u * 64 * 8;
+      if (c < zend) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = x[u][e] * inv;
+        st_bf16x8(pr + c, p);
+      }
+    }
+    if (lane == 0) lse[w] = (mx + log2f(sum)) * 0.69314718055994531f;
+    return;
+  }
   for (int c0 = lane * 8; c0 < ncol; c0 += 64 * 8 * kRowUnroll) {
     float x[kRowUnroll][8];
 #pragma unroll
@@ -145,7 +187,8 @@ __global__ void __launch_bounds__(256) attn_softmax_kernel(const float* __restri
 // makes every row of dS sum to zero (the softmax gradient of the stored P),
 // so the rounding of O and dO does not leak into dQ as a per-row bias.
 // Columns at or beyond the causal limit are written as 0 up to the padding
-// limit (the whole row without the causal mask).
+// limit (the whole row without the causal mask).  Rows of at most
+// 64 x 8 x kRowUnroll written columns take one pass (P and dP read once).
 __global__ void __launch_bounds__(256) attn_ds_kernel(const bf16_t* __restrict__ P, const float* __restrict__ dP,
                                                       bf16_t* __restrict__ dS, int64_t rows, int sq, int64_t ldp,
                                                       int causal, float scale) {
@@ -159,6 +202,41 @@ __global__ void __launch_bounds__(256) attn_ds_kernel(const bf16_t* __restrict__
   const float* dpr = dP + w * ldp;
   bf16_t* dsr = dS + w * ldp;
   float num = 0.f, den = 0.f;
+  if (zend <= 64 * 8 * kRowUnroll) {
+    // the whole row is one pass of kRowUnroll chunks per lane: P and dP are
+    // read once and kept in registers
+    float p[kRowUnroll][8], d[kRowUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = lane * 8 + u * 64 * 8;
+      if (c < ncol) { ld_bf16x8(pr + c, p[u]); ld_f32x8(dpr + c, d[u]); }
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { p[u][e] = 0.f; d[u][e] = 0.f; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = lane * 8 + u * 64 * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < ncol) { num += p[u][e] * d[u][e]; den += p[u][e]; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) { num += __shfl_xor(num, o); den += __shfl_xor(den, o); }
+    const float delta = den > 0.f ? num / den : 0.f;
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = lane * 8 + u * 64 * 8;
+      if (c < zend) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (c + e < ncol) ? p[u][e] * (d[u][e] - delta) * scale : 0.f;
+        st_bf16x8(dsr + c, o);
+      }
+    }
+    return;
+  }
   for (int c0 = lane * 8; c0 < ncol; c0 += 64 * 8 * kRowUnroll) {
     float p[kRowUnroll][8], d[kRowUnroll][8];
 #pragma unroll
@@ -304,6 +382,7 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   s.batch_inner = (int)hs;
   s.sa_o = sq * w3; s.sa_i = d; s.sb_o = sq * w3; s.sb_i = d;
   s.skip_upper = causal ? 1 : 0;
+  s.skip_pad = 1;   // scores are read only up to the diagonal
   TPS_TRY((gemm_bf16<true, true>(qkv, qkv + w, s, EpiScore{S2, ldp, sp, (int)hs, causal ? 1 : 0, scale_log2}, st)));
   // P = softmax rows of S (bf16), lse
   hipLaunchKernelGGL(attn_softmax_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, S2, P, lse_i,
@@ -359,6 +438,7 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   s.batch_inner = (int)hs;
   s.sa_o = sq * w3; s.sa_i = d; s.sb_o = sq * w3; s.sb_i = d;
   s.skip_upper = causal ? 1 : 0;
+  s.skip_pad = kProbPad;   // P: zeros up to the causal pad, nothing beyond
   // P = exp(Q K^T * scale - lse)           (NT)  [sq x sq] per head
   TPS_TRY((gemm_bf16<true, true>(qkv, qkv + w, s,
                                  EpiAttnProb<bf16_t>{P, lse_i, ldp, sp, (int)sq, (int)hs, causal ? 1 : 0,
@@ -367,6 +447,7 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   // dP = dO V^T (fp32)                    (NT)  [sq x sq] per head
   GemmShape s2 = s;
   s2.lda = w; s2.sa_o = sq * w; s2.sa_i = d;
+  s2.skip_pad = 1;   // dP is read only up to the diagonal
   TPS_TRY((gemm_bf16<true, true>(dO, qkv + 2 * w, s2, EpiStore<float>{dP, ldp, hs * sp, sp}, st)));
   // dS = P * (dP - delta) * scale with delta from the same P and dP
   hipLaunchKernelGGL(attn_ds_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, P, dP, dS,

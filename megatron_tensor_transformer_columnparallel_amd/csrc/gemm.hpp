@@ -31,6 +31,11 @@ struct GemmShape {
   // skip_upper: tiles whose every column n exceeds every row m get acc = 0
   // (the epilogue still runs; it is expected to mask n > m itself).
   int skip_upper = 0;
+  // With skip_upper and skip_pad > 0, a tile whose first column is at or
+  // beyond round_up(row + 1, skip_pad) for every one of its rows does nothing
+  // at all (no epilogue): an output that only has to be written up to that
+  // limit (1: the diagonal; 256: a zero pad to the next multiple of 256).
+  int skip_pad = 0;
   int group_m = 8;  // tile rows per group in the tile order (8 measured best for M = 2048)
 };
 
@@ -359,6 +364,10 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
 
+  if (s.skip_upper && s.skip_pad > 0) {
+    const int mend = min(m0 + BM, s.M);
+    if (n0 >= (mend + s.skip_pad - 1) / s.skip_pad * s.skip_pad) return;   // uniform: the whole workgroup leaves
+  }
   int kb, ke;
   k_range(s, m0, BM, BK, kb, ke);
   if (s.skip_upper && n0 > m0 + BM - 1) ke = kb;
