@@ -150,14 +150,42 @@ __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8], int n
   }
 }
 
-// GELU with the exact erf form and its derivative (fp32).
+// GELU with the erf form and its derivative (fp32): gelu(x) = x Phi(x) and
+// gelu'(x) = Phi(x) + x phi(x), with Phi the standard normal CDF and phi its
+// density.  Phi comes from the complementary error function,
+// Phi(x) = erfc(-x / sqrt 2) / 2, evaluated with the Chebyshev-fitted formula
+// of Numerical Recipes (2nd ed., section 6.2, "erfcc"):
+//   t = 1 / (1 + z/2),  erfc(z) = t exp(-z^2 + poly(t)),  z >= 0,
+// whose fractional error is below 1.2e-7 for every z >= 0.  With z = |x|/sqrt 2
+// the tail mass c = erfc(z)/2 is Phi(x) for x < 0 and 1 - Phi(x) for x >= 0,
+// so both tails keep that relative accuracy (far below bf16 rounding).  One
+// reciprocal and one exponential per element for gelu, two for gelu'.
+__device__ __forceinline__ float erfcc_poly(float t) {
+  // -1.26551223 + t (1.00002368 + t (0.37409196 + ... + t 0.17087277))
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  return fmaf(p, t, -1.26551223f);
+}
 __device__ __forceinline__ float gelu_f(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));   // 1 + z/2 >= 1: hardware reciprocal, 1 ulp
+  const float c = 0.5f * t * __expf(fmaf(-z, z, erfcc_poly(t)));   // erfc(z) / 2
+  return x * (x >= 0.f ? 1.0f - c : c);
 }
 __device__ __forceinline__ float gelu_grad_f(float x) {
-  const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
-  const float pdf = 0.39894228040143268f * __expf(-0.5f * x * x);
-  return cdf + x * pdf;
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));   // 1 + z/2 >= 1: hardware reciprocal, 1 ulp
+  const float g = __expf(-z * z);                                   // exp(-x^2 / 2)
+  const float c = 0.5f * t * g * __expf(erfcc_poly(t));             // erfc(z) / 2
+  const float cdf = x >= 0.f ? 1.0f - c : c;
+  return fmaf(x * 0.39894228040143268f, g, cdf);                    // Phi(x) + x phi(x)
 }
 
 // ---------------------------------------------------------------- host side
