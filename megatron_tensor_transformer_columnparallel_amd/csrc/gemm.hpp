@@ -429,6 +429,24 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
       }
     }
   };
+  // One k-step's operand fragments, read into registers ahead of their MFMAs.
+  struct Frags {
+    bf16x8_t a[FM], b[FN];
+  };
+  auto read_frags = [&](const bf16_t* st, int ks, Frags& f) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f.b[j] = fb.read(st + BM * BK, ks, j);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) f.a[i] = fa.read(st, ks, i);
+  };
+  auto mfma_frags = [&](const Frags& f) {
+    // operands swapped: the result's lane layout is C(m = lane & 15, n = 4*(lane >> 4) + e)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
   auto issue = [&](int /*kt*/, int stage) {   // K tiles are issued in order
     bf16_t* st = lds + stage * STAGE;
     la.issue_direct(st, wave);
@@ -445,28 +463,47 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   };
 
   if (mn_inside) {
-    // Interior tile: every full K tile goes global -> LDS directly, NS-1 of
-    // them in flight while tile kt's fragments are read and multiplied.  No
-    // other vector-memory operation is issued in this loop, so the vmcnt
-    // count is exactly the DMA instructions of the tiles after kt.
+    // Interior tile: every full K tile goes global -> LDS directly, up to NS
+    // of them in flight.  Fragments are double-buffered by k-step: the LDS
+    // reads of the next k-step are issued before the MFMAs of the current
+    // one, and the barrier that publishes tile kt+1 (and frees tile kt's
+    // stage for tile kt+NS) sits before the MFMAs of tile kt's last k-step,
+    // so those MFMAs overlap the first reads of tile kt+1.  No other
+    // vector-memory operation is issued in this loop, so the vmcnt count is
+    // exactly the DMA instructions of the tiles after kt+1.
+    static_assert(KS == 2, "the pipelined loop pairs the two k-steps of a 64-wide K tile");
     constexpr int VPT = LoaderA::VECS + LoaderB::VECS;   // DMA instructions per wave per K tile
-    const int pre = min(NS - 1, nkd);
-    for (int p = 0; p < pre; ++p) issue(p, p);
-    int cs = 0, is = pre % NS;   // stage of tile kt; stage of the next tile to issue
-    for (int kt = 0; kt < nkd; ++kt) {
-      if (kt + NS - 1 <= nkd) wait_vmem_n<(NS - 2) * VPT>();   // NS-2 later tiles may stay in flight
+    if (nkd > 0) {
+      const int pre = min(NS, nkd);
+      for (int p = 0; p < pre; ++p) issue(p, p);
+      if (nkd >= NS) wait_vmem_n<(NS - 1) * VPT>();   // tile 0 landed
       else wait_vmem();
-      __syncthreads();   // tile kt visible; every wave is past tile kt-1, whose stage is reused next
-      if (kt + NS - 1 < nkd) {
-        issue(kt + NS - 1, is);
-        is = (is + 1 == NS) ? 0 : is + 1;
+      __syncthreads();
+      Frags f0, f1;
+      read_frags(lds, 0, f0);
+      int cs = 0;   // stage of tile kt (tile j lives in stage j % NS)
+      for (int kt = 0; kt < nkd; ++kt) {
+        read_frags(lds + cs * STAGE, 1, f1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_frags(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nx = (cs + 1 == NS) ? 0 : cs + 1;
+        if (kt + 1 < nkd) {
+          if (kt + NS <= nkd) wait_vmem_n<(NS - 2) * VPT>();   // tile kt+1 landed
+          else wait_vmem();
+          __syncthreads();   // tile kt+1 visible; every wave has read all of tile kt
+          if (kt + NS < nkd) issue(kt + NS, cs);
+          read_frags(lds + nx * STAGE, 0, f0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_frags(f1);
+        __builtin_amdgcn_sched_barrier(0);
+        cs = nx;
       }
-      compute(lds + cs * STAGE);
-      cs = (cs + 1 == NS) ? 0 : cs + 1;
     }
     if (nk > nkd) {
-      // the stage after the last direct tile: its last reader finished before
-      // the final loop barrier, and every DMA has been waited for
+      // the stage after the last direct tile: its last reader (tile nkd-NS)
+      // finished before a loop barrier, and every DMA has been waited for
       bf16_t* st = lds + (nkd % NS) * STAGE;
       load_checked(nkd);
       store_regs(st);
