@@ -174,7 +174,9 @@ __device__ __forceinline__ int kc_swizzle(int row) {
 
 template <int R>
 __device__ __forceinline__ int mn_swizzle(int k) {
-  if constexpr (R >= 128) return 2 * ((k & 3) | ((k >> 1) & 4));
+  // R = 128, 256: 16-chunk windows.  Other widths (64, 192) stay inside
+  // aligned groups of 8 chunks, so the XOR never leaves the row.
+  if constexpr (R % 128 == 0) return 2 * ((k & 3) | ((k >> 1) & 4));
   else return 2 * (((k >> 1) & 1) | ((k >> 2) & 2));
 }
 
@@ -193,38 +195,45 @@ template <int R, int NT, bool KC, int BK>
 struct OperandLoader {
   static constexpr int CPR = KC ? BK / 8 : R / 8;   // 16-byte chunks per LDS row
   static constexpr int VECS = R * BK / 8 / NT;      // slots per thread
-  static constexpr int RSTEP = NT / CPR;            // LDS rows between a thread's slots
   static constexpr int PERIOD = KC ? 8 : 16;        // rows after which the swizzle repeats
-  // A thread's slots sit RSTEP rows apart: either all at one swizzled column
-  // (RSTEP a multiple of the period) or alternating between two (half of it).
-  static constexpr bool ALT = RSTEP % PERIOD != 0;
-  static_assert(VECS >= 1 && NT % CPR == 0 && (2 * RSTEP) % PERIOD == 0, "operand tile vs thread count");
+  // Regular layout: a thread's slots sit RSTEP = NT / CPR rows apart, either
+  // all at one swizzled column (RSTEP a multiple of the period) or
+  // alternating between two (half of it).  Otherwise (a row of chunks that
+  // does not divide the thread count, e.g. 24 for a 192-wide M/N-contiguous
+  // tile) each slot keeps its own offset.
+  static constexpr bool REG = NT % CPR == 0 && (2 * (NT / CPR)) % PERIOD == 0;
+  static constexpr int RSTEP = REG ? NT / CPR : 1;
+  static constexpr bool ALT = REG && RSTEP % PERIOD != 0;
+  static_assert(VECS >= 1 && VECS * NT * 8 == R * BK, "operand tile vs thread count");
   static_assert(KC || R >= 64, "M/N-contiguous tiles need at least 8 chunks per k-row");
 
   u32x4_t v[VECS];
   const bf16_t* base;    // tile origin (row r0, current K tile) -- the same for every lane
-  uint32_t voff;         // bytes from `base` to this thread's first slot
-  uint32_t istep;        // bytes between the thread's slots
+  uint32_t voff;         // regular: bytes from `base` to this thread's first slot
+  uint32_t istep;        // regular: bytes between the thread's slots
+  uint32_t goff[REG ? 1 : VECS];   // irregular: bytes from `base` to each slot
   int64_t kstep;         // elements between K tiles
-  int row0;              // KC: m/n row of the first slot; else its k row
-  int col[2];            // KC: k column, else m/n column, of even and odd slots
+  int row0;              // regular, KC: m/n row of the first slot; else its k row
+  int col[2];            // regular, KC: k column, else m/n column, of even and odd slots
 
   static __device__ __forceinline__ int swz(int row) {
     if constexpr (KC) return kc_swizzle<CPR>(row);
     else return mn_swizzle<R>(row);
   }
+  // LDS row and (swizzled) column of slot i of this thread
+  static __device__ __forceinline__ int slot_row_of(int q) { return q / CPR; }
+  static __device__ __forceinline__ int slot_col_of(int q) { return ((q % CPR) ^ swz(q / CPR)) * 8; }
   __device__ __forceinline__ int slot_col(int i) const { return (ALT && (i & 1)) ? col[1] : col[0]; }
   // byte offset of slot i from `base`
   __device__ __forceinline__ uint32_t slot_off(int i) const {
-    return voff + (uint32_t)i * istep + ((ALT && (i & 1)) ? (uint32_t)(col[1] - col[0]) * 2u : 0u);
+    if constexpr (REG)
+      return voff + (uint32_t)i * istep + ((ALT && (i & 1)) ? (uint32_t)(col[1] - col[0]) * 2u : 0u);
+    else
+      return goff[i];
   }
 
   // ld * rows of the tile * 2 bytes must stay below 2^32 (checked on the host).
   __device__ __forceinline__ void init(const bf16_t* p, int64_t ld, int r0, int k0, int tid) {
-    const int row = tid / CPR, pos = tid % CPR;
-    row0 = row;
-    col[0] = (pos ^ swz(row)) * 8;
-    col[1] = (pos ^ swz(row + RSTEP)) * 8;
     if constexpr (KC) {
       base = p + (int64_t)r0 * ld + k0;
       kstep = BK;
@@ -232,8 +241,22 @@ struct OperandLoader {
       base = p + (int64_t)k0 * ld + r0;
       kstep = (int64_t)BK * ld;
     }
-    voff = (uint32_t)(((int64_t)row * ld + col[0]) * 2);
-    istep = (uint32_t)(RSTEP * ld * 2);
+    if constexpr (REG) {
+      const int row = tid / CPR, pos = tid % CPR;
+      row0 = row;
+      col[0] = (pos ^ swz(row)) * 8;
+      col[1] = (pos ^ swz(row + RSTEP)) * 8;
+      voff = (uint32_t)(((int64_t)row * ld + col[0]) * 2);
+      istep = (uint32_t)(RSTEP * ld * 2);
+    } else {
+      row0 = 0;
+      col[0] = col[1] = 0;
+#pragma unroll
+      for (int i = 0; i < VECS; ++i) {
+        const int q = tid + i * NT;
+        goff[i] = (uint32_t)(((int64_t)slot_row_of(q) * ld + slot_col_of(q)) * 2);
+      }
+    }
   }
 
   // Whole tile inside the operand: global -> LDS without registers, as
@@ -261,12 +284,13 @@ struct OperandLoader {
 
   // Edge tile: r_rem rows (m/n) and k_rem k remain from the tile origin;
   // elements outside are zero.
-  __device__ __forceinline__ void load_checked(int r_rem, int k_rem) {
+  __device__ __forceinline__ void load_checked(int r_rem, int k_rem, int tid) {
     const char* b = reinterpret_cast<const char*>(base);
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
       u32x4_t x = {0u, 0u, 0u, 0u};
-      const int rr = row0 + i * RSTEP, cc = slot_col(i);
+      const int rr = REG ? row0 + i * RSTEP : slot_row_of(tid + i * NT);
+      const int cc = REG ? slot_col(i) : slot_col_of(tid + i * NT);
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b + slot_off(i));
       if constexpr (KC) {
         if (rr < r_rem && cc < k_rem) {
@@ -454,8 +478,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   };
   auto load_checked = [&](int kt) {
     const int k_rem = s.K - kb - kt * BK;
-    la.load_checked(m_rem, k_rem);
-    lb.load_checked(n_rem, k_rem);
+    la.load_checked(m_rem, k_rem, tid);
+    lb.load_checked(n_rem, k_rem, tid);
   };
   auto store_regs = [&](bf16_t* st) {
     la.store(st, tid);
@@ -648,12 +672,19 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
 //     256 tiles, where one K tile in flight leaves the DMA latency exposed
 //     (2048x2048x4096: 62 -> 47 us);
 //   64x64 for problems too small for 64 tiles of 128x128.
+// Before all of these: 256x192 (8 waves of 64x96, two stages) when the
+// 256x256 grid does not fill whole rounds but a 256x192 grid with no edge
+// tiles does (2048x6144x4096 NN: 118 -> 107 us; 4096x6144x2048 TN: 120 us at
+// 128x128 -> 116 us).
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             hipStream_t st) {
   const int64_t t256 = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
   const int64_t t128x256 = ceil_div(s.M, 128) * ceil_div(s.N, 256) * (int64_t)s.batch;
   const int64_t t128 = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
+  const int64_t t192 = ceil_div(s.M, 256) * ceil_div(s.N, 192) * (int64_t)s.batch;
+  const bool full192 = s.M % 256 == 0 && s.N % 192 == 0 && t192 > 0 && t192 % 256 == 0;
+  if (full192 && t256 % 256 != 0) return launch_mfma<256, 192, 64, 4, 2, 2, AK, BKC>(A, B, s, epi, st);
   const bool partial_round = t256 > 256 && t256 < 512 && t256 % 256 != 0;
   if (t256 >= 192 && !partial_round) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
   if (t128x256 >= 192 && t128x256 <= 256) return launch_mfma<128, 256, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);

@@ -45,6 +45,7 @@ def run_mlp_shard(tp, X, A_r, B_r, dZ, tdt):
     (81, 100, 72, 144, 2, "bf16"),      # ragged: rows and columns not tile multiples
     (82, 333, 64, 8000, 2, "bf16"),     # 4000-wide shard: M x f_i GEMMs take the 256x256 tile
     (83, 130, 128, 384, 3, "bf16"),     # three shards
+    (84, 512, 64, 49152, 2, "bf16"),    # M x f_i = 512 x 24576: the 256x192 tile (forward NN, GELU' NT)
 ])
 def test_mlp_shards_match_oracle(tp, w, M, h, f, n, dt):
     say(f"tp_mlp fwd+bwd M={M} h={h} f={f} N={n} {dt}")
