@@ -454,18 +454,22 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
                      b * hs * sq, (int)sq, ldp, causal ? 1 : 0, scale);
   TPS_TRY(check_launch("attn_ds_kernel"));
   // dV = P^T dO                            (TN)  [sq x d] per head, K = queries >= key
+  // dK = dS^T Q                            (TN)  [sq x d] per head
+  // One launch, longest K ranges first: the short tiles of either fill the
+  // CUs left idle by the long ones.
   GemmShape s3 = shape(sq, d, sq, ldp, w);
   s3.batch = (int)(b * hs); s3.batch_inner = (int)hs;
   s3.sa_o = hs * sp; s3.sa_i = sp; s3.sb_o = sq * w; s3.sb_i = d;
   s3.kmode = causal ? 2 : 0;
-  TPS_TRY((gemm_bf16<false, false>(P, dO, s3, EpiStore<bf16_t>{dQKV + 2 * w, w3, sq * w3, d}, st)));
-  // dK = dS^T Q                            (TN)  [sq x d] per head
-  GemmShape s4 = s3;
-  s4.ldb = w3; s4.sb_o = sq * w3; s4.sb_i = d;
-  TPS_TRY((gemm_bf16<false, false>(dS, qkv, s4, EpiStore<bf16_t>{dQKV + w, w3, sq * w3, d}, st)));
+  s3.groups = 2;
+  s3.lpt = 1;
+  const GemmAlt<EpiStore<bf16_t>> dk{dS, qkv, ldp, w3, hs * sp, sp, sq * w3, d,
+                                     EpiStore<bf16_t>{dQKV + w, w3, sq * w3, d}};
+  TPS_TRY((gemm_bf16<false, false>(P, dO, s3, EpiStore<bf16_t>{dQKV + 2 * w, w3, sq * w3, d}, dk, st)));
   // dQ = dS K                              (NN)  [sq x d] per head, K = keys <= query
-  GemmShape s5 = s4;
-  s5.lda = ldp;
+  GemmShape s5 = shape(sq, d, sq, ldp, w3);
+  s5.batch = (int)(b * hs); s5.batch_inner = (int)hs;
+  s5.sa_o = hs * sp; s5.sa_i = sp; s5.sb_o = sq * w3; s5.sb_i = d;
   s5.kmode = causal ? 1 : 0;
   TPS_TRY((gemm_bf16<true, false>(dS, qkv + w, s5, EpiStore<bf16_t>{dQKV, w3, sq * w3, d}, st)));
   // dWqkv_i = X^T dQKV                     (TN)  [h x 3w], K = M

@@ -37,6 +37,24 @@ struct GemmShape {
   // limit (1: the diagonal; 256: a zero pad to the next multiple of 256).
   int skip_pad = 0;
   int group_m = 8;  // tile rows per group in the tile order (8 measured best for M = 2048)
+  // groups = 2: a second problem (GemmAlt) with this same shape, layout,
+  // batch and K ranges runs in the same launch.
+  int groups = 1;
+  // lpt: tiles are issued longest K range first (kmode 1: last tile row
+  // first; kmode 2: first tile row first), ranks outermost and then group,
+  // batch entry and tile column, so every XCD gets the same mix of lengths
+  // and short tiles fill the CUs that long tiles leave idle.
+  int lpt = 0;
+};
+
+// The second problem of a grouped launch: its own operands, strides and
+// epilogue; everything else comes from the GemmShape.
+template <class Epi>
+struct GemmAlt {
+  const bf16_t* A;
+  const bf16_t* B;
+  int64_t lda, ldb, sa_o, sa_i, sb_o, sb_i;
+  Epi epi;
 };
 
 // ------------------------------------------------------------------ epilogues
@@ -364,7 +382,8 @@ struct FragReader {
 // from the accumulators.
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool AK, bool BKC, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64, 1)
-gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, GemmShape s, Epi epi) {
+gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, GemmShape s, Epi epi0,
+                 GemmAlt<Epi> alt) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -378,11 +397,27 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_BYTES / 2];
 
   const int tiles_m = (s.M + BM - 1) / BM, tiles_n = (s.N + BN - 1) / BN;
-  const int total = tiles_m * tiles_n * s.batch;
+  const int total = tiles_m * tiles_n * s.batch * s.groups;
   if ((int)blockIdx.x >= total) return;
-  int z, tm, tn;
-  tile_coords(blockIdx.x, total, tiles_m, tiles_n, s.group_m, z, tm, tn);
+  int z, tm, tn, g = 0;
+  if (s.lpt) {
+    const int per_rank = tiles_n * s.batch * s.groups, per_group = tiles_n * s.batch;
+    const int r = (int)blockIdx.x / per_rank, rem = (int)blockIdx.x - r * per_rank;
+    g = rem / per_group;
+    const int rem2 = rem - g * per_group;
+    z = rem2 / tiles_n;
+    tn = rem2 - z * tiles_n;
+    tm = s.kmode == 1 ? tiles_m - 1 - r : r;
+  } else {
+    tile_coords(blockIdx.x, total, tiles_m, tiles_n, s.group_m, z, tm, tn);   // groups == 1
+  }
   const int zo = z / s.batch_inner, zi = z - zo * s.batch_inner;
+  // operands of this tile's problem
+  const bf16_t* const Ap = g ? alt.A : A;
+  const bf16_t* const Bp = g ? alt.B : B;
+  const int64_t lda = g ? alt.lda : s.lda, ldb = g ? alt.ldb : s.ldb;
+  const int64_t sa_o = g ? alt.sa_o : s.sa_o, sa_i = g ? alt.sa_i : s.sa_i;
+  const int64_t sb_o = g ? alt.sb_o : s.sb_o, sb_i = g ? alt.sb_i : s.sb_i;
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -410,8 +445,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   using LoaderB = OperandLoader<BN, NT, BKC, BK>;
   LoaderA la;
   LoaderB lb;
-  la.init(A + zo * s.sa_o + zi * s.sa_i, s.lda, m0, kb, tid);
-  lb.init(B + zo * s.sb_o + zi * s.sb_i, s.ldb, n0, kb, tid);
+  la.init(Ap + zo * sa_o + zi * sa_i, lda, m0, kb, tid);
+  lb.init(Bp + zo * sb_o + zi * sb_i, ldb, n0, kb, tid);
   FragReader<BM, FM, AK, BK> fa;
   FragReader<BN, FN, BKC, BK> fb;
   fa.init(wm * WTM, lane);
@@ -556,8 +591,9 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   // 16-byte accesses; no LDS and no barrier are involved, so waves leave
   // the K-loop independently.
   static_assert(FN % 2 == 0, "fragments are paired along n");
-  const int g = lane >> 4;
-  const bool odd = g & 1;
+  const Epi epi = g ? alt.epi : epi0;
+  const int lg = lane >> 4;
+  const bool odd = lg & 1;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * WTM + i * 16 + (lane & 15);
@@ -573,7 +609,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
         v[e] = odd ? recv : a0[e];
         v[4 + e] = odd ? a1[e] : recv;
       }
-      const int n = n0 + wn * WTN + (jp + (odd ? 1 : 0)) * 16 + (g >> 1) * 8;
+      const int n = n0 + wn * WTN + (jp + (odd ? 1 : 0)) * 16 + (lg >> 1) * 8;
       if (m < s.M && n < s.N) epi(zo, zi, m, n, v, min(8, s.N - n));
     }
   }
@@ -645,17 +681,29 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B, GemmSh
 
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool AK, bool BKC, class Epi>
 inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
-                              hipStream_t st) {
-  const int64_t tiles = ceil_div(s.M, BM) * ceil_div(s.N, BN) * (int64_t)s.batch;
+                              const GemmAlt<Epi>& alt, hipStream_t st) {
+  const int64_t tiles = ceil_div(s.M, BM) * ceil_div(s.N, BN) * (int64_t)s.batch * s.groups;
   if (tiles == 0) return TPS_OK;
   if (tiles > 0x7fffffff) return set_error(TPS_EINVAL, "gemm: too many tiles");
+  if (s.groups != 1 && (s.groups != 2 || !s.lpt)) return set_error(TPS_EINVAL, "gemm: groups must be 1, or 2 with lpt");
   // per-lane operand offsets inside a tile are 32-bit byte offsets
-  const int64_t span_a = (AK ? BM : BK) * s.lda * 2, span_b = (BKC ? BN : BK) * s.ldb * 2;
+  int64_t lda = s.lda, ldb = s.ldb;
+  if (s.groups == 2) {
+    lda = lda > alt.lda ? lda : alt.lda;
+    ldb = ldb > alt.ldb ? ldb : alt.ldb;
+  }
+  const int64_t span_a = (AK ? BM : BK) * lda * 2, span_b = (BKC ? BN : BK) * ldb * 2;
   if (span_a >= (1LL << 32) || span_b >= (1LL << 32))
     return set_error(TPS_EINVAL, "gemm: leading dimension too large for 32-bit tile offsets");
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, NS, AK, BKC, Epi>), dim3((unsigned)tiles),
-                     dim3(WM * WN * 64), 0, st, A, B, s, epi);
+                     dim3(WM * WN * 64), 0, st, A, B, s, epi, alt);
   return check_launch("gemm_bf16_kernel");
+}
+
+// The second problem slot of a single-problem launch (never read).
+template <class Epi>
+inline GemmAlt<Epi> no_alt(const Epi& e) {
+  return GemmAlt<Epi>{nullptr, nullptr, 0, 0, 0, 0, 0, 0, e};
 }
 
 // Tile shape by problem size, from cold-cache timings of these kernels on
@@ -672,25 +720,35 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
 //     256 tiles, where one K tile in flight leaves the DMA latency exposed
 //     (2048x2048x4096: 62 -> 47 us);
 //   64x64 for problems too small for 64 tiles of 128x128.
-// Before all of these: 256x192 (8 waves of 64x96, two stages) when the
+// Longest-first (lpt) launches always take 128x128 with three stages: one
+// workgroup per CU, so the CUs that finish short tiles pick up the next
+// ones (dV and dK together: 57.6 -> 39.2 us against two launches).
+// Otherwise, before all of these: 256x192 (8 waves of 64x96, two stages) when the
 // 256x256 grid does not fill whole rounds but a 256x192 grid with no edge
 // tiles does (2048x6144x4096 NN: 118 -> 107 us; 4096x6144x2048 TN: 120 us at
 // 128x128 -> 116 us).
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
-                            hipStream_t st) {
-  const int64_t t256 = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch;
-  const int64_t t128x256 = ceil_div(s.M, 128) * ceil_div(s.N, 256) * (int64_t)s.batch;
-  const int64_t t128 = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch;
-  const int64_t t192 = ceil_div(s.M, 256) * ceil_div(s.N, 192) * (int64_t)s.batch;
+                            const GemmAlt<Epi>& alt, hipStream_t st) {
+  const int64_t t256 = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch * s.groups;
+  const int64_t t128x256 = ceil_div(s.M, 128) * ceil_div(s.N, 256) * (int64_t)s.batch * s.groups;
+  const int64_t t128 = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch * s.groups;
+  const int64_t t192 = ceil_div(s.M, 256) * ceil_div(s.N, 192) * (int64_t)s.batch * s.groups;
   const bool full192 = s.M % 256 == 0 && s.N % 192 == 0 && t192 > 0 && t192 % 256 == 0;
-  if (full192 && t256 % 256 != 0) return launch_mfma<256, 192, 64, 4, 2, 2, AK, BKC>(A, B, s, epi, st);
+  if (s.lpt) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
+  if (full192 && t256 % 256 != 0) return launch_mfma<256, 192, 64, 4, 2, 2, AK, BKC>(A, B, s, epi, alt, st);
   const bool partial_round = t256 > 256 && t256 < 512 && t256 % 256 != 0;
-  if (t256 >= 192 && !partial_round) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
-  if (t128x256 >= 192 && t128x256 <= 256) return launch_mfma<128, 256, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);
-  if (t128 > 256) return launch_mfma<128, 128, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, st);
-  if (t128 >= 64) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, st);
-  return launch_mfma<64, 64, 64, 2, 2, 2, AK, BKC>(A, B, s, epi, st);
+  if (t256 >= 192 && !partial_round) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, alt, st);
+  if (t128x256 >= 192 && t128x256 <= 256) return launch_mfma<128, 256, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
+  if (t128 > 256) return launch_mfma<128, 128, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, alt, st);
+  if (t128 >= 64) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
+  return launch_mfma<64, 64, 64, 2, 2, 2, AK, BKC>(A, B, s, epi, alt, st);
+}
+
+// A single problem.
+template <bool AK, bool BKC, class Epi>
+inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi, hipStream_t st) {
+  return gemm_bf16<AK, BKC>(A, B, s, epi, no_alt(epi), st);
 }
 
 template <bool AK, bool BKC, class Epi>
