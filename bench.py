@@ -222,7 +222,7 @@ def cpu_baseline():
 # --no-embed --no-layer`, divided by what the same counters read for a plain
 # copy (shard_reduce with one part over 512 MiB) per byte moved.  Valid only
 # for the GEMM source it was taken on (sha256 prefix below); otherwise null.
-ROOFLINE_TRAFFIC = {"gemm_sha": "bc9f184fe7f48c65", "bytes_per_launch": 826632410}
+ROOFLINE_TRAFFIC = {"gemm_sha": "225e482dd4bc6067", "bytes_per_launch": 827550703}
 
 
 def _gemm_sha():
