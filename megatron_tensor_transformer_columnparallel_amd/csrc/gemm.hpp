@@ -45,6 +45,10 @@ struct GemmShape {
   // batch entry and tile column, so every XCD gets the same mix of lengths
   // and short tiles fill the CUs that long tiles leave idle.
   int lpt = 0;
+  // Output coordinates of this problem's (0, 0): the epilogue sees
+  // (m + m_base, n + n_base), so a problem can be one part of a larger
+  // output (the tail split below).
+  int m_base = 0, n_base = 0;
 };
 
 // The second problem of a grouped launch: its own operands, strides and
@@ -610,7 +614,7 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
         v[4 + e] = odd ? a1[e] : recv;
       }
       const int n = n0 + wn * WTN + (jp + (odd ? 1 : 0)) * 16 + (lg >> 1) * 8;
-      if (m < s.M && n < s.N) epi(zo, zi, m, n, v, min(8, s.N - n));
+      if (m < s.M && n < s.N) epi(zo, zi, m + s.m_base, n + s.n_base, v, min(8, s.N - n));
     }
   }
 }
@@ -673,11 +677,14 @@ gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B, GemmSh
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + tr * 4 + i;
-    if (m < s.M) epi(zo, zi, m, n, acc[i], min(8, s.N - n));
+    if (m < s.M) epi(zo, zi, m + s.m_base, n + s.n_base, acc[i], min(8, s.N - n));
   }
 }
 
 // ------------------------------------------------------------------ dispatch
+
+#define TPS_GEMM_TRY(expr) \
+  do { tps_status _st = (expr); if (_st != TPS_OK) return _st; } while (0)
 
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool AK, bool BKC, class Epi>
 inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
@@ -731,6 +738,33 @@ template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             const GemmAlt<Epi>& alt, hipStream_t st) {
   const int64_t t256 = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch * s.groups;
+  // Tail split: a single problem whose 256x256 grid ends in a round at most
+  // a quarter full runs as whole rounds of 256x256 tiles plus the leftover
+  // columns (or rows) as a second launch with smaller tiles.  Each output
+  // element is summed in the same K order either way (bit-identical).
+  // 2048x25129x4096 NT: 479 -> 416 us; 25129x4096x2048 TN: 513 -> 469 us (cold).
+  if (s.batch == 1 && s.groups == 1 && s.kmode == 0 && !s.skip_upper && t256 > 256 && t256 % 256 != 0 &&
+      t256 % 256 <= 64) {
+    const int64_t tmr = ceil_div(s.M, 256), tnr = ceil_div(s.N, 256), full = t256 / 256 * 256;
+    if (256 % tmr == 0 && full / tmr < tnr) {          // split the columns
+      const int nm = (int)(full / tmr * 256);
+      GemmShape a = s, b = s;
+      a.N = nm;
+      b.N = s.N - nm;
+      b.n_base = s.n_base + nm;
+      TPS_GEMM_TRY((gemm_bf16<AK, BKC>(A, B, a, epi, alt, st)));
+      return gemm_bf16<AK, BKC>(A, B + (BKC ? (int64_t)nm * s.ldb : (int64_t)nm), b, epi, alt, st);
+    }
+    if (256 % tnr == 0 && full / tnr < tmr) {          // split the rows
+      const int mm = (int)(full / tnr * 256);
+      GemmShape a = s, b = s;
+      a.M = mm;
+      b.M = s.M - mm;
+      b.m_base = s.m_base + mm;
+      TPS_GEMM_TRY((gemm_bf16<AK, BKC>(A, B, a, epi, alt, st)));
+      return gemm_bf16<AK, BKC>(A + (AK ? (int64_t)mm * s.lda : (int64_t)mm), B, b, epi, alt, st);
+    }
+  }
   const int64_t t128x256 = ceil_div(s.M, 128) * ceil_div(s.N, 256) * (int64_t)s.batch * s.groups;
   const int64_t t128 = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch * s.groups;
   const int64_t t192 = ceil_div(s.M, 256) * ceil_div(s.N, 192) * (int64_t)s.batch * s.groups;

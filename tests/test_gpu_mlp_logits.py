@@ -112,6 +112,7 @@ def test_mlp_workload2_full_size(tp):
     (1, 64, 64, 300, 2, "f32", 4),        # workload-1 shapes
     (84, 300, 2048, 15985, 2, "bf16", 8),   # ragged shard widths 7993/7992, ldl > v_rows
     (85, 2000, 64, 15985, 2, "bf16", 0),    # T x v_r logits take the 256x256 tile
+    (86, 512, 512, 66000, 2, "bf16", 0),    # 258-tile grids: logits split by columns, dE by rows
 ])
 def test_tied_logits_match_oracle(tp, w, T, H, V, n, dt, pad):
     say(f"tied_logits fwd+bwd T={T} H={H} V={V} {dt}")
