@@ -234,6 +234,8 @@ struct OperandLoader {
   uint32_t voff;         // regular: bytes from `base` to this thread's first slot
   uint32_t istep;        // regular: bytes between the thread's slots
   uint32_t goff[REG ? 1 : VECS];   // irregular: bytes from `base` to each slot
+  uint32_t rowb;         // regular: bytes per source row
+  int rv;                // regular, KC: last row inside the operand (same for every lane); later slots re-read it
   int64_t kstep;         // elements between K tiles
   int row0;              // regular, KC: m/n row of the first slot; else its k row
   int col[2];            // regular, KC: k column, else m/n column, of even and odd slots
@@ -248,14 +250,20 @@ struct OperandLoader {
   __device__ __forceinline__ int slot_col(int i) const { return (ALT && (i & 1)) ? col[1] : col[0]; }
   // byte offset of slot i from `base`
   __device__ __forceinline__ uint32_t slot_off(int i) const {
-    if constexpr (REG)
-      return voff + (uint32_t)i * istep + ((ALT && (i & 1)) ? (uint32_t)(col[1] - col[0]) * 2u : 0u);
-    else
+    if constexpr (REG) {
+      const uint32_t alt = (ALT && (i & 1)) ? (uint32_t)(col[1] - col[0]) * 2u : 0u;
+      if constexpr (KC) return voff + (uint32_t)((min(row0 + i * RSTEP, rv) - row0) * (int)rowb) + alt;
+      else return voff + (uint32_t)i * istep + alt;
+    } else {
       return goff[i];
+    }
   }
 
   // ld * rows of the tile * 2 bytes must stay below 2^32 (checked on the host).
-  __device__ __forceinline__ void init(const bf16_t* p, int64_t ld, int r0, int k0, int tid) {
+  // K-contiguous tiles with r_valid < R rows inside the operand re-read its
+  // last row in place of the missing ones (every k of a full K tile is in
+  // range), so they can take the direct path; the epilogue drops those rows.
+  __device__ __forceinline__ void init(const bf16_t* p, int64_t ld, int r0, int k0, int tid, int r_valid = R) {
     if constexpr (KC) {
       base = p + (int64_t)r0 * ld + k0;
       kstep = BK;
@@ -270,6 +278,8 @@ struct OperandLoader {
       col[1] = (pos ^ swz(row + RSTEP)) * 8;
       voff = (uint32_t)(((int64_t)row * ld + col[0]) * 2);
       istep = (uint32_t)(RSTEP * ld * 2);
+      rowb = (uint32_t)(ld * 2);
+      rv = (r_valid < R ? r_valid : R) - 1;
     } else {
       row0 = 0;
       col[0] = col[1] = 0;
@@ -435,8 +445,10 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   k_range(s, m0, BM, BK, kb, ke);
   if (s.skip_upper && n0 > m0 + BM - 1) ke = kb;
   const int nk = (ke - kb + BK - 1) / BK;
-  // K tiles [0, nkd) are loaded directly (tile inside M and N, all BK k in range)
-  const bool mn_inside = (m0 + BM <= s.M) && (n0 + BN <= s.N);
+  // K tiles [0, nkd) are loaded directly: all BK k in range, and every row
+  // inside the operand or the operand K-contiguous (missing rows re-read the
+  // last one; their outputs are never stored)
+  const bool mn_inside = (AK || m0 + BM <= s.M) && (BKC || n0 + BN <= s.N);
   const int nkd = mn_inside ? (ke - kb) / BK : 0;
 
   f32x4_t acc[FM][FN];
@@ -449,8 +461,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   using LoaderB = OperandLoader<BN, NT, BKC, BK>;
   LoaderA la;
   LoaderB lb;
-  la.init(Ap + zo * sa_o + zi * sa_i, lda, m0, kb, tid);
-  lb.init(Bp + zo * sb_o + zi * sb_i, ldb, n0, kb, tid);
+  la.init(Ap + zo * sa_o + zi * sa_i, lda, m0, kb, tid, s.M - m0);
+  lb.init(Bp + zo * sb_o + zi * sb_i, ldb, n0, kb, tid, s.N - n0);
   FragReader<BM, FM, AK, BK> fa;
   FragReader<BN, FN, BKC, BK> fb;
   fa.init(wm * WTM, lane);
