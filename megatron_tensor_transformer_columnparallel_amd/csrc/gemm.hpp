@@ -1,9 +1,9 @@
 // Dense GEMM kernels for gfx950: C(m,n) = sum_k A(m,k) B(k,n), fp32 accumulate,
 // result handed to a fused epilogue functor.
 //
-// bf16 path: LDS-tiled MFMA kernel (v_mfma_f32_16x16x32_bf16), double-buffered
-// LDS fed by direct global -> LDS loads (registers only for edge tiles),
-// XCD-aware tile order.  Each operand keeps its global orientation in LDS;
+// bf16 path: LDS-tiled MFMA kernel (v_mfma_f32_16x16x32_bf16), multi-stage
+// LDS fed by direct global -> LDS loads (registers only for a ragged last K
+// tile), XCD-aware tile order.  Each operand keeps its global orientation in LDS;
 // fragments of an M/N-contiguous operand come out of the LDS transpose read.
 //
 // fp32 path: LDS-tiled SIMT kernel (4x4 outputs per thread), same epilogues.
@@ -228,6 +228,7 @@ struct OperandLoader {
   static constexpr bool ALT = REG && RSTEP % PERIOD != 0;
   static_assert(VECS >= 1 && VECS * NT * 8 == R * BK, "operand tile vs thread count");
   static_assert(KC || R >= 64, "M/N-contiguous tiles need at least 8 chunks per k-row");
+  static_assert(REG || !KC, "K-contiguous tiles always have the regular layout");
 
   u32x4_t v[VECS];
   const bf16_t* base;    // tile origin (row r0, current K tile) -- the same for every lane
@@ -259,10 +260,15 @@ struct OperandLoader {
     }
   }
 
-  // ld * rows of the tile * 2 bytes must stay below 2^32 (checked on the host).
-  // K-contiguous tiles with r_valid < R rows inside the operand re-read its
-  // last row in place of the missing ones (every k of a full K tile is in
-  // range), so they can take the direct path; the epilogue drops those rows.
+  // ld * rows of the tile * 2 bytes must stay below 2^32, and ld a multiple
+  // of 8 (checked on the host).  A tile with only r_valid < R of its rows
+  // (K-contiguous) or columns (M/N-contiguous) inside the operand still takes
+  // the direct path for full K tiles: K-contiguous slots past the end re-read
+  // the last row; M/N-contiguous chunks past the end re-read the chunk that
+  // holds the last element (a chunk that straddles the end reads at most 7
+  // elements beyond it, inside the row since ld is a multiple of 8).  The
+  // values read for missing rows or columns only reach outputs the epilogue
+  // drops.
   __device__ __forceinline__ void init(const bf16_t* p, int64_t ld, int r0, int k0, int tid, int r_valid = R) {
     if constexpr (KC) {
       base = p + (int64_t)r0 * ld + k0;
@@ -271,11 +277,16 @@ struct OperandLoader {
       base = p + (int64_t)k0 * ld + r0;
       kstep = (int64_t)BK * ld;
     }
+    const int cmax = ((min(r_valid, R) - 1) / 8) * 8;   // M/N-contiguous: last chunk with a valid element
     if constexpr (REG) {
       const int row = tid / CPR, pos = tid % CPR;
       row0 = row;
       col[0] = (pos ^ swz(row)) * 8;
       col[1] = (pos ^ swz(row + RSTEP)) * 8;
+      if constexpr (!KC) {
+        col[0] = min(col[0], cmax);
+        col[1] = min(col[1], cmax);
+      }
       voff = (uint32_t)(((int64_t)row * ld + col[0]) * 2);
       istep = (uint32_t)(RSTEP * ld * 2);
       rowb = (uint32_t)(ld * 2);
@@ -286,7 +297,7 @@ struct OperandLoader {
 #pragma unroll
       for (int i = 0; i < VECS; ++i) {
         const int q = tid + i * NT;
-        goff[i] = (uint32_t)(((int64_t)slot_row_of(q) * ld + slot_col_of(q)) * 2);
+        goff[i] = (uint32_t)(((int64_t)slot_row_of(q) * ld + min(slot_col_of(q), cmax)) * 2);
       }
     }
   }
@@ -314,15 +325,16 @@ struct OperandLoader {
     base += kstep;
   }
 
-  // Edge tile: r_rem rows (m/n) and k_rem k remain from the tile origin;
-  // elements outside are zero.
+  // Ragged last K tile: r_rem rows (m/n) and k_rem k remain from the tile
+  // origin; k outside is zero (m/n outside only reaches dropped outputs).
   __device__ __forceinline__ void load_checked(int r_rem, int k_rem, int tid) {
     const char* b = reinterpret_cast<const char*>(base);
 #pragma unroll
     for (int i = 0; i < VECS; ++i) {
       u32x4_t x = {0u, 0u, 0u, 0u};
       const int rr = REG ? row0 + i * RSTEP : slot_row_of(tid + i * NT);
-      const int cc = REG ? slot_col(i) : slot_col_of(tid + i * NT);
+      // the (clamped) column this slot reads; its validity is checked below
+      const int cc = REG ? slot_col(i) : min(slot_col_of(tid + i * NT), ((min(r_rem, R) - 1) / 8) * 8);
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(b + slot_off(i));
       if constexpr (KC) {
         if (rr < r_rem && cc < k_rem) {
@@ -389,11 +401,10 @@ struct FragReader {
 
 // One workgroup computes a BM x BN tile with WM x WN waves, each wave a
 // (BM/WM) x (BN/WN) block of 16x16 MFMA tiles.  K advances in tiles of BK
-// through NS LDS stages.  Interior tiles (the whole BM x BN block inside
-// the matrix) keep NS-1 K tiles in flight from global memory straight into
-// LDS while the MFMAs consume the current one; edge tiles go through
-// bounds-checked register loads (two of the stages).  The epilogue runs
-// from the accumulators.
+// through NS LDS stages: up to NS full K tiles are in flight from global
+// memory straight into LDS while the MFMAs consume the current one (tiles
+// that stick out of M or N included); a ragged last K tile goes through
+// bounds-checked register loads.  The epilogue runs from the accumulators.
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool AK, bool BKC, class Epi>
 __global__ void __launch_bounds__(WM * WN * 64, 1)
 gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, GemmShape s, Epi epi0,
@@ -445,11 +456,11 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
   k_range(s, m0, BM, BK, kb, ke);
   if (s.skip_upper && n0 > m0 + BM - 1) ke = kb;
   const int nk = (ke - kb + BK - 1) / BK;
-  // K tiles [0, nkd) are loaded directly: all BK k in range, and every row
-  // inside the operand or the operand K-contiguous (missing rows re-read the
-  // last one; their outputs are never stored)
-  const bool mn_inside = (AK || m0 + BM <= s.M) && (BKC || n0 + BN <= s.N);
-  const int nkd = mn_inside ? (ke - kb) / BK : 0;
+  // Full K tiles [0, nkd) are loaded directly, also for tiles that stick out
+  // of M or N (the loaders re-read valid rows or chunks for the missing ones,
+  // whose outputs the epilogue drops); a ragged last K tile goes through
+  // bounds-checked register loads.
+  const int nkd = (ke - kb) / BK;
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -537,8 +548,8 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
     lb.store(st + BM * BK, tid);
   };
 
-  if (mn_inside) {
-    // Interior tile: every full K tile goes global -> LDS directly, up to NS
+  {
+    // Every full K tile goes global -> LDS directly, up to NS
     // of them in flight.  Fragments are double-buffered by k-step: the LDS
     // reads of the next k-step are issued before the MFMAs of the current
     // one, and the barrier that publishes tile kt+1 (and frees tile kt's
@@ -583,17 +594,6 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
       load_checked(nkd);
       store_regs(st);
       __syncthreads();
-      compute(st);
-    }
-  } else {
-    // Edge tile: bounds-checked loads through registers into alternating
-    // stages (no register double-buffering: the loaded values are dead once
-    // stored, which keeps them out of the MFMA loop's register budget).
-    for (int kt = 0; kt < nk; ++kt) {
-      bf16_t* st = lds + (kt & 1) * STAGE;
-      load_checked(kt);
-      store_regs(st);
-      __syncthreads();   // stage kt & 1 written; everyone is past tile kt-1
       compute(st);
     }
   }
@@ -711,6 +711,11 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
     lda = lda > alt.lda ? lda : alt.lda;
     ldb = ldb > alt.ldb ? ldb : alt.ldb;
   }
+  // 16-byte chunks of every row (and of each partial tile's re-read chunk)
+  // stay aligned and inside their row only with leading dims that are
+  // multiples of 8
+  if (lda % 8 != 0 || ldb % 8 != 0 || (s.groups == 2 && (alt.lda % 8 != 0 || alt.ldb % 8 != 0)))
+    return set_error(TPS_EINVAL, "gemm: leading dimensions must be multiples of 8");
   const int64_t span_a = (AK ? BM : BK) * lda * 2, span_b = (BKC ? BN : BK) * ldb * 2;
   if (span_a >= (1LL << 32) || span_b >= (1LL << 32))
     return set_error(TPS_EINVAL, "gemm: leading dimension too large for 32-bit tile offsets");
