@@ -95,9 +95,10 @@ __global__ void __launch_bounds__(1024) bitonic_local_kernel(uint64_t* keys, int
 }
 
 // Single-workgroup stable sort by row for T <= kRadixMax tokens: the
-// 32-bit keys (row << tbits | t) start in token order, so a stable LSD radix
-// sort on the row bits (8 bits per pass) leaves each row's tokens ascending
-// in t.  Out-of-range tokens get row = v_rows and sort last.  Per pass, each
+// in-range tokens are first compacted, in token order, into 32-bit keys
+// (row << tbits | t) (out-of-range tokens carry no gradient and only fill
+// the tail of the output with kNoKey), so a stable LSD radix sort on the row
+// bits (8 bits per pass) leaves each row's tokens ascending in t.  Per pass, each
 // of the 16 waves owns a contiguous run of the keys and its own 256 digit
 // counters; lanes with equal digits are found with eight ballots, so a
 // block's count per digit and a lane's rank among earlier lanes with its
@@ -128,10 +129,15 @@ __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const i
   __shared__ uint32_t off[kRadixWaves * 256];   // [wave][digit]: a wave's counters are contiguous
   __shared__ uint32_t wsum[kRadixWaves];
   static_assert(256 * kRadixWaves == 4 * kRadixThreads, "scan: four entries per thread");
+  __shared__ uint32_t nin_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t tmask = (1u << tbits) - 1u;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   {
-    // all id loads in flight at once, then the keys
+    // all id loads in flight at once; then, block of kRadixThreads tokens by
+    // block, the in-range keys are appended in token order: a lane's place
+    // is the in-range lanes before it in its wave plus the earlier waves'
+    // totals
     constexpr int PER = kRadixMax / kRadixThreads;
     int32_t idv[PER];
 #pragma unroll
@@ -139,20 +145,32 @@ __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const i
       const int t = tid + i * kRadixThreads;
       idv[i] = t < ntok ? ids[t] : 0;
     }
+    uint32_t base = 0;   // keys appended by earlier blocks (same value in every thread)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int t = tid + i * kRadixThreads;
-      if (t < ntok) {
-        const int64_t local = (int64_t)idv[i] - v_start;
-        const uint32_t row = (local >= 0 && local < v_rows) ? (uint32_t)local : (uint32_t)v_rows;
-        kb[0][t] = (row << tbits) | (uint32_t)t;
+      const int64_t local = (int64_t)idv[i] - v_start;
+      const bool in = t < ntok && local >= 0 && local < v_rows;
+      const uint64_t bal = __ballot(in);
+      if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
+      __syncthreads();
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (int w = 0; w < kRadixWaves; ++w) {
+        const uint32_t c = wsum[w];
+        before += w < wave ? c : 0u;
+        all += c;
       }
+      if (in) kb[0][base + before + (uint32_t)__popcll(bal & lt_mask)] = ((uint32_t)local << tbits) | (uint32_t)t;
+      base += all;
+      __syncthreads();   // wsum is rewritten by the next block
     }
+    if (tid == 0) nin_s = base;
   }
   __syncthreads();
-  const int per = (ntok + kRadixWaves - 1) / kRadixWaves;   // keys per wave
-  const int lo = min(ntok, wave * per), hi = min(ntok, lo + per);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nin = (int)nin_s;
+  const int per = (nin + kRadixWaves - 1) / kRadixWaves;   // keys per wave
+  const int lo = min(nin, wave * per), hi = min(nin, lo + per);
   uint32_t* my = off + wave * 256;
   int cur = 0;
   for (int shift = 0; shift < rbits; shift += 8) {
@@ -213,9 +231,12 @@ __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const i
     __syncthreads();
   }
   for (int t = tid; t < ntok; t += kRadixThreads) {
-    const uint32_t key = kb[cur][t];
-    const uint32_t row = key >> tbits;
-    keys_out[t] = (row >= (uint32_t)v_rows) ? kNoKey : (((uint64_t)row << 32) | (uint64_t)(key & tmask));
+    if (t < nin) {
+      const uint32_t key = kb[cur][t];
+      keys_out[t] = ((uint64_t)(key >> tbits) << 32) | (uint64_t)(key & tmask);
+    } else {
+      keys_out[t] = kNoKey;
+    }
   }
 }
 
