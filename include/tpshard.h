@@ -197,6 +197,8 @@ tps_status shard_reduce_add(tps_dtype res_dt, const void* res, tps_dtype part_dt
 tps_status vocab_embed_fwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
                            const int32_t* ids, const void* E_r, void* Y_r, tps_stream_t stream);
 
+/* Workspace of vocab_embed_bwd: the sort keys (8 bytes per token, T rounded
+ * up to a power of two) and 256 row-bucket counts (4 bytes each). */
 size_t vocab_embed_bwd_workspace(int64_t T, int64_t v_rows);
 
 /*

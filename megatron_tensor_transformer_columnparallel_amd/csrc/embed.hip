@@ -94,11 +94,16 @@ __global__ void __launch_bounds__(1024) bitonic_local_kernel(uint64_t* keys, int
   for (int i = threadIdx.x; i < chunk; i += 1024) keys[base + i] = s[i];
 }
 
-// Single-workgroup stable sort by row for T <= kRadixMax tokens: the
-// in-range tokens are first compacted, in token order, into 32-bit keys
-// (row << tbits | t) (out-of-range tokens carry no gradient and only fill
-// the tail of the output with kNoKey), so a stable LSD radix sort on the row
-// bits (8 bits per pass) leaves each row's tokens ascending in t.  Per pass, each
+// Stable sort by row for T <= kRadixMax tokens, one workgroup per bucket of
+// `bucket_rows` consecutive rows (one bucket holding every row when counts
+// is null).  A bucket's tokens are first compacted, in token order, into
+// 32-bit keys ((row - first row of the bucket) << tbits | t) (out-of-range
+// tokens carry no gradient and only fill the tail of the output with
+// kNoKey), so a stable LSD radix sort on those row bits (8 bits per pass)
+// leaves each row's tokens ascending in t.  The bucket's keys go to the
+// output after those of all earlier buckets (counts[] from
+// embed_bucket_count_kernel), so the buckets together give the same order
+// as one sort of every key.  Per pass, each
 // of the 16 waves owns a contiguous run of the keys and its own 256 digit
 // counters; lanes with equal digits are found with eight ballots, so a
 // block's count per digit and a lane's rank among earlier lanes with its
@@ -121,51 +126,99 @@ __device__ __forceinline__ uint64_t same_digit_lanes(uint32_t d, bool valid) {
   return same;
 }
 
+// Tokens of each bucket of `bucket_rows` rows (one workgroup per bucket).
+__global__ void __launch_bounds__(256) embed_bucket_count_kernel(const int32_t* __restrict__ ids,
+                                                                 uint32_t* __restrict__ counts, int ntok,
+                                                                 int64_t v_start, int v_rows, int bucket_rows) {
+  __shared__ uint32_t ws[4];
+  const int64_t lo = v_start + (int64_t)blockIdx.x * bucket_rows;
+  const int64_t hi = v_start + min((int64_t)v_rows, (int64_t)(blockIdx.x + 1) * bucket_rows);
+  uint32_t c = 0;
+#pragma unroll 16
+  for (int t = threadIdx.x; t < ntok; t += 256) {   // unrolled: 16 loads in flight
+    const int64_t id = ids[t];
+    c += (id >= lo && id < hi) ? 1u : 0u;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
 __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const int32_t* __restrict__ ids,
                                                                           uint64_t* __restrict__ keys_out,
+                                                                          const uint32_t* __restrict__ counts,
                                                                           int ntok, int64_t v_start,
-                                                                          int v_rows, int tbits, int rbits) {
+                                                                          int v_rows, int tbits, int rbits,
+                                                                          int bucket_rows) {
   __shared__ uint32_t kb[2][kRadixMax];
   __shared__ uint32_t off[kRadixWaves * 256];   // [wave][digit]: a wave's counters are contiguous
   __shared__ uint32_t wsum[kRadixWaves];
+  __shared__ uint32_t out0_s;
   static_assert(256 * kRadixWaves == 4 * kRadixThreads, "scan: four entries per thread");
   __shared__ uint32_t nin_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t tmask = (1u << tbits) - 1u;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int g = blockIdx.x;
+  const int row_lo = counts ? g * bucket_rows : 0;
+  const int row_hi = counts ? min(v_rows, row_lo + bucket_rows) : v_rows;
   {
-    // all id loads in flight at once; then, block of kRadixThreads tokens by
-    // block, the in-range keys are appended in token order: a lane's place
-    // is the in-range lanes before it in its wave plus the earlier waves'
-    // totals
+    // output position of this bucket's first key: the earlier buckets' counts
+    uint32_t c = (counts && tid < g) ? counts[tid] : 0u;   // g < gridDim.x <= kRadixThreads
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) wsum[wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t t = 0;
+      for (int w = 0; w < kRadixWaves; ++w) t += wsum[w];
+      out0_s = t;
+    }
+    __syncthreads();
+  }
+  const uint32_t out0 = out0_s;
+  {
+    // every wave compacts its own run of 64 * PER consecutive tokens: all id
+    // loads in flight at once, the in-range lanes counted per chunk of 64 by
+    // ballot, one barrier for the runs' totals, then the keys are written in
+    // token order at the earlier runs' total plus the in-range lanes before
+    // them
     constexpr int PER = kRadixMax / kRadixThreads;
+    const int tb = wave * 64 * PER;
     int32_t idv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int t = tid + i * kRadixThreads;
+      const int t = tb + i * 64 + lane;
       idv[i] = t < ntok ? ids[t] : 0;
     }
-    uint32_t base = 0;   // keys appended by earlier blocks (same value in every thread)
+    uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int t = tid + i * kRadixThreads;
+      const int t = tb + i * 64 + lane;
       const int64_t local = (int64_t)idv[i] - v_start;
-      const bool in = t < ntok && local >= 0 && local < v_rows;
-      const uint64_t bal = __ballot(in);
-      if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
-      __syncthreads();
-      uint32_t before = 0, all = 0;
-#pragma unroll
-      for (int w = 0; w < kRadixWaves; ++w) {
-        const uint32_t c = wsum[w];
-        before += w < wave ? c : 0u;
-        all += c;
-      }
-      if (in) kb[0][base + before + (uint32_t)__popcll(bal & lt_mask)] = ((uint32_t)local << tbits) | (uint32_t)t;
-      base += all;
-      __syncthreads();   // wsum is rewritten by the next block
+      cnt += (uint32_t)__popcll(__ballot(t < ntok && local >= row_lo && local < row_hi));
     }
-    if (tid == 0) nin_s = base;
+    if (lane == 0) wsum[wave] = cnt;
+    __syncthreads();
+    uint32_t pos = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kRadixWaves; ++w) {
+      const uint32_t c = wsum[w];
+      pos += w < wave ? c : 0u;
+      all += c;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = tb + i * 64 + lane;
+      const int64_t local = (int64_t)idv[i] - v_start;
+      const bool in = t < ntok && local >= row_lo && local < row_hi;
+      const uint64_t bal = __ballot(in);
+      if (in) kb[0][pos + (uint32_t)__popcll(bal & lt_mask)] = ((uint32_t)(local - row_lo) << tbits) | (uint32_t)t;
+      pos += (uint32_t)__popcll(bal);
+    }
+    if (tid == 0) nin_s = all;
   }
   __syncthreads();
   const int nin = (int)nin_s;
@@ -230,14 +283,13 @@ __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const i
     cur ^= 1;
     __syncthreads();
   }
-  for (int t = tid; t < ntok; t += kRadixThreads) {
-    if (t < nin) {
-      const uint32_t key = kb[cur][t];
-      keys_out[t] = ((uint64_t)(key >> tbits) << 32) | (uint64_t)(key & tmask);
-    } else {
-      keys_out[t] = kNoKey;
-    }
+  for (int i = tid; i < nin; i += kRadixThreads) {
+    const uint32_t key = kb[cur][i];
+    keys_out[out0 + i] = ((uint64_t)((key >> tbits) + (uint32_t)row_lo) << 32) | (uint64_t)(key & tmask);
   }
+  // the last bucket ends at the number of in-range tokens; the rest is kNoKey
+  if (g == (int)gridDim.x - 1)
+    for (int t = (int)out0 + nin + tid; t < ntok; t += kRadixThreads) keys_out[t] = kNoKey;
 }
 
 __global__ void __launch_bounds__(256) bitonic_global_kernel(uint64_t* keys, int64_t n, int64_t k, int64_t j) {
@@ -384,10 +436,14 @@ extern "C" tps_status vocab_embed_fwd(tps_dtype dt, int64_t T, int64_t H, int64_
   return check_launch("embed_fwd_kernel");
 }
 
+// Row buckets of the sort: up to kRadixBuckets workgroups of at most 256 rows.
+constexpr int kRadixBuckets = 256;
+
 extern "C" size_t vocab_embed_bwd_workspace(int64_t T, int64_t v_rows) {
   (void)v_rows;
   if (T <= 0) return 0;
-  return (size_t)next_pow2(T) * sizeof(uint64_t);
+  // sort keys, then the bucket counts
+  return (size_t)next_pow2(T) * sizeof(uint64_t) + kRadixBuckets * sizeof(uint32_t);
 }
 
 extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
@@ -406,9 +462,21 @@ extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint64_t* keys = static_cast<uint64_t*>(ws);
   const int tbits = ceil_log2(T), rbits = ceil_log2(v_rows + 1);
-  if (T <= kRadixMax && tbits + rbits <= 32) {
-    hipLaunchKernelGGL(embed_radix_sort_kernel, dim3(1), dim3(kRadixThreads), 0, st, ids, keys, (int)T, v_start,
-                       (int)v_rows, tbits, rbits);
+  if (T <= kRadixMax && tbits + 8 <= 32 && v_rows <= 256LL * kRadixBuckets) {
+    // one workgroup per bucket of at most 256 rows: one 8-bit pass each
+    const int brows = (int)ceil_div(v_rows, kRadixBuckets);
+    const int nb = (int)ceil_div(v_rows, brows);
+    uint32_t* counts = reinterpret_cast<uint32_t*>(keys + next_pow2(T));
+    hipLaunchKernelGGL(embed_bucket_count_kernel, dim3((unsigned)nb), dim3(256), 0, st, ids, counts, (int)T, v_start,
+                       (int)v_rows, brows);
+    s = check_launch("embed_bucket_count_kernel");
+    if (s != TPS_OK) return s;
+    hipLaunchKernelGGL(embed_radix_sort_kernel, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ids, keys,
+                       (const uint32_t*)counts, (int)T, v_start, (int)v_rows, tbits, ceil_log2(brows), brows);
+    s = check_launch("embed_radix_sort_kernel");
+  } else if (T <= kRadixMax && tbits + rbits <= 32) {
+    hipLaunchKernelGGL(embed_radix_sort_kernel, dim3(1), dim3(kRadixThreads), 0, st, ids, keys,
+                       (const uint32_t*)nullptr, (int)T, v_start, (int)v_rows, tbits, rbits, (int)v_rows);
     s = check_launch("embed_radix_sort_kernel");
   } else {
     const int64_t npad = next_pow2(T);
