@@ -218,12 +218,13 @@ def cpu_baseline():
                       f"{flops / 1e9:.1f} GFLOP in {t:.2f} s", "seconds": round(t, 2)}
 
 
-# HBM traffic of the roofline kernel from two rocprofv3 --pmc passes
-# (FETCH_SIZE, WRITE_SIZE) over `bench.py --steps 2 --warmup 1 --no-cpu
-# --no-embed --no-layer`, divided by what the same counters read for a plain
-# copy (shard_reduce with one part over 512 MiB) per byte moved.  Valid only
-# for the GEMM source it was taken on (sha256 prefix below); otherwise null.
-ROOFLINE_TRAFFIC = {"gemm_sha": "225e482dd4bc6067", "bytes_per_launch": 827550703}
+# HBM traffic of one tied_logits call (both of its GEMM launches) from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over `bench.py --steps 2
+# --warmup 1 --no-cpu --no-embed --no-layer --calib`, divided by what the same
+# counters read for a plain copy (shard_reduce with one part over 512 MiB) per
+# byte moved.  Valid only for the GEMM source it was taken on (sha256 prefix
+# below); otherwise null.
+ROOFLINE_TRAFFIC = {"gemm_sha": "384f6bc0df6eba9f", "bytes_per_launch": 792193341}
 
 
 def _gemm_sha():
