@@ -253,6 +253,20 @@ tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype dx_dt, int64
                          const void* dy, void* dx, float* dgamma, float* dbeta, void* ws,
                          size_t ws_bytes, tps_stream_t stream);
 
+/*
+ * layernorm_bwd_residual: the same backward pass for a pre-LN sublayer whose
+ * residual connection also carries gradient: out = res + dL/dx, res and out
+ * fp32 [M x H] (out must not alias res); out_copy (bf16 [M x H], may be
+ * null) receives out rounded once, for the next GEMMs.  dgamma, dbeta and
+ * the workspace as for layernorm_bwd.  Equivalent to layernorm_bwd into a
+ * temporary followed by the elementwise add, without the temporary.
+ */
+tps_status layernorm_bwd_residual(tps_dtype x_dt, tps_dtype dy_dt, int64_t M, int64_t H,
+                                  const void* x, const float* gamma, const float* mean,
+                                  const float* rstd, const void* dy, const float* res, float* out,
+                                  void* out_copy, float* dgamma, float* dbeta, void* ws,
+                                  size_t ws_bytes, tps_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ SIGNATURES = {
     "layernorm_bwd_workspace": (_sz, [_i64, _i64]),
     "layernorm_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
+    "layernorm_bwd_residual": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]),
 }
 
 
@@ -306,3 +308,18 @@ def layernorm_bwd(x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws, stream=None):
     _check(lib.layernorm_bwd(_dt(x), _dt(dy), _dt(dx), M, H, _p(x), _p(gamma), _p(mean), _p(rstd), _p(dy), _p(dx),
                              _p(dgamma), _p(dbeta), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "layernorm_bwd")
+
+
+def layernorm_bwd_residual(x, gamma, mean, rstd, dy, res, out, dgamma, dbeta, ws, out_copy=None, stream=None):
+    """out = res + (LayerNorm gradient), fp32; x and dy fp32 or bf16; optional bf16 copy of out."""
+    _contig(x, gamma, mean, rstd, dy, res, out, dgamma, dbeta, ws)
+    M, H = x.shape
+    assert dy.shape == (M, H) and res.shape == (M, H) and out.shape == (M, H)
+    assert res.dtype == torch.float32 and out.dtype == torch.float32
+    if out_copy is not None:
+        _contig(out_copy)
+        assert out_copy.shape == (M, H) and out_copy.dtype == torch.bfloat16
+    _check(lib.layernorm_bwd_residual(_dt(x), _dt(dy), M, H, _p(x), _p(gamma), _p(mean), _p(rstd), _p(dy), _p(res),
+                                      _p(out), _p(out_copy), _p(dgamma),
+                                      _p(dbeta), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "layernorm_bwd_residual")

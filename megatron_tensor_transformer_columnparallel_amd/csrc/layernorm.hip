@@ -101,11 +101,15 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const TX* __restrict__ x, c
   if (threadIdx.x == 0) { mean[row] = mu; rstd[row] = rs; }
 }
 
-template <typename TX, typename TDY, typename TDX>
+// RES: dx = res + (the LayerNorm gradient), and a bf16 copy of dx when
+// `copy` is not null (the residual connection's gradient, added where the
+// row is in registers).
+template <bool RES, typename TX, typename TDY, typename TDX>
 __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
                                                      const TDY* __restrict__ dy, TDX* __restrict__ dx,
-                                                     float* __restrict__ part, int64_t M, int64_t H) {
+                                                     float* __restrict__ part, int64_t M, int64_t H,
+                                                     const float* __restrict__ res, bf16_t* __restrict__ copy) {
   constexpr int V = kLnV;
   constexpr int NCH = kLnNCH;
   __shared__ float red[8];
@@ -148,6 +152,13 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
         float o[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) o[e] = rs * (gv[i][e] - m1 - xh[i][e] * m2);
+        if constexpr (RES) {
+          float rv[V];
+          LnVec<float>::load(res + row * H + c, rv);
+#pragma unroll
+          for (int e = 0; e < V; ++e) o[e] += rv[e];
+          if (copy) LnVec<bf16_t>::store(copy + row * H + c, o);
+        }
         LnVec<TDX>::store(dx + row * H + c, o);
       }
     }
@@ -174,13 +185,15 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const TX* __restrict__ x, c
 // row.  Same partial-sum layout as ln_bwd_kernel.
 constexpr int kLnBwdThreads = 512;
 
-template <int NCH, typename TX, typename TDY, typename TDX>
+template <int NCH, bool RES, typename TX, typename TDY, typename TDX>
 __global__ void __launch_bounds__(kLnBwdThreads) ln_bwd_rows_kernel(const TX* __restrict__ x,
                                                                     const float* __restrict__ gamma,
                                                                     const float* __restrict__ mean,
                                                                     const float* __restrict__ rstd,
                                                                     const TDY* __restrict__ dy, TDX* __restrict__ dx,
-                                                                    float* __restrict__ part, int64_t M) {
+                                                                    float* __restrict__ part, int64_t M,
+                                                                    const float* __restrict__ res,
+                                                                    bf16_t* __restrict__ copy) {
   constexpr int V = kLnV;
   constexpr int NW = kLnBwdThreads / 64;
   constexpr int64_t H = (int64_t)NCH * kLnBwdThreads * V;
@@ -207,6 +220,13 @@ __global__ void __launch_bounds__(kLnBwdThreads) ln_bwd_rows_kernel(const TX* __
   // One row: sums, the shared row means, dx, and the dgamma/dbeta partials.
   auto row_pass = [&](int rr, const float (&xv)[NCH][V], const float (&dv)[NCH][V]) {
     const int64_t row = r0 + rr;
+    // the residual gradient's row is loaded first: its latency hides behind the row sums
+    float rv[NCH][V];
+    if constexpr (RES) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        LnVec<float>::load(res + row * H + ((int64_t)i * kLnBwdThreads + threadIdx.x) * V, rv[i]);
+    }
     const float mu = mean[row], rs = rstd[row];
     float xh[NCH][V], gv[NCH][V];
     float s1 = 0.f, s2 = 0.f;
@@ -241,6 +261,11 @@ __global__ void __launch_bounds__(kLnBwdThreads) ln_bwd_rows_kernel(const TX* __
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = rs * (gv[i][e] - m1 - xh[i][e] * m2);
+      if constexpr (RES) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] += rv[i][e];
+        if (copy) LnVec<bf16_t>::store(copy + row * H + c, o);
+      }
       LnVec<TDX>::store(dx + row * H + c, o);
     }
   };
@@ -330,20 +355,20 @@ static void launch_ln_fwd(int64_t M, int64_t H, float eps, const void* x, const 
                      static_cast<TY*>(y), mean, rstd, H, eps);
 }
 
-template <typename TX, typename TDY, typename TDX>
+template <bool RES, typename TX, typename TDY, typename TDX>
 static void launch_ln_bwd(int64_t M, int64_t H, const void* x, const float* g, const float* mean, const float* rstd,
-                          const void* dy, void* dx, float* part, hipStream_t st) {
+                          const void* dy, void* dx, float* part, const float* res, bf16_t* copy, hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(M, kLnRowsPerBlock));
   const TX* xp = static_cast<const TX*>(x);
   const TDY* dyp = static_cast<const TDY*>(dy);
   TDX* dxp = static_cast<TDX*>(dx);
   constexpr int64_t W1 = (int64_t)kLnBwdThreads * kLnV;   // 4096
   if (H == W1)
-    hipLaunchKernelGGL((ln_bwd_rows_kernel<1, TX, TDY, TDX>), grid, dim3(kLnBwdThreads), 0, st, xp, g, mean, rstd,
-                       dyp, dxp, part, M);
+    hipLaunchKernelGGL((ln_bwd_rows_kernel<1, RES, TX, TDY, TDX>), grid, dim3(kLnBwdThreads), 0, st, xp, g, mean,
+                       rstd, dyp, dxp, part, M, res, copy);
   else
-    hipLaunchKernelGGL((ln_bwd_kernel<TX, TDY, TDX>), grid, dim3(256), 0, st, xp, g, mean, rstd, dyp, dxp, part, M,
-                       H);
+    hipLaunchKernelGGL((ln_bwd_kernel<RES, TX, TDY, TDX>), grid, dim3(256), 0, st, xp, g, mean, rstd, dyp, dxp, part,
+                       M, H, res, copy);
 }
 
 }  // namespace tps
@@ -381,14 +406,45 @@ extern "C" tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype d
   float* part = static_cast<float*>(ws);
   const int k = (x_dt == TPS_BF16 ? 4 : 0) | (dy_dt == TPS_BF16 ? 2 : 0) | (dx_dt == TPS_BF16 ? 1 : 0);
   switch (k) {
-    case 7: launch_ln_bwd<bf16_t, bf16_t, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    case 6: launch_ln_bwd<bf16_t, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    case 5: launch_ln_bwd<bf16_t, float, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    case 4: launch_ln_bwd<bf16_t, float, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    case 3: launch_ln_bwd<float, bf16_t, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    case 2: launch_ln_bwd<float, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    case 1: launch_ln_bwd<float, float, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
-    default: launch_ln_bwd<float, float, float>(M, H, x, gamma, mean, rstd, dy, dx, part, st); break;
+    case 7: launch_ln_bwd<false, bf16_t, bf16_t, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    case 6: launch_ln_bwd<false, bf16_t, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    case 5: launch_ln_bwd<false, bf16_t, float, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    case 4: launch_ln_bwd<false, bf16_t, float, float>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    case 3: launch_ln_bwd<false, float, bf16_t, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    case 2: launch_ln_bwd<false, float, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    case 1: launch_ln_bwd<false, float, float, bf16_t>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+    default: launch_ln_bwd<false, float, float, float>(M, H, x, gamma, mean, rstd, dy, dx, part, nullptr, nullptr, st); break;
+  }
+  s = check_launch("ln_bwd_kernel");
+  if (s != TPS_OK) return s;
+  const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
+  hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(2 * H, 32)), dim3(256), 0, st, part, dgamma,
+                     dbeta, nblk, H);
+  return check_launch("ln_param_reduce_kernel");
+}
+
+extern "C" tps_status layernorm_bwd_residual(tps_dtype x_dt, tps_dtype dy_dt, int64_t M, int64_t H, const void* x,
+                                             const float* gamma, const float* mean, const float* rstd,
+                                             const void* dy, const float* res, float* out, void* out_copy,
+                                             float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
+                                             tps_stream_t stream) {
+  tps_status s = ln_checks("layernorm_bwd_residual", {x_dt, dy_dt}, M, H,
+                           {x, gamma, mean, rstd, dy, res, out, dgamma, dbeta, ws});
+  if (s != TPS_OK) return s;
+  if (out_copy && !aligned16(out_copy))
+    return set_error(TPS_EINVAL, "layernorm_bwd_residual: out_copy not 16-byte aligned");
+  if ((const void*)res == (const void*)out) return set_error(TPS_EINVAL, "layernorm_bwd_residual: out must not alias res");
+  if (ws_bytes < layernorm_bwd_workspace(M, H))
+    return set_error(TPS_EWORKSPACE, "layernorm_bwd_residual: workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(ws);
+  bf16_t* copy = static_cast<bf16_t*>(out_copy);
+  const int k = (x_dt == TPS_BF16 ? 2 : 0) | (dy_dt == TPS_BF16 ? 1 : 0);
+  switch (k) {
+    case 3: launch_ln_bwd<true, bf16_t, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, out, part, res, copy, st); break;
+    case 2: launch_ln_bwd<true, bf16_t, float, float>(M, H, x, gamma, mean, rstd, dy, out, part, res, copy, st); break;
+    case 1: launch_ln_bwd<true, float, bf16_t, float>(M, H, x, gamma, mean, rstd, dy, out, part, res, copy, st); break;
+    default: launch_ln_bwd<true, float, float, float>(M, H, x, gamma, mean, rstd, dy, out, part, res, copy, st); break;
   }
   s = check_launch("ln_bwd_kernel");
   if (s != TPS_OK) return s;

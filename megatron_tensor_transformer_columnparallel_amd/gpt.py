@@ -117,7 +117,6 @@ class TPGPT:
         self.dx, self.dx2 = _emp((M, H), f32), _emp((M, H), f32)          # residual gradient (fp32)
         self.dx_bf, self.dx2_bf = _emp((M, H)), _emp((M, H))               # its bf16 copies (GEMM inputs)
         self.dy = _emp((M, H), f32)
-        self.dln = _emp((M, H), f32)
         self.dparts = [_emp((M, H)) for _ in range(c.n)]
         self.ws_mlp = _emp((tp.tp_mlp_bwd_workspace(torch.bfloat16, M, H, self.fi),), torch.uint8)
         # one scratch buffer serves the attention forward and backward calls
@@ -177,13 +176,13 @@ class TPGPT:
                 tp.tp_mlp_bwd(a["y2"], p["A"], p["B"], sa["P"], sa["H"], self.dx_bf, dp, gs["A"], gs["B"],
                               self.ws_mlp)
             tp.shard_reduce(self.dparts, self.dy)                                    # f backward
-            tp.layernorm_bwd(a["x2"], lw["g2"], a["m2"], a["r2"], self.dy, self.dln, g["g2"], g["b2"], self.ws_ln)
-            tp.shard_reduce_add(self.dx, [self.dln], self.dx2, self.dx2_bf)          # residual
+            tp.layernorm_bwd_residual(a["x2"], lw["g2"], a["m2"], a["r2"], self.dy, self.dx, self.dx2,
+                                      g["g2"], g["b2"], self.ws_ln, out_copy=self.dx2_bf)   # + residual
             for p, sa, gs, dp in zip(lw["sh"], a["sh"], g["sh"], self.dparts):
                 tp.tp_attn_bwd(a["y1"], p["Wqkv"], p["Wo"], sa["QKV"], sa["O"], sa["lse"], self.dx2_bf, dp,
                                gs["Wqkv"], gs["Wo"], self.ws_attn, cf.b, cf.s, self.hs, cf.d, True)
             tp.shard_reduce(self.dparts, self.dy)                                    # f backward
-            tp.layernorm_bwd(x_in, lw["g1"], a["m1"], a["r1"], self.dy, self.dln, g["g1"], g["b1"], self.ws_ln)
-            tp.shard_reduce_add(self.dx2, [self.dln], self.dx, self.dx_bf)           # residual
+            tp.layernorm_bwd_residual(x_in, lw["g1"], a["m1"], a["r1"], self.dy, self.dx2, self.dx,
+                                      g["g1"], g["b1"], self.ws_ln, out_copy=self.dx_bf)    # + residual
         for r, (s, _) in enumerate(self.vr):
             tp.vocab_embed_bwd(ids, self.dx, self.dE[r], s, self.ws_emb)            # tied: adds input side

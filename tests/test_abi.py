@@ -128,3 +128,21 @@ def test_workspace_queries_and_too_small_workspace(tp):
 def test_attention_fp32_is_reported_unsupported(tp):
     st = tp.lib.tp_attn_fwd(0, 1, 16, 64, 2, 64, 1, *([ALIGNED] * 8), 1 << 30, None)
     assert st == tp.binding.TPS_EUNSUPPORTED
+
+
+def test_layernorm_bwd_residual_validation(tp):
+    lib = tp.lib
+    need = lib.layernorm_bwd_workspace(64, 4096)
+    args = [ALIGNED] * 5   # x, gamma, mean, rstd, dy
+    # out aliasing res is rejected before anything is enqueued
+    st = lib.layernorm_bwd_residual(0, 0, 64, 4096, *args, ALIGNED + 64, ALIGNED + 64, None, ALIGNED, ALIGNED,
+                                    ALIGNED, need, None)
+    assert st == tp.binding.TPS_EINVAL
+    # too small a workspace
+    st = lib.layernorm_bwd_residual(0, 0, 64, 4096, *args, ALIGNED, ALIGNED + 64, None, ALIGNED, ALIGNED,
+                                    ALIGNED, need - 1, None)
+    assert st == tp.binding.TPS_EWORKSPACE
+    # misaligned copy
+    st = lib.layernorm_bwd_residual(0, 0, 64, 4096, *args, ALIGNED, ALIGNED + 64, ALIGNED + 2, ALIGNED, ALIGNED,
+                                    ALIGNED, need, None)
+    assert st == tp.binding.TPS_EINVAL

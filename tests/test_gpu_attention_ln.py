@@ -119,3 +119,32 @@ def test_layernorm_matches_oracle(tp, M, H, dt, ydt):
     assert rel_err(to_f64(dx), dx_ref) <= tol
     assert rel_err(to_f64(dgam), dg_ref) <= (F32_TOL if tol == F32_TOL else 1e-3)
     assert rel_err(to_f64(dbet), db_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("M,H,dt,copy", [(2048, 4096, "f32", True), (300, 4096, "bf16", True), (13, 4096, "f32", False),
+                                         (37, 136, "f32", True)])
+def test_layernorm_bwd_residual_matches_oracle(tp, M, H, dt, copy):
+    """out = res + LayerNorm gradient (fp32), optional bf16 copy; x and dy of dtype dt."""
+    say(f"layernorm_bwd_residual M={M} H={H} x,dy {dt} copy={copy}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    x = synth.make(79, 0, (M, H), 2.0, dt)
+    dy = synth.make(79, 1, (M, H), 1.0, dt)
+    res = synth.make(79, 2, (M, H), 1.0, "f32")
+    g = synth.Tensor(1.0 + 0.1 * synth.normal(79, 3, (H,)), "f32")
+    bt = synth.Tensor(0.1 * synth.normal(79, 4, (H,)), "f32")
+    y, mean, rstd = empty((M, H), tdt), empty((M,), torch.float32), empty((M,), torch.float32)
+    dx_in, dg = to_dev(x), to_dev(g)
+    tp.layernorm_fwd(dx_in, dg, to_dev(bt), y, mean, rstd, 1e-5)
+    _, mu_ref, rs_ref = O.layernorm_forward(x.f64, g.f64, bt.f64, 1e-5)
+    out, dgam, dbet = empty((M, H), torch.float32), empty((H,), torch.float32), empty((H,), torch.float32)
+    cp = empty((M, H), torch.bfloat16) if copy else None
+    ws = workspace(tp.layernorm_bwd_workspace(M, H))
+    tp.layernorm_bwd_residual(dx_in, dg, mean, rstd, to_dev(dy), to_dev(res), out, dgam, dbet, ws, out_copy=cp)
+    dx_ref, dg_ref, db_ref = O.layernorm_backward(x.f64, g.f64, mu_ref, rs_ref, dy.f64)
+    ref = res.f64 + dx_ref
+    tol = BF16_TOL if dt == "bf16" else F32_TOL
+    assert rel_err(to_f64(out), ref) <= tol
+    assert rel_err(to_f64(dgam), dg_ref) <= (F32_TOL if tol == F32_TOL else 1e-3)
+    assert rel_err(to_f64(dbet), db_ref) <= 1e-5
+    if copy:   # the copy is the fp32 output rounded once (round to nearest even)
+        assert np.array_equal(raw_bits(cp), synth.to_bf16_bits(out.cpu().numpy()))

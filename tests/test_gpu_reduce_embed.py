@@ -208,3 +208,19 @@ def test_embed_bwd_sort_sizes(tp, T):
     got = to_f64(dE)
     untouched = np.all(ref == 0, axis=1)
     assert np.all(got[untouched] == 0)
+
+
+def test_embed_bwd_wide_shard_single_sort(tp):
+    """More than 65536 rows per shard: the one-workgroup sort over every row (17 row bits)."""
+    say("vocab_embed_bwd v_rows=70000 T=3000")
+    T, H, V = 3000, 16, 140000
+    g = synth.rng(98, 0)
+    ids = g.integers(-10, V + 10, T).astype(np.int32)
+    ids[:40] = 69999          # last row of shard 0, repeated
+    ids[40:70] = 70000        # first row of shard 1
+    dY = synth.make(98, 1, (T, H), 1.0, "bf16")
+    for r in range(2):
+        s, c = O.partition(V, 2, r)
+        dE = _embed_bwd(tp, ids, dY, s, c, H)
+        ref = O.vocab_embed_backward(ids, dY.f64, s, c)
+        assert rel_err(to_f64(dE), ref) <= 1e-5
