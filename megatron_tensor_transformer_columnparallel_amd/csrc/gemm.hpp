@@ -9,6 +9,8 @@
 // fp32 path: LDS-tiled SIMT kernel (4x4 outputs per thread), same epilogues.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tps {
@@ -309,21 +311,24 @@ struct OperandLoader {
   // reads of the other stages (it would otherwise wait for them before every
   // fragment read); completion is awaited explicitly with a vmcnt wait before
   // the barrier that publishes the stage.
-  __device__ __forceinline__ void issue_direct(bf16_t* region, int wave) {
-    // readfirstlane yields a signed int: each half goes through uint32_t so
-    // that the low half is zero-extended, not sign-extended, into 64 bits.
+  // Wave-uniform copy of `base` for the scalar operand of the DMA.
+  // readfirstlane yields a signed int: each half goes through uint32_t so
+  // that the low half is zero-extended, not sign-extended, into 64 bits.
+  __device__ __forceinline__ uint64_t sbase() const {
     const uint64_t b = (uint64_t)(uintptr_t)base;
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-#pragma unroll
-    for (int i = 0; i < VECS; ++i) {
-      const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(region + (i * NT + wave * 64) * 8);
-      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                   :: "v"(slot_off(i)), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
-    }
-    base += kstep;
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
   }
+  // Slot i of every lane of the wave: 64 lanes x 16 bytes into LDS at byte
+  // address `m0` (wave-uniform: the region's slots of this wave, i*NT*16
+  // bytes further per slot).  M0 is written one wait state ahead of the DMA
+  // that reads it.
+  __device__ __forceinline__ void issue_one(int i, uint64_t sb, uint32_t m0_wave) const {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(slot_off(i)), "s"(sb), "s"(m0_wave + (uint32_t)(i * NT * 16)) : "memory", "m0");
+  }
+  __device__ __forceinline__ void advance() { base += kstep; }
 
   // Ragged last K tile: r_rem rows (m/n) and k_rem k remain from the tile
   // origin; k outside is zero (m/n outside only reaches dropped outputs).
@@ -533,11 +538,6 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   };
-  auto issue = [&](int /*kt*/, int stage) {   // K tiles are issued in order
-    bf16_t* st = lds + stage * STAGE;
-    la.issue_direct(st, wave);
-    lb.issue_direct(st + BM * BK, wave);
-  };
   auto load_checked = [&](int kt) {
     const int k_rem = s.K - kb - kt * BK;
     la.load_checked(m_rem, k_rem, tid);
@@ -548,44 +548,99 @@ gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, Gem
     lb.store(st + BM * BK, tid);
   };
 
+  // LDS byte address of this wave's DMA slots in stage 0 (wave-uniform).
+  const uint32_t lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)((uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)lds + (uint32_t)wave * 1024u));
+  constexpr int VA = LoaderA::VECS;
+  constexpr int VPT = VA + LoaderB::VECS;   // DMA instructions per wave per K tile
+  // DMA instruction d of the K tile bound for `stage` (A slots, then B).
+  auto dma_one = [&](int d, int stage, uint64_t sa, uint64_t sb) {
+    const uint32_t m0 = lds_wave + (uint32_t)(stage * STAGE * 2);
+    if (d < VA) la.issue_one(d, sa, m0);
+    else lb.issue_one(d - VA, sb, m0 + (uint32_t)(BM * BK * 2));
+  };
+  auto issue = [&](int stage) {   // K tiles are issued in order
+    const uint64_t sa = la.sbase(), sb = lb.sbase();
+#pragma unroll
+    for (int d = 0; d < VPT; ++d) dma_one(d, stage, sa, sb);
+    la.advance();
+    lb.advance();
+  };
+  auto read_one = [&](const bf16_t* st, int ks, Frags& f, int r) {
+    if (r < FN) f.b[r] = fb.read(st + BM * BK, ks, r);
+    else f.a[r - FN] = fa.read(st, ks, r - FN);
+  };
+  // The MFMAs of one k-step with the FM + FN fragment reads of the next
+  // k-step spread evenly between them and, with `dma`, the DMA instructions
+  // of the K tile bound for `dstage` one after each of the first MFMAs: no
+  // wave issues a burst of memory instructions while its matrix unit idles,
+  // and the LDS command queue sees a steady stream instead of one burst per
+  // wave.
+  auto mfma_mix = [&](const Frags& f, const bf16_t* nst, int nks, Frags& nf, auto dma, int dstage) {
+    constexpr bool DMA = decltype(dma)::value;
+    constexpr int NM = FM * FN, NR = FM + FN;
+    uint64_t sa = 0, sb = 0;
+    if constexpr (DMA) {
+      sa = la.sbase();
+      sb = lb.sbase();
+    }
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const int i = t / FN, j = t % FN;
+      // operands swapped: the result's lane layout is C(m = lane & 15, n = 4*(lane >> 4) + e)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+      if constexpr (DMA) {
+        if (t < VPT) dma_one(t, dstage, sa, sb);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+        if ((r * NM) / NR == t) read_one(nst, nks, nf, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DMA) {
+#pragma unroll
+      for (int d = NM; d < VPT; ++d) dma_one(d, dstage, sa, sb);
+      la.advance();
+      lb.advance();
+    }
+  };
+
   {
-    // Every full K tile goes global -> LDS directly, up to NS
-    // of them in flight.  Fragments are double-buffered by k-step: the LDS
-    // reads of the next k-step are issued before the MFMAs of the current
-    // one, and the barrier that publishes tile kt+1 (and frees tile kt's
-    // stage for tile kt+NS) sits before the MFMAs of tile kt's last k-step,
-    // so those MFMAs overlap the first reads of tile kt+1.  No other
-    // vector-memory operation is issued in this loop, so the vmcnt count is
-    // exactly the DMA instructions of the tiles after kt+1.
+    // Every full K tile goes global -> LDS directly, up to NS of them in
+    // flight.  Fragments are double-buffered by k-step: the LDS reads of the
+    // next k-step go out between the MFMAs of the current one, and the
+    // barrier that publishes tile kt+1 (and frees tile kt's stage for tile
+    // kt+NS) sits before the MFMAs of tile kt's last k-step, so those MFMAs
+    // overlap the first reads of tile kt+1 and the DMA of tile kt+NS.  No
+    // other vector-memory operation is issued in this loop, so the vmcnt
+    // count is exactly the DMA instructions of the tiles after kt+1.  The
+    // barrier also waits for every LDS read of the wave, so the fragments of
+    // tile kt's last k-step are complete when their MFMAs start.
     static_assert(KS == 2, "the pipelined loop pairs the two k-steps of a 64-wide K tile");
-    constexpr int VPT = LoaderA::VECS + LoaderB::VECS;   // DMA instructions per wave per K tile
     if (nkd > 0) {
       const int pre = min(NS, nkd);
-      for (int p = 0; p < pre; ++p) issue(p, p);
+      for (int p = 0; p < pre; ++p) issue(p);
       if (nkd >= NS) wait_vmem_n<(NS - 1) * VPT>();   // tile 0 landed
       else wait_vmem();
       __syncthreads();
       Frags f0, f1;
       read_frags(lds, 0, f0);
       int cs = 0;   // stage of tile kt (tile j lives in stage j % NS)
-      for (int kt = 0; kt < nkd; ++kt) {
-        read_frags(lds + cs * STAGE, 1, f1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_frags(f0);
-        __builtin_amdgcn_sched_barrier(0);
+      int kt = 0;
+      auto step = [&](auto dma) {
+        mfma_mix(f0, lds + cs * STAGE, 1, f1, std::false_type{}, 0);
         const int nx = (cs + 1 == NS) ? 0 : cs + 1;
-        if (kt + 1 < nkd) {
-          if (kt + NS <= nkd) wait_vmem_n<(NS - 2) * VPT>();   // tile kt+1 landed
-          else wait_vmem();
-          __syncthreads();   // tile kt+1 visible; every wave has read all of tile kt
-          if (kt + NS < nkd) issue(kt + NS, cs);
-          read_frags(lds + nx * STAGE, 0, f0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_frags(f1);
-        __builtin_amdgcn_sched_barrier(0);
+        if (kt + NS <= nkd) wait_vmem_n<(NS - 2) * VPT>();   // tile kt+1 landed
+        else wait_vmem();
+        __syncthreads();   // tile kt+1 visible; every wave has read all of tile kt
+        mfma_mix(f1, lds + nx * STAGE, 0, f0, dma, cs);   // tile kt+NS goes to stage cs
         cs = nx;
-      }
+      };
+      for (; kt + NS < nkd; ++kt) step(std::true_type{});
+      for (; kt + 1 < nkd; ++kt) step(std::false_type{});
+      mfma_mix(f0, lds + cs * STAGE, 1, f1, std::false_type{}, 0);   // the last tile
+      mfma_frags(f1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (nk > nkd) {
       // the stage after the last direct tile: its last reader (tile nkd-NS)
