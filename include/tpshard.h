@@ -198,7 +198,7 @@ tps_status vocab_embed_fwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, 
                            const int32_t* ids, const void* E_r, void* Y_r, tps_stream_t stream);
 
 /* Workspace of vocab_embed_bwd: the sort keys (8 bytes per token, T rounded
- * up to a power of two) and 256 row-bucket counts (4 bytes each). */
+ * up to a power of two). */
 size_t vocab_embed_bwd_workspace(int64_t T, int64_t v_rows);
 
 /*

@@ -7,8 +7,9 @@
 //
 // Backward (vocab_embed_bwd): dE_r[id - v_start] += dY[t] for in-range t.
 // Deterministic and free of atomics: the composite keys (local_row << 32 | t)
-// are unique, so sorting them (bitonic network) yields one fixed order, with
-// each row's tokens contiguous and ascending in t.  One wavefront per segment
+// are unique, so sorting them (a radix sort per bucket of rows, or a bitonic
+// network past 16384 tokens) yields one fixed order, with each row's tokens
+// contiguous and ascending in t.  One wavefront per segment
 // head then adds that row's dY rows, in that order, to the row of dE_r in
 // fp32 with a plain read-modify-write (each row has exactly one owner).
 #include "common.hpp"
@@ -95,15 +96,15 @@ __global__ void __launch_bounds__(1024) bitonic_local_kernel(uint64_t* keys, int
 }
 
 // Stable sort by row for T <= kRadixMax tokens, one workgroup per bucket of
-// `bucket_rows` consecutive rows (one bucket holding every row when counts
-// is null).  A bucket's tokens are first compacted, in token order, into
+// `bucket_rows` consecutive rows (a single workgroup when one bucket holds
+// every row).  A bucket's tokens are first compacted, in token order, into
 // 32-bit keys ((row - first row of the bucket) << tbits | t) (out-of-range
 // tokens carry no gradient and only fill the tail of the output with
 // kNoKey), so a stable LSD radix sort on those row bits (8 bits per pass)
 // leaves each row's tokens ascending in t.  The bucket's keys go to the
-// output after those of all earlier buckets (counts[] from
-// embed_bucket_count_kernel), so the buckets together give the same order
-// as one sort of every key.  Per pass, each
+// output after those of all earlier buckets -- the in-range tokens whose row
+// lies below the bucket's, counted in the same pass over the ids -- so the
+// buckets together give the same order as one sort of every key.  Per pass, each
 // of the 16 waves owns a contiguous run of the keys and its own 256 digit
 // counters; lanes with equal digits are found with eight ballots, so a
 // block's count per digit and a lane's rank among earlier lanes with its
@@ -126,59 +127,23 @@ __device__ __forceinline__ uint64_t same_digit_lanes(uint32_t d, bool valid) {
   return same;
 }
 
-// Tokens of each bucket of `bucket_rows` rows (one workgroup per bucket).
-__global__ void __launch_bounds__(256) embed_bucket_count_kernel(const int32_t* __restrict__ ids,
-                                                                 uint32_t* __restrict__ counts, int ntok,
-                                                                 int64_t v_start, int v_rows, int bucket_rows) {
-  __shared__ uint32_t ws[4];
-  const int64_t lo = v_start + (int64_t)blockIdx.x * bucket_rows;
-  const int64_t hi = v_start + min((int64_t)v_rows, (int64_t)(blockIdx.x + 1) * bucket_rows);
-  uint32_t c = 0;
-#pragma unroll 16
-  for (int t = threadIdx.x; t < ntok; t += 256) {   // unrolled: 16 loads in flight
-    const int64_t id = ids[t];
-    c += (id >= lo && id < hi) ? 1u : 0u;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) counts[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
-}
-
 __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const int32_t* __restrict__ ids,
                                                                           uint64_t* __restrict__ keys_out,
-                                                                          const uint32_t* __restrict__ counts,
                                                                           int ntok, int64_t v_start,
                                                                           int v_rows, int tbits, int rbits,
                                                                           int bucket_rows) {
   __shared__ uint32_t kb[2][kRadixMax];
   __shared__ uint32_t off[kRadixWaves * 256];   // [wave][digit]: a wave's counters are contiguous
   __shared__ uint32_t wsum[kRadixWaves];
-  __shared__ uint32_t out0_s;
+  __shared__ uint32_t wbelow[kRadixWaves];
   static_assert(256 * kRadixWaves == 4 * kRadixThreads, "scan: four entries per thread");
-  __shared__ uint32_t nin_s;
+  __shared__ uint32_t nin_s, out0_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t tmask = (1u << tbits) - 1u;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int g = blockIdx.x;
-  const int row_lo = counts ? g * bucket_rows : 0;
-  const int row_hi = counts ? min(v_rows, row_lo + bucket_rows) : v_rows;
-  {
-    // output position of this bucket's first key: the earlier buckets' counts
-    uint32_t c = (counts && tid < g) ? counts[tid] : 0u;   // g < gridDim.x <= kRadixThreads
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
-    if (lane == 0) wsum[wave] = c;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t t = 0;
-      for (int w = 0; w < kRadixWaves; ++w) t += wsum[w];
-      out0_s = t;
-    }
-    __syncthreads();
-  }
-  const uint32_t out0 = out0_s;
+  const int row_lo = g * bucket_rows;
+  const int row_hi = min(v_rows, row_lo + bucket_rows);
   {
     // every wave compacts its own run of 64 * PER consecutive tokens: all id
     // loads in flight at once, the in-range lanes counted per chunk of 64 by
@@ -190,17 +155,23 @@ __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const i
     int32_t idv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      // unconditional loads (clamped index, validity checked below): a
+      // guarded load would be waited for before the next one is issued
       const int t = tb + i * 64 + lane;
-      idv[i] = t < ntok ? ids[t] : 0;
+      idv[i] = ids[min(t, ntok - 1)];
     }
-    uint32_t cnt = 0;
+    uint32_t cnt = 0, below = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int t = tb + i * 64 + lane;
       const int64_t local = (int64_t)idv[i] - v_start;
       cnt += (uint32_t)__popcll(__ballot(t < ntok && local >= row_lo && local < row_hi));
+      below += (uint32_t)__popcll(__ballot(t < ntok && local >= 0 && local < row_lo));
     }
-    if (lane == 0) wsum[wave] = cnt;
+    if (lane == 0) {
+      wsum[wave] = cnt;
+      wbelow[wave] = below;
+    }
     __syncthreads();
     uint32_t pos = 0, all = 0;
 #pragma unroll
@@ -218,10 +189,16 @@ __global__ void __launch_bounds__(kRadixThreads) embed_radix_sort_kernel(const i
       if (in) kb[0][pos + (uint32_t)__popcll(bal & lt_mask)] = ((uint32_t)(local - row_lo) << tbits) | (uint32_t)t;
       pos += (uint32_t)__popcll(bal);
     }
-    if (tid == 0) nin_s = all;
+    if (tid == 0) {
+      uint32_t b0 = 0;
+      for (int w = 0; w < kRadixWaves; ++w) b0 += wbelow[w];
+      nin_s = all;
+      out0_s = b0;   // in-range tokens of the earlier buckets
+    }
   }
   __syncthreads();
   const int nin = (int)nin_s;
+  const uint32_t out0 = out0_s;
   const int per = (nin + kRadixWaves - 1) / kRadixWaves;   // keys per wave
   const int lo = min(nin, wave * per), hi = min(nin, lo + per);
   uint32_t* my = off + wave * 256;
@@ -303,78 +280,125 @@ __global__ void __launch_bounds__(256) bitonic_global_kernel(uint64_t* keys, int
 }
 
 // One wavefront per sorted position; a position that starts a row's segment
-// owns that row.  The wave takes the segment's tokens 64 at a time (one key
-// per lane; the segment ends at the first key of another row -- kNoKey sorts
-// last and matches no row), then, for SL slabs of 64 lanes x VEC columns at a
-// time, starts from the row's current dE (the output-side gradient) and adds
-// the segment's dY rows in increasing token order in fp32.  Token indices
-// are read from the keys' lanes into scalar registers, so no load waits on
-// another; each lane keeps SL x VEC fp32 partial sums.  The finished row is
-// written back with non-temporal stores (each row is written exactly once).
+// owns that row.  The row goes in passes of NSL slabs of 256 columns; lane l
+// holds columns 4l .. 4l+3 of each slab, so every load and store instruction
+// of the wave covers one contiguous span (1 KiB of dE, 512 bytes of bf16 dY).
+// A pass starts from the row's current dE (the output-side gradient) and adds
+// the segment's dY rows in increasing token order in fp32, with the loads of
+// two tokens in flight together.  The segment's tokens come 64 at a time (one
+// key per lane; the segment ends at the first key of another row -- kNoKey
+// sorts last and matches no row) and are read from the keys' lanes into
+// scalar registers.  The finished pass is written back once, with
+// non-temporal stores.
+// 4 consecutive columns of a dY row as loaded (raw; `off` in bytes from the
+// wave-uniform row start) and added into fp32.
+template <typename T> struct AccumLoad;
+template <> struct AccumLoad<bf16_t> {
+  typedef u32x2_t raw;
+  __device__ static raw get(const char* row, uint32_t off) { return *reinterpret_cast<const u32x2_t*>(row + off); }
+  __device__ static void add(float a[4], raw x) {
+    a[0] += bf16lo(x[0]); a[1] += bf16hi(x[0]); a[2] += bf16lo(x[1]); a[3] += bf16hi(x[1]);
+  }
+};
+template <> struct AccumLoad<float> {
+  typedef f32x4_t raw;
+  __device__ static raw get(const char* row, uint32_t off) { return *reinterpret_cast<const f32x4_t*>(row + off); }
+  __device__ static void add(float a[4], raw x) { a[0] += x[0]; a[1] += x[1]; a[2] += x[2]; a[3] += x[3]; }
+};
+
 template <typename T>
 __global__ void __launch_bounds__(256) embed_bwd_accum_kernel(const uint64_t* __restrict__ keys,
                                                                const T* __restrict__ dY, float* __restrict__ dE,
                                                                int64_t ntok, int64_t H) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int SL = 4;
+  constexpr int NSL = 16;   // a 4096-column row in one pass
   const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (p >= ntok) return;
-  const uint64_t key = keys[p];
-  if (key == kNoKey) return;
-  const uint64_t row = key >> 32;
-  if (p > 0 && (keys[p - 1] >> 32) == row) return;  // not the head of its segment
   const int lane = threadIdx.x & 63;
-  float* drow = dE + (int64_t)row * H;
-  for (int64_t b = p; b < ntok; b += 64) {
-    const int64_t q = b + lane;
-    const uint64_t kq = q < ntok ? keys[q] : kNoKey;
+  // Keys of positions b .. b+63 (one per lane; kNoKey past the end), loaded
+  // unconditionally at a clamped position.
+  auto chunk_keys = [&](int64_t b) {
+    const uint64_t k = keys[min(b + lane, ntok - 1)];
+    return b + lane < ntok ? k : kNoKey;
+  };
+  // The first 64 keys from position p (kept for every pass) and the key
+  // before p, loaded together; p's own key is lane 0's.
+  const uint64_t k0 = chunk_keys(p);
+  const uint64_t kprev = keys[p > 0 ? p - 1 : 0];
+  const uint64_t key = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(k0 >> 32), 0) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k0, 0);
+  const uint64_t row = key >> 32;
+  // out of range, or not the head of its segment (one test, so that both
+  // loads are issued before the branch)
+  const bool skip = (key == kNoKey) | ((p > 0) & ((kprev >> 32) == row));
+  if (skip) return;
+  char* const drow = reinterpret_cast<char*>(dE + (int64_t)row * H);
+  // keys of a chunk -> the number n of its leading positions in the segment
+  // (a contiguous prefix) and the lanes' tokens
+  auto segment = [&](uint64_t kq, int& n, int& tl) {
     const uint64_t in_seg = __ballot(kq != kNoKey && (kq >> 32) == row);
-    // positions b .. b + n - 1 belong to the segment (a contiguous prefix)
-    const int n = in_seg == ~0ull ? 64 : (int)__builtin_ctzll(~in_seg);
-    if (n == 0) break;
-    const int tl = (int)(kq & 0xffffffffu);
-    for (int64_t c0 = (int64_t)lane * VEC; c0 < H; c0 += 64 * VEC * SL) {
-      float acc[SL][VEC];
+    n = in_seg == ~0ull ? 64 : (int)__builtin_ctzll(~in_seg);
+    tl = (int)(kq & 0xffffffffu);
+  };
+  int n0, tl0;
+  segment(k0, n0, tl0);
+  // Every load below is unconditional, at a column clamped into the row
+  // (H is a multiple of 4): a guarded load would be waited for before the
+  // next one is issued.  Sums for columns past H are dropped at the store.
+  // Addresses are a wave-uniform row start plus a 32-bit byte offset per
+  // slab, shared by every row the pass touches.  The pass loop is uniform
+  // over the wave (the ballots need every lane).
+  for (int64_t cb = 0; cb < H; cb += 256 * NSL) {
+    uint32_t col[NSL];
 #pragma unroll
-      for (int sl = 0; sl < SL; ++sl) {
-        const int64_t c = c0 + (int64_t)sl * 64 * VEC;
+    for (int sl = 0; sl < NSL; ++sl) col[sl] = (uint32_t)min(cb + (int64_t)lane * 4 + sl * 256, H - 4);
+    float acc[NSL][4];
 #pragma unroll
-        for (int i = 0; i < VEC; i += 4) {
-          f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-          if (c < H) d = *reinterpret_cast<const f32x4_t*>(drow + c + i);
-          acc[sl][i] = d[0]; acc[sl][i + 1] = d[1]; acc[sl][i + 2] = d[2]; acc[sl][i + 3] = d[3];
+    for (int sl = 0; sl < NSL; ++sl) {
+      const f32x4_t d = *reinterpret_cast<const f32x4_t*>(drow + col[sl] * 4u);
+      acc[sl][0] = d[0]; acc[sl][1] = d[1]; acc[sl][2] = d[2]; acc[sl][3] = d[3];
+    }
+    // tokens 0 .. n-1 of a chunk, in order, two rows in flight at a time
+    auto add_tokens = [&](int n, int tl) {
+      int u = 0;
+      for (; u + 2 <= n; u += 2) {
+        const char* s0 = reinterpret_cast<const char*>(dY + (int64_t)__builtin_amdgcn_readlane(tl, u) * H);
+        const char* s1 = reinterpret_cast<const char*>(dY + (int64_t)__builtin_amdgcn_readlane(tl, u + 1) * H);
+        typename AccumLoad<T>::raw x0[NSL], x1[NSL];
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          x0[sl] = AccumLoad<T>::get(s0, col[sl] * (uint32_t)sizeof(T));
+          x1[sl] = AccumLoad<T>::get(s1, col[sl] * (uint32_t)sizeof(T));
+        }
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          AccumLoad<T>::add(acc[sl], x0[sl]);
+          AccumLoad<T>::add(acc[sl], x1[sl]);
         }
       }
-      for (int u = 0; u < n; ++u) {
-        const int64_t t = __builtin_amdgcn_readlane(tl, u);
-        const T* src = dY + t * H;
+      if (u < n) {
+        const char* s0 = reinterpret_cast<const char*>(dY + (int64_t)__builtin_amdgcn_readlane(tl, u) * H);
+        typename AccumLoad<T>::raw x0[NSL];
 #pragma unroll
-        for (int sl = 0; sl < SL; ++sl) {
-          const int64_t c = c0 + (int64_t)sl * 64 * VEC;
-          if (c < H) {
-            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + c);
-            if constexpr (VEC == 8) {
+        for (int sl = 0; sl < NSL; ++sl) x0[sl] = AccumLoad<T>::get(s0, col[sl] * (uint32_t)sizeof(T));
 #pragma unroll
-              for (int w = 0; w < 4; ++w) { acc[sl][2 * w] += bf16lo(x[w]); acc[sl][2 * w + 1] += bf16hi(x[w]); }
-            } else {
-#pragma unroll
-              for (int w = 0; w < 4; ++w) acc[sl][w] += __uint_as_float(x[w]);
-            }
-          }
-        }
+        for (int sl = 0; sl < NSL; ++sl) AccumLoad<T>::add(acc[sl], x0[sl]);
       }
-#pragma unroll
-      for (int sl = 0; sl < SL; ++sl) {
-        const int64_t c = c0 + (int64_t)sl * 64 * VEC;
-        if (c < H) {
-#pragma unroll
-          for (int i = 0; i < VEC; i += 4)
-            __builtin_nontemporal_store(f32x4_t{acc[sl][i], acc[sl][i + 1], acc[sl][i + 2], acc[sl][i + 3]},
-                                        reinterpret_cast<f32x4_t*>(drow + c + i));
-        }
+    };
+    add_tokens(n0, tl0);
+    if (n0 == 64) {
+      for (int64_t b = p + 64; b < ntok; b += 64) {
+        int n, tl;
+        segment(chunk_keys(b), n, tl);
+        add_tokens(n, tl);
+        if (n < 64) break;
       }
     }
-    if (n < 64) break;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (cb + (int64_t)lane * 4 + sl * 256 < H)
+        __builtin_nontemporal_store(f32x4_t{acc[sl][0], acc[sl][1], acc[sl][2], acc[sl][3]},
+                                    reinterpret_cast<f32x4_t*>(drow + col[sl] * 4u));
+    }
   }
 }
 
@@ -442,8 +466,7 @@ constexpr int kRadixBuckets = 256;
 extern "C" size_t vocab_embed_bwd_workspace(int64_t T, int64_t v_rows) {
   (void)v_rows;
   if (T <= 0) return 0;
-  // sort keys, then the bucket counts
-  return (size_t)next_pow2(T) * sizeof(uint64_t) + kRadixBuckets * sizeof(uint32_t);
+  return (size_t)next_pow2(T) * sizeof(uint64_t);   // the sort keys
 }
 
 extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
@@ -466,17 +489,12 @@ extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_
     // one workgroup per bucket of at most 256 rows: one 8-bit pass each
     const int brows = (int)ceil_div(v_rows, kRadixBuckets);
     const int nb = (int)ceil_div(v_rows, brows);
-    uint32_t* counts = reinterpret_cast<uint32_t*>(keys + next_pow2(T));
-    hipLaunchKernelGGL(embed_bucket_count_kernel, dim3((unsigned)nb), dim3(256), 0, st, ids, counts, (int)T, v_start,
-                       (int)v_rows, brows);
-    s = check_launch("embed_bucket_count_kernel");
-    if (s != TPS_OK) return s;
     hipLaunchKernelGGL(embed_radix_sort_kernel, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ids, keys,
-                       (const uint32_t*)counts, (int)T, v_start, (int)v_rows, tbits, ceil_log2(brows), brows);
+                       (int)T, v_start, (int)v_rows, tbits, ceil_log2(brows), brows);
     s = check_launch("embed_radix_sort_kernel");
   } else if (T <= kRadixMax && tbits + rbits <= 32) {
     hipLaunchKernelGGL(embed_radix_sort_kernel, dim3(1), dim3(kRadixThreads), 0, st, ids, keys,
-                       (const uint32_t*)nullptr, (int)T, v_start, (int)v_rows, tbits, rbits, (int)v_rows);
+                       (int)T, v_start, (int)v_rows, tbits, rbits, (int)v_rows);
     s = check_launch("embed_radix_sort_kernel");
   } else {
     const int64_t npad = next_pow2(T);

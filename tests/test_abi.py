@@ -107,8 +107,8 @@ def test_workspace_queries_and_too_small_workspace(tp):
     lib = tp.lib
     assert lib.tp_mlp_bwd_workspace(1, 2048, 1024, 2048) == 2048 * 2048 * 2
     # sort keys (next power of two of T) + 256 row-bucket counts
-    assert lib.vocab_embed_bwd_workspace(16384, 25129) == 16384 * 8 + 256 * 4
-    assert lib.vocab_embed_bwd_workspace(20000, 25129) == 32768 * 8 + 256 * 4
+    assert lib.vocab_embed_bwd_workspace(16384, 25129) == 16384 * 8
+    assert lib.vocab_embed_bwd_workspace(20000, 25129) == 32768 * 8
     assert lib.layernorm_bwd_workspace(2048, 4096) == 256 * 2 * 4096 * 4
     need = lib.tp_mlp_bwd_workspace(1, 8, 64, 128)
     st = lib.tp_mlp_bwd(1, 8, 64, 128, *([ALIGNED] * 10), need - 1, None)
