@@ -224,7 +224,7 @@ def cpu_baseline():
 # counters read for a plain copy (shard_reduce with one part over 512 MiB) per
 # byte moved.  Valid only for the GEMM source it was taken on (sha256 prefix
 # below); otherwise null.
-ROOFLINE_TRAFFIC = {"gemm_sha": "384f6bc0df6eba9f", "bytes_per_launch": 792193341}
+ROOFLINE_TRAFFIC = {"gemm_sha": "3488e65ee78570d0", "bytes_per_launch": 791722430}
 
 
 def _gemm_sha():
