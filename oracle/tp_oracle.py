@@ -34,6 +34,7 @@ __all__ = [
     "shard_reduce",
     "vocab_embed_forward", "vocab_embed_mask", "vocab_embed_backward",
     "tied_logits", "tied_logits_backward",
+    "vocab_ce_forward", "vocab_ce_backward",
     "layernorm_forward", "layernorm_backward",
     "param_count", "param_count_tied_unique",
     "round_to_bf16", "round_to_f32", "bf16_next_up",
@@ -55,6 +56,10 @@ PINS = {
     "vocab_embed_forward": "worked examples [0,212,7,9] (V=300,N=2) and [2,7,1,5]/[0,3)",
     "vocab_embed_backward": "scalar-loop brute force; column-sum identity; finite differences",
     "tied_logits_backward": "finite differences through both uses of the table",
+    "vocab_ce_forward": "page's 10-word two-shard masking layout; uniform logits give log V; "
+                        "per-row shift invariance; library logsumexp; scalar-loop brute force",
+    "vocab_ce_backward": "central finite differences of the loss; rows sum to zero; "
+                         "closed form 1/V - onehot for uniform logits",
     "layernorm_forward": "mean 0 / variance 1 invariants and scalar-loop brute force",
     "layernorm_backward": "central finite differences",
     "param_count": "page value 2,827,821,056 for H=4096, L=12, V=50257",
@@ -390,6 +395,74 @@ def tied_logits_backward(X, E_r, dL_r):
     updated with their sum; the total is ``dE_r + vocab_embed_backward(...)``.
     """
     return dL_r @ E_r, dL_r.T @ X
+
+
+# ---------------------------------------------------------------------------
+# Vocab-parallel cross entropy over the shards of the tied logits.
+# ---------------------------------------------------------------------------
+
+def vocab_ce_forward(logit_shards, targets, starts):
+    """Cross entropy of every token over logits split by vocab rows across
+    shards, computed the way the pages lay it out (page "5-megatron", section
+    _VocabParallelCrossEntropy, its flow and its code; page "notion
+    310f8c09", section 交叉熵张量并行, stages two to four; page
+    "Megtron张量/模型并行", section Cross-entropy层), in this order:
+
+    1. each shard's row maximum; the maximum over shards (the MAX all-reduce);
+    2. every shard subtracts that global maximum from its logits;
+    3. each shard takes its shifted logit at the target's column when the
+       target lies in its range [start, start + rows), else 0; the values are
+       summed over shards (a SUM all-reduce), giving the target's logit;
+    4. each shard's row sum of exp of its shifted logits; summed over shards
+       (a SUM all-reduce), giving the softmax denominator;
+    5. loss = log(denominator) - target's shifted logit.
+
+    ``logit_shards``: list of [T x rows_r] arrays (fp64 values); ``targets``:
+    [T] integer ids; ``starts``: first vocab row of every shard.  A target
+    that lies in no shard contributes 0 in step 3 on every shard, as in the
+    page's code.  Returns ``(loss, softmax_shards, gmax, denom)``: loss [T],
+    the shards' softmax exp(shifted) / denom (what the page's code keeps for
+    the backward), the global maximum and the denominator [T].
+    """
+    targets = np.asarray(targets, dtype=np.int64)
+    shards = [np.asarray(x, dtype=np.float64) for x in logit_shards]
+    gmax = np.max(np.stack([x.max(axis=1) for x in shards]), axis=0)
+    shifted = [x - gmax[:, None] for x in shards]
+    picked = np.zeros(len(targets))
+    rows_t = np.arange(len(targets))
+    for x, start in zip(shifted, starts):
+        rows = x.shape[1]
+        out = (targets < start) | (targets >= start + rows)
+        local = np.where(out, 0, targets - start)
+        part = x[rows_t, local].copy()
+        part[out] = 0.0
+        picked += part
+    exps = [np.exp(x) for x in shifted]
+    denom = np.zeros(len(targets))
+    for e in exps:
+        denom += e.sum(axis=1)
+    loss = np.log(denom) - picked
+    softmax = [e / denom[:, None] for e in exps]
+    return loss, softmax, gmax, denom
+
+
+def vocab_ce_backward(softmax_shards, targets, starts, dloss):
+    """Gradient of ``vocab_ce_forward`` w.r.t. each shard's logits: the kept
+    softmax, minus 1 at the target's column on the shard that owns the
+    target, times the upstream gradient of each token's loss (page
+    "5-megatron", section _VocabParallelCrossEntropy, the backward of its
+    code)."""
+    targets = np.asarray(targets, dtype=np.int64)
+    dloss = np.asarray(dloss, dtype=np.float64)
+    rows_t = np.arange(len(targets))
+    grads = []
+    for sm, start in zip(softmax_shards, starts):
+        rows = sm.shape[1]
+        g = np.array(sm, dtype=np.float64, copy=True)
+        inr = (targets >= start) & (targets < start + rows)
+        g[rows_t[inr], targets[inr] - start] -= 1.0
+        grads.append(g * dloss[:, None])
+    return grads
 
 
 # ---------------------------------------------------------------------------

@@ -518,3 +518,117 @@ def test_gpt_backward_finite_difference():
                 a[idx] = old
                 fd = (fp - fm) / 2e-6
                 assert abs(fd - gr[idx]) <= 2e-6 * max(1.0, abs(fd)), (li, key, idx)
+
+
+# ---------------------------------------------------------------- vocab-parallel cross entropy
+
+def _ce_shards(x, starts_counts):
+    return [x[:, s:s + c] for s, c in starts_counts]
+
+
+def test_ce_page_masking_layout():
+    """The pages' 10-word, two-shard, three-token layout: the -1 of each
+    token's gradient lands on the shard that owns its target (the picks of
+    that shard), and uniform logits give loss log 10 for every token."""
+    gx = golden("ce_masking_example.json")
+    V, sc, tg = gx["vocab"], gx["shards"], np.array(gx["targets"])
+    x = np.full((len(tg), V), 0.75)
+    loss, sm, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, [s for s, _ in sc])
+    assert np.allclose(loss, math.log(V), rtol=0, atol=1e-15)
+    grads = O.vocab_ce_backward(sm, tg, [s for s, _ in sc], np.ones(len(tg)))
+    for r, (s, c) in enumerate(sc):
+        has_minus_one = (grads[r] < 0).any(axis=1)
+        assert has_minus_one.tolist() == gx["picks_per_shard"][r]
+
+
+@pytest.mark.parametrize("V,n", [(7, 2), (50, 3), (13, 1)])
+def test_ce_uniform_logits_closed_form(V, n):
+    """All logits equal: loss = log V and gradient 1/V - onehot(target)."""
+    g = rng(31)
+    T = 6
+    tg = g.integers(0, V, T)
+    sc = [O.partition(V, n, r) for r in range(n)]
+    x = np.full((T, V), -3.25)
+    loss, sm, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, [s for s, _ in sc])
+    assert np.allclose(loss, math.log(V), rtol=0, atol=1e-14)
+    grad = np.concatenate(O.vocab_ce_backward(sm, tg, [s for s, _ in sc], np.ones(T)), axis=1)
+    want = np.full((T, V), 1.0 / V)
+    want[np.arange(T), tg] -= 1.0
+    assert np.allclose(grad, want, rtol=0, atol=1e-15)
+
+
+def test_ce_row_shift_invariance():
+    """Adding a constant to every logit of a row changes neither the loss nor
+    the gradient."""
+    g = rng(32)
+    T, V, n = 5, 23, 3
+    sc = [O.partition(V, n, r) for r in range(n)]
+    x = g.standard_normal((T, V)) * 4
+    tg = g.integers(0, V, T)
+    c = g.standard_normal(T)[:, None] * 100
+    st = [s for s, _ in sc]
+    l0, s0, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, st)
+    l1, s1, _, _ = O.vocab_ce_forward(_ce_shards(x + c, sc), tg, st)
+    assert np.allclose(l0, l1, rtol=1e-12, atol=1e-12)
+    for a, b in zip(s0, s1):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("scale", [1.0, 30.0, 3000.0])
+def test_ce_matches_library_logsumexp(scale):
+    """loss = logsumexp(row) - row[target], with scipy's logsumexp (the oracle
+    does not use it), including logits large enough to overflow exp."""
+    from scipy.special import logsumexp
+    g = rng(33)
+    T, V, n = 9, 101, 2
+    sc = [O.partition(V, n, r) for r in range(n)]
+    x = g.standard_normal((T, V)) * scale
+    tg = g.integers(0, V, T)
+    loss, _, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, [s for s, _ in sc])
+    want = logsumexp(x, axis=1) - x[np.arange(T), tg]
+    assert np.allclose(loss, want, rtol=1e-12, atol=1e-12 * scale)
+
+
+def test_ce_bruteforce_loop():
+    """Scalar loops with math.exp / math.log on small logits (no shift
+    needed): loss = log(sum_j exp x_j) - x_target."""
+    g = rng(34)
+    T, V, n = 4, 9, 2
+    sc = [O.partition(V, n, r) for r in range(n)]
+    x = g.standard_normal((T, V))
+    tg = g.integers(0, V, T)
+    loss, _, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, [s for s, _ in sc])
+    for t in range(T):
+        s = math.fsum(math.exp(float(v)) for v in x[t])
+        assert abs(loss[t] - (math.log(s) - float(x[t, tg[t]]))) <= 1e-13
+
+
+def test_ce_target_outside_every_shard():
+    """A target no shard owns picks 0 everywhere (the page's mask), and 0 is
+    the max-shifted value, so the loss is logsumexp(row) - max(row); the
+    gradient is the softmax alone."""
+    from scipy.special import logsumexp, softmax
+    g = rng(35)
+    T, V = 3, 12
+    sc = [O.partition(V, 2, r) for r in range(2)]
+    x = g.standard_normal((T, V))
+    tg = np.array([V, -1, V + 5])
+    loss, sm, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, [s for s, _ in sc])
+    assert np.allclose(loss, logsumexp(x, axis=1) - x.max(axis=1), rtol=1e-13)
+    grad = np.concatenate(O.vocab_ce_backward(sm, tg, [s for s, _ in sc], np.ones(T)), axis=1)
+    assert np.allclose(grad, softmax(x, axis=1), rtol=1e-12, atol=1e-15)
+
+
+def test_ce_backward_finite_difference_and_zero_row_sums():
+    g = rng(36)
+    T, V, n = 3, 11, 2
+    sc = [O.partition(V, n, r) for r in range(n)]
+    st = [s for s, _ in sc]
+    x = g.standard_normal((T, V)) * 2
+    tg = g.integers(0, V, T)
+    w = g.standard_normal(T)
+    _, sm, _, _ = O.vocab_ce_forward(_ce_shards(x, sc), tg, st)
+    grad = np.concatenate(O.vocab_ce_backward(sm, tg, st, w), axis=1)
+    _fd_check(lambda: float(np.sum(w * O.vocab_ce_forward(_ce_shards(x, sc), tg, st)[0])), [x], [grad],
+              h=1e-6, tol=1e-7)
+    assert np.allclose(grad.sum(axis=1), 0.0, atol=1e-14)
