@@ -232,6 +232,46 @@ tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, i
                            void* dX_r, float* dE_r, tps_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Vocab-parallel cross entropy on the tied logits (page "5-megatron",
+ * section _VocabParallelCrossEntropy; page "notion 310f8c09", section
+ * 交叉熵张量并行).  Per token t with target id y_t and logits split by vocab
+ * rows over the shards: loss_t = log(sum_j exp(x_tj - m_t)) - (x_{t,y_t} - m_t)
+ * with m_t the maximum over every shard, i.e. logsumexp - target logit; a
+ * target that no shard owns contributes 0 as its shifted logit (the pages'
+ * mask), so its loss is logsumexp - m_t.  The shards exchange per-token
+ * statistics only (the pages' MAX and SUM all-reduces of b*s values); on one
+ * device vocab_ce_combine takes every shard's statistics at once.
+ *
+ * vocab_ce_stats: one shard's statistics, one pass over its logits.
+ *   L_r [T x v_rows] of dt with row stride ldl (ldl >= v_rows, multiple of 8
+ *   for bf16 / 4 for fp32; padding columns are not read for use); targets [T]
+ *   int32 (any value); stats_r [T x 4] fp32 OUTPUT, 16-byte aligned:
+ *   {m_r = max_j L_r[t,j], s_r = sum_j exp(L_r[t,j] - m_r),
+ *    x_r = L_r[t, y_t - v_start] if v_start <= y_t < v_start + v_rows else 0,
+ *    own_r = 1 if so else 0}.  Logits must be finite.
+ * vocab_ce_combine: stats is a host array of n_parts (1..8) device pointers
+ *   to the shards' statistics (every shard of the vocabulary, any order of
+ *   shards); loss [T] and lse [T] fp32 OUTPUTS:
+ *   m = max_r m_r, den = sum_r s_r exp(m_r - m) (shard order),
+ *   pick = sum_r own_r (x_r - m), loss = log(den) - pick, lse = m + log(den).
+ * vocab_ce_bwd: dL_r[t,j] = dloss[t] * (exp(L_r[t,j] - lse[t]) - [j = y_t - v_start])
+ *   for j < v_rows, as dt with row stride ldl (padding columns not written);
+ *   dloss [T] fp32 is the upstream gradient of each token's loss.  dL_r may
+ *   be L_r itself (in place, as the pages' code does); otherwise the two must
+ *   not overlap.  The result is what tied_logits_bwd takes as dL_r.
+ * Errors: TPS_EINVAL for a bad dtype, T < 0, v_rows <= 0, v_start < 0, a bad
+ * ldl, null or misaligned pointers, n_parts outside 1..8; nothing is
+ * enqueued then.  T = 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+tps_status vocab_ce_stats(tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start,
+                          const void* L_r, const int32_t* targets, float* stats_r, tps_stream_t stream);
+tps_status vocab_ce_combine(int n_parts, const float* const* stats, int64_t T, float* loss, float* lse,
+                            tps_stream_t stream);
+tps_status vocab_ce_bwd(tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start,
+                        const void* L_r, const int32_t* targets, const float* lse, const float* dloss,
+                        void* dL_r, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * LayerNorm (replicated on every shard), for stacking layers.  Page
  * "5-megatron", section 训练一般流程 counts two LayerNorms of 2H parameters
  * per layer; the formula is the standard one with biased variance:

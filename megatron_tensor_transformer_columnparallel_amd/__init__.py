@@ -14,5 +14,6 @@ from .binding import (  # noqa: F401
     shard_reduce, shard_reduce_add,
     vocab_embed_fwd, vocab_embed_bwd, vocab_embed_bwd_workspace,
     tied_logits, tied_logits_bwd,
+    vocab_ce_stats, vocab_ce_combine, vocab_ce_bwd,
     layernorm_fwd, layernorm_bwd, layernorm_bwd_workspace, layernorm_bwd_residual,
 )

@@ -42,6 +42,9 @@ SIGNATURES = {
     "vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tied_logits": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "vocab_ce_stats": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "vocab_ce_combine": (_i32, [_i32, ctypes.POINTER(_vp), _i64, _vp, _vp, _vp]),
+    "vocab_ce_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "layernorm_fwd": (_i32, [_i32, _i32, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "layernorm_bwd_workspace": (_sz, [_i64, _i64]),
     "layernorm_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -283,6 +286,44 @@ def tied_logits_bwd(X, E_r, dL_r, dX_r, dE_r, stream=None):
     assert dL_r.shape == (T, v_rows) and dL_r.stride(1) == 1 and dE_r.dtype == torch.float32
     _check(lib.tied_logits_bwd(dt, T, H, v_rows, dL_r.stride(0), _p(X), _p(E_r), _p(dL_r), _p(dX_r), _p(dE_r),
                                _stream(stream)), "tied_logits_bwd")
+
+
+# ------------------------------------------------------------------ vocab-parallel cross entropy
+
+def vocab_ce_stats(L_r, targets, stats_r, v_start, stream=None):
+    """stats_r [T x 4] fp32 <- one shard's (max, exp-sum, target logit, owned).
+    L_r may be a column slice of a wider buffer: its row stride is passed as ldl."""
+    dt = _dt(L_r)
+    T, v_rows = L_r.shape
+    assert L_r.stride(1) == 1 and targets.dtype == torch.int32 and targets.numel() == T
+    assert stats_r.dtype == torch.float32 and stats_r.shape == (T, 4)
+    _contig(targets, stats_r)
+    _check(lib.vocab_ce_stats(dt, T, v_rows, L_r.stride(0), v_start, _p(L_r), _p(targets), _p(stats_r),
+                              _stream(stream)), "vocab_ce_stats")
+
+
+def vocab_ce_combine(stats, loss, lse, stream=None):
+    """loss, lse [T] fp32 <- every shard's statistics."""
+    if not 1 <= len(stats) <= 8:
+        raise ValueError("1..8 shards")
+    T = loss.numel()
+    _contig(loss, lse, *stats)
+    assert lse.numel() == T and all(s.shape == (T, 4) and s.dtype == torch.float32 for s in stats)
+    arr = (_vp * len(stats))(*[_p(s) for s in stats])
+    _check(lib.vocab_ce_combine(len(stats), arr, T, _p(loss), _p(lse), _stream(stream)), "vocab_ce_combine")
+
+
+def vocab_ce_bwd(L_r, targets, lse, dloss, dL_r, v_start, stream=None):
+    """dL_r <- dloss * (softmax - onehot of the owned target); dL_r may be L_r.
+    Both share L_r's row stride."""
+    dt = _dt(L_r)
+    _same(dt, dL_r)
+    T, v_rows = L_r.shape
+    assert dL_r.shape == (T, v_rows) and dL_r.stride() == L_r.stride() and L_r.stride(1) == 1
+    assert targets.dtype == torch.int32 and targets.numel() == T
+    _contig(targets, lse, dloss)
+    _check(lib.vocab_ce_bwd(dt, T, v_rows, L_r.stride(0), v_start, _p(L_r), _p(targets), _p(lse), _p(dloss),
+                            _p(dL_r), _stream(stream)), "vocab_ce_bwd")
 
 
 # ------------------------------------------------------------------ LayerNorm

@@ -1,0 +1,250 @@
+// Vocab-parallel cross entropy over the shards of the tied logits.
+//
+// The method (page "5-megatron", section _VocabParallelCrossEntropy; page
+// "notion 310f8c09", section 交叉熵张量并行) takes, per token, the maximum
+// logit over all shards (a MAX all-reduce), subtracts it, picks the shifted
+// logit at the target's column on the shard that owns the target (0
+// elsewhere; a SUM all-reduce), sums exp of the shifted logits over all
+// shards (a SUM all-reduce), and returns loss = log(sum) - pick; the backward
+// is softmax - onehot(owned target) times the upstream gradient.
+//
+// Here each shard's logits are read once (vocab_ce_stats): per token the
+// shard's own maximum m_r, the sum s_r of exp(x - m_r) over the shard, the
+// raw target logit and whether the shard owns the target.  The exchange
+// (vocab_ce_combine) forms the global maximum m = max_r m_r, the sum
+// sum_r s_r exp(m_r - m) -- equal to the sum of exp(x - m) over every shard --
+// and the pick, then the loss and log-sum-exp lse = m + log(sum).  The
+// backward (vocab_ce_bwd) reads each shard's logits once more and writes
+// dL = dloss * (exp(x - lse) - [column is the target]).  All three are bound
+// by HBM: one wavefront per token row, 16-byte vectors, every load issued
+// unconditionally at a clamped chunk so that a whole group is in flight.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace tps {
+
+namespace {
+
+struct StatPtrs {
+  const float* p[8];
+};
+
+// Chunk c (VEC elements) of a row as fp32; elements at columns >= n are set
+// to `fill`.  The read itself is clamped to the last chunk holding a valid
+// column (inside the row's stride, which is a multiple of VEC).
+template <typename T>
+__device__ __forceinline__ void load_chunk(const T* row, int64_t c, int64_t nch, int64_t n, float fill,
+                                           float* v) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t cc = c < nch ? c : nch - 1;
+  float x[VEC];
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + cc * VEC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo(w[i]); x[2 * i + 1] = bf16hi(w[i]); }
+  } else {
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(row + cc * VEC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = w[i];
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) v[e] = (c * VEC + e < n) ? x[e] : fill;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr int kGroup = 8;   // chunks per lane in flight at once
+
+// One wavefront per token row: (m_r, s_r, target logit, owned) as 4 floats.
+// Each lane keeps a running maximum and a sum relative to it over groups of
+// kGroup chunks (the sum is rescaled when a group raises the maximum); the
+// lanes' pairs are then combined across the wave the same way.
+template <typename T>
+__global__ void __launch_bounds__(256) ce_stats_kernel(const T* __restrict__ L, int64_t ldl, int64_t ntok,
+                                                       int64_t v_rows, int64_t v_start,
+                                                       const int32_t* __restrict__ targets,
+                                                       float* __restrict__ stats) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int lane = threadIdx.x & 63;
+  const T* row = L + t * ldl;
+  const int64_t nch = (v_rows + VEC - 1) / VEC;
+  // the target's column, read unconditionally (clamped) and kept only when owned
+  const int64_t tl = (int64_t)targets[t] - v_start;
+  const bool own = tl >= 0 && tl < v_rows;
+  const float xt = Elem<T>::to_f32(row[tl < 0 ? 0 : (tl < v_rows ? tl : v_rows - 1)]);
+  float m = -INFINITY, s = 0.f;
+  for (int64_t c0 = lane; c0 < nch; c0 += 64 * kGroup) {
+    float v[kGroup][VEC];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) load_chunk<T>(row, c0 + g * 64, nch, v_rows, -INFINITY, v[g]);
+    float gm = m;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) gm = fmaxf(gm, v[g][e]);
+    // m == -inf only before a lane's first valid column: nothing to rescale then
+    float acc = m == -INFINITY ? 0.f : s * __expf(m - gm);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += __expf(v[g][e] - gm);
+    m = gm;
+    s = acc;
+  }
+  const float mw = wave_max(m);
+  const float sw = wave_sum(m == -INFINITY ? 0.f : s * __expf(m - mw));
+  if (lane == 0) {
+    const f32x4_t out = {mw, sw, own ? xt : 0.f, own ? 1.f : 0.f};
+    *reinterpret_cast<f32x4_t*>(stats + 4 * t) = out;
+  }
+}
+
+// One thread per token: the exchange over the shards' statistics, in shard
+// order.
+__global__ void __launch_bounds__(256) ce_combine_kernel(StatPtrs st, int np, int64_t ntok,
+                                                         float* __restrict__ loss, float* __restrict__ lse) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= ntok) return;
+  f32x4_t v[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    if (r < np) v[r] = *reinterpret_cast<const f32x4_t*>(st.p[r] + 4 * t);
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    if (r < np) m = fmaxf(m, v[r][0]);
+  float denom = 0.f, pick = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    if (r < np) {
+      denom += v[r][1] * __expf(v[r][0] - m);
+      if (v[r][3] != 0.f) pick += v[r][2] - m;
+    }
+  const float ld = __logf(denom);
+  loss[t] = ld - pick;
+  lse[t] = m + ld;
+}
+
+// One wavefront per token row: dL = dloss * (exp(x - lse) - [column = target]).
+// Columns past v_rows (up to the row stride) are neither read for use nor
+// written.
+template <typename T>
+__global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, int64_t ntok, int64_t v_rows,
+                                                     int64_t v_start, const int32_t* __restrict__ targets,
+                                                     const float* __restrict__ lse,
+                                                     const float* __restrict__ dloss, T* dL) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int lane = threadIdx.x & 63;
+  const T* row = L + t * ldl;
+  T* drow = dL + t * ldl;
+  const int64_t nch = (v_rows + VEC - 1) / VEC;
+  const int64_t tl = (int64_t)targets[t] - v_start;   // owned when 0 <= tl < v_rows
+  const float l = lse[t], g = dloss[t];
+  for (int64_t c0 = lane; c0 < nch; c0 += 64 * kGroup) {
+    float v[kGroup][VEC];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) load_chunk<T>(row, c0 + k * 64, nch, v_rows, 0.f, v[k]);
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const int64_t c = c0 + k * 64;
+      if (c >= nch) continue;
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float p = __expf(v[k][e] - l);
+        o[e] = g * (c * VEC + e == tl ? p - 1.f : p);
+      }
+      const int nvalid = (int)(v_rows - c * VEC < VEC ? v_rows - c * VEC : VEC);
+      if constexpr (sizeof(T) == 2) store8<bf16_t>(reinterpret_cast<bf16_t*>(drow) + c * VEC, o, nvalid);
+      else store4<float>(reinterpret_cast<float*>(drow) + c * VEC, o, nvalid);
+    }
+  }
+}
+
+tps_status ce_row_checks(const char* fn, tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start) {
+  if (dt != TPS_F32 && dt != TPS_BF16) return set_error(TPS_EINVAL, std::string(fn) + ": bad dtype");
+  if (T < 0 || v_rows <= 0 || v_start < 0)
+    return set_error(TPS_EINVAL, std::string(fn) + ": need T >= 0, v_rows > 0, v_start >= 0");
+  if (ldl < v_rows || ldl % vec_elems(dt))
+    return set_error(TPS_EINVAL, std::string(fn) + ": ldl must be >= v_rows and a multiple of 8 (bf16) / 4 (fp32)");
+  if (T >= 0x7fffffffLL * 4) return set_error(TPS_EINVAL, std::string(fn) + ": T too large");
+  return TPS_OK;
+}
+
+}  // namespace
+
+}  // namespace tps
+
+using namespace tps;
+
+extern "C" tps_status vocab_ce_stats(tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start,
+                                     const void* L_r, const int32_t* targets, float* stats_r,
+                                     tps_stream_t stream) {
+  tps_status s = ce_row_checks("vocab_ce_stats", dt, T, v_rows, ldl, v_start);
+  if (s != TPS_OK) return s;
+  if (!L_r || !targets || !stats_r) return set_error(TPS_EINVAL, "vocab_ce_stats: null pointer");
+  if (!aligned16(L_r) || !aligned16(stats_r))
+    return set_error(TPS_EINVAL, "vocab_ce_stats: L_r and stats_r must be 16-byte aligned");
+  if (T == 0) return TPS_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)ceil_div(T, 4));
+  if (dt == TPS_BF16)
+    hipLaunchKernelGGL(ce_stats_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
+                       v_rows, v_start, targets, stats_r);
+  else
+    hipLaunchKernelGGL(ce_stats_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(L_r), ldl, T,
+                       v_rows, v_start, targets, stats_r);
+  return check_launch("ce_stats_kernel");
+}
+
+extern "C" tps_status vocab_ce_combine(int n_parts, const float* const* stats, int64_t T, float* loss, float* lse,
+                                       tps_stream_t stream) {
+  if (n_parts < 1 || n_parts > 8) return set_error(TPS_EINVAL, "vocab_ce_combine: n_parts must be 1..8");
+  if (T < 0) return set_error(TPS_EINVAL, "vocab_ce_combine: T < 0");
+  if (!stats || !loss || !lse) return set_error(TPS_EINVAL, "vocab_ce_combine: null pointer");
+  StatPtrs sp{};
+  for (int r = 0; r < n_parts; ++r) {
+    if (!stats[r]) return set_error(TPS_EINVAL, "vocab_ce_combine: null statistics pointer");
+    if (!aligned16(stats[r])) return set_error(TPS_EINVAL, "vocab_ce_combine: statistics must be 16-byte aligned");
+    sp.p[r] = stats[r];
+  }
+  if (T == 0) return TPS_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st, sp, n_parts, T, loss,
+                     lse);
+  return check_launch("ce_combine_kernel");
+}
+
+extern "C" tps_status vocab_ce_bwd(tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start,
+                                   const void* L_r, const int32_t* targets, const float* lse, const float* dloss,
+                                   void* dL_r, tps_stream_t stream) {
+  tps_status s = ce_row_checks("vocab_ce_bwd", dt, T, v_rows, ldl, v_start);
+  if (s != TPS_OK) return s;
+  if (!L_r || !targets || !lse || !dloss || !dL_r) return set_error(TPS_EINVAL, "vocab_ce_bwd: null pointer");
+  if (!aligned16(L_r) || !aligned16(dL_r))
+    return set_error(TPS_EINVAL, "vocab_ce_bwd: L_r and dL_r must be 16-byte aligned");
+  if (T == 0) return TPS_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)ceil_div(T, 4));
+  if (dt == TPS_BF16)
+    hipLaunchKernelGGL(ce_bwd_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
+                       v_rows, v_start, targets, lse, dloss, static_cast<bf16_t*>(dL_r));
+  else
+    hipLaunchKernelGGL(ce_bwd_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(L_r), ldl, T,
+                       v_rows, v_start, targets, lse, dloss, static_cast<float*>(dL_r));
+  return check_launch("ce_bwd_kernel");
+}

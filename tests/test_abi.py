@@ -32,7 +32,8 @@ def test_header_declares_the_path():
     names = _declared()
     for must in ["tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "shard_reduce",
                  "vocab_embed_fwd", "vocab_embed_bwd", "tied_logits", "tied_logits_bwd",
-                 "layernorm_fwd", "layernorm_bwd", "tps_partition"]:
+                 "layernorm_fwd", "layernorm_bwd", "tps_partition",
+                 "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_bwd"]:
         assert must in names
 
 
@@ -85,6 +86,17 @@ ALIGNED = 1 << 20  # a fake, 16-byte aligned address: validation fails before an
     ("layernorm_fwd", (0, 1, 4, 0, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),
     ("layernorm_fwd", (0, 1, 4, 12, 1e-5, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),  # H % 8
     ("shard_reduce_add", (0, ALIGNED, 1, 0, None, 0, ALIGNED, 1, None, 16, None)),                  # n_parts = 0
+    ("vocab_ce_stats", (1, 16, 150, 144, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # ldl < v_rows
+    ("vocab_ce_stats", (1, 16, 150, 154, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # ldl % 8
+    ("vocab_ce_stats", (1, 16, 0, 152, 0, ALIGNED, ALIGNED, ALIGNED, None)),                        # v_rows = 0
+    ("vocab_ce_stats", (1, 16, 150, 152, -1, ALIGNED, ALIGNED, ALIGNED, None)),                     # v_start < 0
+    ("vocab_ce_stats", (1, 16, 150, 152, 0, ALIGNED, None, ALIGNED, None)),                         # null targets
+    ("vocab_ce_stats", (1, 16, 150, 152, 0, ALIGNED, ALIGNED, ALIGNED + 4, None)),                  # misaligned
+    ("vocab_ce_stats", (5, 16, 150, 152, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # bad dtype
+    ("vocab_ce_stats", (0, -1, 150, 152, 0, ALIGNED, ALIGNED, ALIGNED, None)),                      # T < 0
+    ("vocab_ce_bwd", (1, 16, 150, 152, 0, ALIGNED, ALIGNED, None, ALIGNED, ALIGNED, None)),         # null lse
+    ("vocab_ce_bwd", (1, 16, 150, 152, 0, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED + 2, None)),  # misaligned dL
+    ("vocab_ce_bwd", (0, 16, 150, 150, 0, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),      # fp32 ldl % 4
 ])
 def test_validation_rejects_before_enqueue(tp, case):
     name, args = case
@@ -146,3 +158,16 @@ def test_layernorm_bwd_residual_validation(tp):
     st = lib.layernorm_bwd_residual(0, 0, 64, 4096, *args, ALIGNED, ALIGNED + 64, ALIGNED + 2, ALIGNED, ALIGNED,
                                     ALIGNED, need, None)
     assert st == tp.binding.TPS_EINVAL
+
+
+def test_vocab_ce_combine_validation(tp):
+    lib = tp.lib
+    ok = (ctypes.c_void_p * 9)(*([ALIGNED] * 9))
+    for n in (0, 9):
+        assert lib.vocab_ce_combine(n, ok, 16, ALIGNED, ALIGNED, None) == tp.binding.TPS_EINVAL
+    bad = (ctypes.c_void_p * 2)(ALIGNED, None)
+    assert lib.vocab_ce_combine(2, bad, 16, ALIGNED, ALIGNED, None) == tp.binding.TPS_EINVAL
+    mis = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED + 8)
+    assert lib.vocab_ce_combine(2, mis, 16, ALIGNED, ALIGNED, None) == tp.binding.TPS_EINVAL
+    assert lib.vocab_ce_combine(2, ok, 16, None, ALIGNED, None) == tp.binding.TPS_EINVAL
+    assert lib.tps_last_error().startswith(b"vocab_ce_combine")
