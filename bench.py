@@ -191,6 +191,57 @@ def embed_bench(tp, torch, reps=20):
     return res
 
 
+def ce_bench(tp, torch, reps=20):
+    """HBM rates of the vocab-parallel cross entropy on one shard of the tied
+    logits: T = 8*2048 tokens, shard 0 of V = 50257 (25129 rows, row stride
+    25136), bf16 logits ~ N(0, 2^2).  Three buffer sets (2.5 GB each way) are
+    rotated so that the 256 MB last-level cache cannot serve the repeats."""
+    T, V, ldl = 8 * 2048, 50257, 25136
+    start, rows = tp.tps_partition(V, 2, 0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4100)
+    targets = torch.randint(0, V, (T,), generator=g, device="cuda", dtype=torch.int32)
+    sets = []
+    for _ in range(3):
+        L = torch.zeros((T, ldl), dtype=torch.bfloat16, device="cuda")
+        L[:, :rows] = (torch.randn((T, rows), generator=g, device="cuda") * 2).to(torch.bfloat16)
+        dL = torch.empty((T, ldl), dtype=torch.bfloat16, device="cuda")
+        st = torch.empty((T, 4), dtype=torch.float32, device="cuda")
+        st1 = torch.empty((T, 4), dtype=torch.float32, device="cuda")
+        sets.append((L, dL, st, st1))
+    loss = torch.empty(T, device="cuda")
+    lse = torch.empty(T, device="cuda")
+    dloss = torch.full((T,), 1.0 / T, device="cuda")
+    for L, _, st, st1 in sets:   # a second shard's statistics for the exchange (the same logits)
+        tp.vocab_ce_stats(L[:, :rows], targets, st1, start + rows)
+    # algorithmic bytes (every element the method must read or write once)
+    lbytes = T * rows * 2
+    res = {}
+    for name, fn, nbytes in [
+        ("vocab_ce_stats", lambda s: tp.vocab_ce_stats(s[0][:, :rows], targets, s[2], start), lbytes + 4 * T + 16 * T),
+        ("vocab_ce_combine", lambda s: tp.vocab_ce_combine([s[2], s[3]], loss, lse), 2 * 16 * T + 8 * T),
+        ("vocab_ce_bwd", lambda s: tp.vocab_ce_bwd(s[0][:, :rows], targets, lse, dloss, s[1][:, :rows], start),
+         2 * lbytes + 12 * T),
+    ]:
+        for s in sets:
+            fn(s)
+        torch.cuda.synchronize()
+        ev = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(sets[i % 3])
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes": nbytes}
+    res["shape"] = {"T": T, "V": V, "shard_rows": rows, "ldl": ldl, "dtype": "bf16"}
+    return res
+
+
 def cpu_baseline():
     """The fp64 oracle on a bounded sample of the step: one shard of one
     layer's MLP sublayer forward and backward at the full shape (M=2048,
@@ -242,6 +293,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-embed", action="store_true", help="skip the embedding-kernel rates")
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer step")
+    ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy kernel rates")
     ap.add_argument("--calib", action="store_true", help="one 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -331,6 +383,10 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_embed:
         out["embed"] = embed_bench(tp, torch)
+        torch.cuda.empty_cache()
+    if not args.no_ce:
+        out["cross_entropy"] = ce_bench(tp, torch)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

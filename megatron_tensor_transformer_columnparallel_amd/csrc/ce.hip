@@ -30,26 +30,21 @@ struct StatPtrs {
   const float* p[8];
 };
 
-// Chunk c (VEC elements) of a row as fp32; elements at columns >= n are set
-// to `fill`.  The read itself is clamped to the last chunk holding a valid
-// column (inside the row's stride, which is a multiple of VEC).
+// Chunk c (VEC elements) of a row as fp32, read at chunk min(c, nch - 1):
+// the last chunk holding a valid column, inside the row's stride (a multiple
+// of VEC).  Callers mask what lies past the row.
 template <typename T>
-__device__ __forceinline__ void load_chunk(const T* row, int64_t c, int64_t nch, int64_t n, float fill,
-                                           float* v) {
-  constexpr int VEC = 16 / sizeof(T);
-  const int64_t cc = c < nch ? c : nch - 1;
-  float x[VEC];
+__device__ __forceinline__ void load_chunk(const T* row, int c, int nch, float* v) {
+  const int cc = c < nch ? c : nch - 1;
   if constexpr (sizeof(T) == 2) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + cc * VEC);
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + (int64_t)cc * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { x[2 * i] = bf16lo(w[i]); x[2 * i + 1] = bf16hi(w[i]); }
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16lo(w[i]); v[2 * i + 1] = bf16hi(w[i]); }
   } else {
-    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(row + cc * VEC);
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(row + (int64_t)cc * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = w[i];
+    for (int i = 0; i < 4; ++i) v[i] = w[i];
   }
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) v[e] = (c * VEC + e < n) ? x[e] : fill;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -63,15 +58,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kGroup = 8;   // chunks per lane in flight at once
+constexpr int kGroup = 8;                        // chunks per lane in flight at once
+constexpr float kLog2e = 1.4426950408889634f;
+// exp(x - m) as 2^((x - m) log2 e) with the hardware 2^x.  The difference
+// comes first (exact when x is near m), so large logits lose nothing there.
+__device__ __forceinline__ float exp_shifted(float x, float m) {
+  return __builtin_amdgcn_exp2f((x - m) * kLog2e);
+}
 
 // One wavefront per token row: (m_r, s_r, target logit, owned) as 4 floats.
 // Each lane keeps a running maximum and a sum relative to it over groups of
 // kGroup chunks (the sum is rescaled when a group raises the maximum); the
-// lanes' pairs are then combined across the wave the same way.
+// lanes' pairs are then combined across the wave the same way.  Only a chunk
+// that reaches past the row masks its elements (to -inf).
 template <typename T>
 __global__ void __launch_bounds__(256) ce_stats_kernel(const T* __restrict__ L, int64_t ldl, int64_t ntok,
-                                                       int64_t v_rows, int64_t v_start,
+                                                       int v_rows, int64_t v_start,
                                                        const int32_t* __restrict__ targets,
                                                        float* __restrict__ stats) {
   constexpr int VEC = 16 / sizeof(T);
@@ -79,32 +81,43 @@ __global__ void __launch_bounds__(256) ce_stats_kernel(const T* __restrict__ L, 
   if (t >= ntok) return;
   const int lane = threadIdx.x & 63;
   const T* row = L + t * ldl;
-  const int64_t nch = (v_rows + VEC - 1) / VEC;
+  const int nch = (v_rows + VEC - 1) / VEC;
   // the target's column, read unconditionally (clamped) and kept only when owned
   const int64_t tl = (int64_t)targets[t] - v_start;
   const bool own = tl >= 0 && tl < v_rows;
   const float xt = Elem<T>::to_f32(row[tl < 0 ? 0 : (tl < v_rows ? tl : v_rows - 1)]);
   float m = -INFINITY, s = 0.f;
-  for (int64_t c0 = lane; c0 < nch; c0 += 64 * kGroup) {
+  for (int c0 = lane; c0 < nch; c0 += 64 * kGroup) {
     float v[kGroup][VEC];
+    // every load of the group first: a branch between two loads makes the
+    // second wait for the first
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) load_chunk<T>(row, c0 + g * 64, nch, v_rows, -INFINITY, v[g]);
+    for (int g = 0; g < kGroup; ++g) load_chunk<T>(row, c0 + g * 64, nch, v[g]);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int c = c0 + g * 64;
+      if (c * VEC + VEC > v_rows) {   // past the row, or its partial last chunk
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (c * VEC + e >= v_rows) v[g][e] = -INFINITY;
+      }
+    }
     float gm = m;
 #pragma unroll
     for (int g = 0; g < kGroup; ++g)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) gm = fmaxf(gm, v[g][e]);
     // m == -inf only before a lane's first valid column: nothing to rescale then
-    float acc = m == -INFINITY ? 0.f : s * __expf(m - gm);
+    float acc = m == -INFINITY ? 0.f : s * exp_shifted(m, gm);
 #pragma unroll
     for (int g = 0; g < kGroup; ++g)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc += __expf(v[g][e] - gm);
+      for (int e = 0; e < VEC; ++e) acc += exp_shifted(v[g][e], gm);
     m = gm;
     s = acc;
   }
   const float mw = wave_max(m);
-  const float sw = wave_sum(m == -INFINITY ? 0.f : s * __expf(m - mw));
+  const float sw = wave_sum(m == -INFINITY ? 0.f : s * exp_shifted(m, mw));
   if (lane == 0) {
     const f32x4_t out = {mw, sw, own ? xt : 0.f, own ? 1.f : 0.f};
     *reinterpret_cast<f32x4_t*>(stats + 4 * t) = out;
@@ -138,10 +151,11 @@ __global__ void __launch_bounds__(256) ce_combine_kernel(StatPtrs st, int np, in
 }
 
 // One wavefront per token row: dL = dloss * (exp(x - lse) - [column = target]).
-// Columns past v_rows (up to the row stride) are neither read for use nor
-// written.
+// Columns past v_rows (up to the row stride) are neither used nor written.
+// The target's column is tested once per chunk; bf16 results are rounded to
+// nearest-even by the hardware pair conversion.
 template <typename T>
-__global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, int64_t ntok, int64_t v_rows,
+__global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, int64_t ntok, int v_rows,
                                                      int64_t v_start, const int32_t* __restrict__ targets,
                                                      const float* __restrict__ lse,
                                                      const float* __restrict__ dloss, T* dL) {
@@ -151,26 +165,42 @@ __global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, in
   const int lane = threadIdx.x & 63;
   const T* row = L + t * ldl;
   T* drow = dL + t * ldl;
-  const int64_t nch = (v_rows + VEC - 1) / VEC;
-  const int64_t tl = (int64_t)targets[t] - v_start;   // owned when 0 <= tl < v_rows
+  const int nch = (v_rows + VEC - 1) / VEC;
+  const int64_t tl64 = (int64_t)targets[t] - v_start;
+  const int tl = (tl64 >= 0 && tl64 < v_rows) ? (int)tl64 : -VEC;   // owned column, or none
   const float l = lse[t], g = dloss[t];
-  for (int64_t c0 = lane; c0 < nch; c0 += 64 * kGroup) {
+  for (int c0 = lane; c0 < nch; c0 += 64 * kGroup) {
     float v[kGroup][VEC];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) load_chunk<T>(row, c0 + k * 64, nch, v_rows, 0.f, v[k]);
+    for (int k = 0; k < kGroup; ++k) load_chunk<T>(row, c0 + k * 64, nch, v[k]);
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
-      const int64_t c = c0 + k * 64;
+      const int c = c0 + k * 64;
       if (c >= nch) continue;
       float o[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float p = __expf(v[k][e] - l);
-        o[e] = g * (c * VEC + e == tl ? p - 1.f : p);
+      for (int e = 0; e < VEC; ++e) o[e] = g * exp_shifted(v[k][e], l);
+      if (tl - c * VEC >= 0 && tl - c * VEC < VEC) {   // the chunk holding the owned target
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (c * VEC + e == tl) o[e] -= g;
       }
-      const int nvalid = (int)(v_rows - c * VEC < VEC ? v_rows - c * VEC : VEC);
-      if constexpr (sizeof(T) == 2) store8<bf16_t>(reinterpret_cast<bf16_t*>(drow) + c * VEC, o, nvalid);
-      else store4<float>(reinterpret_cast<float*>(drow) + c * VEC, o, nvalid);
+      if constexpr (sizeof(T) == 2) {
+        if (c * VEC + VEC <= v_rows) {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+          u32x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{o[2 * i], o[2 * i + 1]}, b2));
+          *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8) = w;
+        } else {
+          store8<bf16_t>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8, o, v_rows - c * VEC);
+        }
+      } else {
+        store4<float>(reinterpret_cast<float*>(drow) + (int64_t)c * 4, o,
+                      v_rows - c * VEC < VEC ? v_rows - c * VEC : VEC);
+      }
     }
   }
 }
@@ -182,6 +212,7 @@ tps_status ce_row_checks(const char* fn, tps_dtype dt, int64_t T, int64_t v_rows
   if (ldl < v_rows || ldl % vec_elems(dt))
     return set_error(TPS_EINVAL, std::string(fn) + ": ldl must be >= v_rows and a multiple of 8 (bf16) / 4 (fp32)");
   if (T >= 0x7fffffffLL * 4) return set_error(TPS_EINVAL, std::string(fn) + ": T too large");
+  if (v_rows > 0x7fffffffLL - 64) return set_error(TPS_EINVAL, std::string(fn) + ": v_rows must fit in int32");
   return TPS_OK;
 }
 
@@ -204,10 +235,10 @@ extern "C" tps_status vocab_ce_stats(tps_dtype dt, int64_t T, int64_t v_rows, in
   const dim3 grid((unsigned)ceil_div(T, 4));
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(ce_stats_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
-                       v_rows, v_start, targets, stats_r);
+                       (int)v_rows, v_start, targets, stats_r);
   else
     hipLaunchKernelGGL(ce_stats_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(L_r), ldl, T,
-                       v_rows, v_start, targets, stats_r);
+                       (int)v_rows, v_start, targets, stats_r);
   return check_launch("ce_stats_kernel");
 }
 
@@ -242,9 +273,9 @@ extern "C" tps_status vocab_ce_bwd(tps_dtype dt, int64_t T, int64_t v_rows, int6
   const dim3 grid((unsigned)ceil_div(T, 4));
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(ce_bwd_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
-                       v_rows, v_start, targets, lse, dloss, static_cast<bf16_t*>(dL_r));
+                       (int)v_rows, v_start, targets, lse, dloss, static_cast<bf16_t*>(dL_r));
   else
     hipLaunchKernelGGL(ce_bwd_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(L_r), ldl, T,
-                       v_rows, v_start, targets, lse, dloss, static_cast<float*>(dL_r));
+                       (int)v_rows, v_start, targets, lse, dloss, static_cast<float*>(dL_r));
   return check_launch("ce_bwd_kernel");
 }
