@@ -124,6 +124,10 @@ class TPGPT:
                                  tp.tp_attn_bwd_workspace(torch.bfloat16, c.b, c.s, H, self.hs, c.d)),), torch.uint8)
         self.ws_ln = _emp((tp.layernorm_bwd_workspace(M, H),), torch.uint8)
         self.ws_emb = _emp((tp.vocab_embed_bwd_workspace(M, max(n for _, n in self.vr)),), torch.uint8)
+        # vocab-parallel cross entropy: per-shard statistics, per-token loss and log-sum-exp
+        self.ce_stats = [_emp((M, 4), f32) for _ in range(c.n)]
+        self.ce_loss, self.ce_lse = _emp((M,), f32), _emp((M,), f32)
+        self.ce_dloss = torch.full((M,), 1.0 / M, dtype=f32, device="cuda")   # gradient of the mean loss
         # when a list, (start, end) torch.cuda.Events around each tied_logits call are appended to it
         self.logit_events = None
 
@@ -158,6 +162,23 @@ class TPGPT:
             if self.logit_events is not None:
                 e1.record()
                 self.logit_events.append((e0, e1))
+
+    def loss(self, targets, dloss=None):
+        """Vocab-parallel cross entropy of the logits of the last forward
+        against ``targets`` [M] int32 (page "5-megatron", section
+        _VocabParallelCrossEntropy): each shard's statistics, the exchange over
+        shards, then each shard's logits are overwritten in place with their
+        gradient for ``dloss`` [M] fp32 (default 1/M per token, the gradient of
+        the mean loss).  Returns the per-token loss [M] and the per-shard
+        logit gradients to pass to ``backward``."""
+        cf = self.c
+        for r, (s, _) in enumerate(self.vr):
+            tp.vocab_ce_stats(self.logits_view(r), targets, self.ce_stats[r], s)
+        tp.vocab_ce_combine(self.ce_stats, self.ce_loss, self.ce_lse)
+        dl = self.ce_dloss if dloss is None else dloss
+        for r, (s, _) in enumerate(self.vr):
+            tp.vocab_ce_bwd(self.logits_view(r), targets, self.ce_lse, dl, self.logits_view(r), s)
+        return self.ce_loss, [self.logits_view(r) for r in range(cf.n)]
 
     def backward(self, ids, dlogits):
         """dlogits[r]: [M x v_r] (row stride a multiple of 8) gradient of shard r's logits."""

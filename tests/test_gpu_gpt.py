@@ -116,3 +116,41 @@ def test_gpt_workload5_full_size():
     shape = GPTShape()
     say(f"stacked model, full workload {shape}")
     run_and_compare(shape, 5, ln_random=False, check_all=False)
+
+
+def test_gpt_small_with_vocab_cross_entropy():
+    """The small stack trained on its real loss: logits -> vocab-parallel
+    cross entropy (mean over tokens) -> its logit gradient -> backward, against
+    the oracle's gpt_forward, vocab_ce_forward/backward and gpt_backward."""
+    from megatron_tensor_transformer_columnparallel_amd.gpt import GPTShape
+    c = GPTShape(L=2, b=2, s=64, H=256, heads=4, d=64, f=1024, V=1000, n=2)
+    say(f"stacked model with cross entropy {c}")
+    ids, E, hl, model, _ = build_model(52, c, ln_random=True)
+    tg = synth.uniform_ids(52, 950, c.M, c.V)
+    dids, dtg = ids_dev(ids), ids_dev(tg)
+    model.forward(dids)
+    loss, dl = model.loss(dtg)
+    model.backward(dids, dl)
+    torch.cuda.synchronize()
+    layers64 = [{k: t.f64 for k, t in l.items()} for l in hl]
+    lg, cache = O.gpt_forward(ids, E.f64, layers64, c.b, c.s, c.heads, c.d, c.n, c.eps)
+    starts = [O.partition(c.V, c.n, r)[0] for r in range(c.n)]
+    ref_loss, sm, _, _ = O.vocab_ce_forward(lg, tg, starts)
+    ref_dl = O.vocab_ce_backward(sm, tg, starts, np.full(c.M, 1.0 / c.M))
+    e = rel_err(loss.cpu().numpy(), ref_loss)
+    print(f"  loss err {e:.2e} (mean loss {ref_loss.mean():.4f})", flush=True)
+    assert e <= BF16_TOL
+    for r in range(c.n):
+        e = rel_err(to_f64(dl[r]), ref_dl[r])
+        print(f"  dlogits[{r}] err {e:.2e}", flush=True)
+        assert e <= BF16_TOL
+    dE_ref, grads = O.gpt_backward(ids, E.f64, layers64, cache, ref_dl, c.b, c.s, c.heads, c.d, c.n)
+    e = rel_err(np.concatenate([to_f64(x) for x in model.dE], axis=0), dE_ref)
+    print(f"  dE err {e:.2e}", flush=True)
+    assert e <= BF16_TOL
+    g = model.grads[c.L - 1]["sh"]
+    for k, got in [("A", np.concatenate([to_f64(x["A"]) for x in g], axis=1)),
+                   ("B", np.concatenate([to_f64(x["B"]) for x in g], axis=0))]:
+        e = rel_err(got, grads[c.L - 1][k])
+        print(f"  layer {c.L - 1} d{k} err {e:.2e}", flush=True)
+        assert e <= BF16_TOL
