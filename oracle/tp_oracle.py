@@ -35,6 +35,7 @@ __all__ = [
     "vocab_embed_forward", "vocab_embed_mask", "vocab_embed_backward",
     "tied_logits", "tied_logits_backward",
     "vocab_ce_forward", "vocab_ce_backward",
+    "column_linear_forward", "column_linear_backward", "row_linear_forward", "row_linear_backward",
     "layernorm_forward", "layernorm_backward",
     "param_count", "param_count_tied_unique",
     "round_to_bf16", "round_to_f32", "bf16_next_up",
@@ -60,6 +61,12 @@ PINS = {
                         "per-row shift invariance; library logsumexp; scalar-loop brute force",
     "vocab_ce_backward": "central finite differences of the loss; rows sum to zero; "
                          "closed form 1/V - onehot for uniform logits",
+    "column_linear_forward": "scalar-loop brute force of X A + b; gathered shards = unsharded; "
+                             "skip_bias_add leaves X A",
+    "column_linear_backward": "central finite differences (dX summed over shards, dA, db)",
+    "row_linear_forward": "scalar-loop brute force; scattered and parallel inputs agree; "
+                          "bias added once after the sum",
+    "row_linear_backward": "central finite differences; gathered dX_r = unsharded dX",
     "layernorm_forward": "mean 0 / variance 1 invariants and scalar-loop brute force",
     "layernorm_backward": "central finite differences",
     "param_count": "page value 2,827,821,056 for H=4096, L=12, V=50257",
@@ -395,6 +402,68 @@ def tied_logits_backward(X, E_r, dL_r):
     updated with their sum; the total is ``dE_r + vocab_embed_backward(...)``.
     """
     return dL_r @ E_r, dL_r.T @ X
+
+
+# ---------------------------------------------------------------------------
+# The two linear layers on their own (page "5-megatron", sections
+# ColumnParallelLinear and RowParallelLinear), in math layout: Y = X A + b.
+# ---------------------------------------------------------------------------
+
+def column_linear_forward(X, A, b, n, gather_output=True, skip_bias_add=False):
+    """ColumnParallelLinear over n shards: A = [A_1 .. A_n] split along its
+    columns, each shard computes Y_r = X A_r + b_r with its slice b_r of the
+    bias (the f operator copies X to every shard), and with ``gather_output``
+    the shards' outputs are concatenated along columns (the g operator's
+    all-gather).  With ``skip_bias_add`` no bias is added (the layer returns
+    it instead).  Returns the list of Y_r, and their concatenation when
+    gathered."""
+    X = np.asarray(X, dtype=np.float64)
+    outs = []
+    for r in range(n):
+        Ar = split_columns(A, n, r)
+        Yr = X @ Ar
+        if b is not None and not skip_bias_add:
+            s, c = partition(np.shape(A)[1], n, r)
+            Yr = Yr + np.asarray(b, dtype=np.float64)[s:s + c][None, :]
+        outs.append(Yr)
+    return outs, (np.concatenate(outs, axis=1) if gather_output else None)
+
+
+def column_linear_backward(X, A_r, dY_r):
+    """Backward of one column shard for its output gradient dY_r (the split
+    of a gathered gradient, the g operator's backward): dX_r = dY_r A_r^T is a
+    partial that the f operator's backward sums over shards; dA_r = X^T dY_r;
+    the bias slice's gradient is the column sum of dY_r.  Returns
+    (dX_r, dA_r, db_r)."""
+    dY_r = np.asarray(dY_r, dtype=np.float64)
+    return dY_r @ np.asarray(A_r).T, np.asarray(X).T @ dY_r, dY_r.sum(axis=0)
+
+
+def row_linear_forward(X, B, b, n, input_is_parallel=False, skip_bias_add=False):
+    """RowParallelLinear over n shards: B = [B_1; ..; B_n] split along its
+    rows; unless ``input_is_parallel`` the full input X is split along its
+    columns into X_r (the scatter); each shard computes the partial
+    X_r B_r, the partials are summed (the all-reduce), and then the full bias
+    is added once unless ``skip_bias_add``.  ``X`` is the full input, or the
+    list of X_r when ``input_is_parallel``.  Returns (partials, output)."""
+    parts = []
+    for r in range(n):
+        Xr = np.asarray(X[r] if input_is_parallel else split_columns(X, n, r), dtype=np.float64)
+        parts.append(Xr @ split_rows(B, n, r))
+    Y = shard_reduce(parts)
+    if b is not None and not skip_bias_add:
+        Y = Y + np.asarray(b, dtype=np.float64)[None, :]
+    return parts, Y
+
+
+def row_linear_backward(X_r, B_r, dY):
+    """Backward of one row shard for the full output gradient dY (the
+    all-reduce's backward is the identity): dX_r = dY B_r^T (the scatter's
+    backward gathers the shards' dX_r along columns), dB_r = X_r^T dY, and the
+    replicated bias's gradient is the column sum of dY.  Returns
+    (dX_r, dB_r, db)."""
+    dY = np.asarray(dY, dtype=np.float64)
+    return dY @ np.asarray(B_r).T, np.asarray(X_r).T @ dY, dY.sum(axis=0)
 
 
 # ---------------------------------------------------------------------------

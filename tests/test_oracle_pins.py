@@ -632,3 +632,80 @@ def test_ce_backward_finite_difference_and_zero_row_sums():
     _fd_check(lambda: float(np.sum(w * O.vocab_ce_forward(_ce_shards(x, sc), tg, st)[0])), [x], [grad],
               h=1e-6, tol=1e-7)
     assert np.allclose(grad.sum(axis=1), 0.0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- column / row parallel linear
+
+def _linear_loop(X, A, b):
+    M, K = X.shape
+    N = A.shape[1]
+    Y = np.zeros((M, N))
+    for m in range(M):
+        for j in range(N):
+            Y[m, j] = math.fsum(float(X[m, k]) * float(A[k, j]) for k in range(K)) + (b[j] if b is not None else 0.0)
+    return Y
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_column_linear_bruteforce_gather_and_skip_bias(n):
+    g = rng(40)
+    X, A, b = g.standard_normal((5, 7)), g.standard_normal((7, 10)), g.standard_normal(10)
+    outs, Y = O.column_linear_forward(X, A, b, n)
+    assert np.allclose(Y, _linear_loop(X, A, b), rtol=1e-13, atol=1e-13)
+    for r in range(n):
+        s, c = O.partition(10, n, r)
+        assert np.allclose(outs[r], _linear_loop(X, A[:, s:s + c], b[s:s + c]), rtol=1e-13, atol=1e-13)
+    outs2, none = O.column_linear_forward(X, A, b, n, gather_output=False, skip_bias_add=True)
+    assert none is None
+    assert np.allclose(np.concatenate(outs2, axis=1), _linear_loop(X, A, None), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_row_linear_bruteforce_scatter_parallel_and_bias_once(n):
+    g = rng(41)
+    X, B, b = g.standard_normal((4, 9)), g.standard_normal((9, 6)), g.standard_normal(6)
+    _, Y = O.row_linear_forward(X, B, b, n)
+    assert np.allclose(Y, _linear_loop(X, B, b), rtol=1e-13, atol=1e-13)
+    Xs = [X[:, s:s + c] for s, c in (O.partition(9, n, r) for r in range(n))]
+    parts, Y2 = O.row_linear_forward(Xs, B, b, n, input_is_parallel=True)
+    assert np.allclose(Y2, Y, rtol=1e-13, atol=1e-13)
+    _, Y3 = O.row_linear_forward(X, B, b, n, skip_bias_add=True)
+    assert np.allclose(Y3, _linear_loop(X, B, None), rtol=1e-13, atol=1e-13)
+
+
+def test_column_then_row_is_the_unsharded_two_layer_product():
+    """Column split feeding the row split without a gather (the MLP pattern,
+    without the activation): sum_r (X A_r + b_r) B_r + c = (X A + b) B + c."""
+    g = rng(42)
+    n = 2
+    X, A, b, B, c = (g.standard_normal((3, 5)), g.standard_normal((5, 8)), g.standard_normal(8),
+                     g.standard_normal((8, 4)), g.standard_normal(4))
+    outs, _ = O.column_linear_forward(X, A, b, n, gather_output=False)
+    _, Y = O.row_linear_forward(outs, B, c, n, input_is_parallel=True)
+    assert np.allclose(Y, (X @ A + b) @ B + c, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_backward_finite_difference():
+    g = rng(43)
+    n = 2
+    X, A, b = g.standard_normal((3, 4)), g.standard_normal((4, 6)), g.standard_normal(6)
+    B, c = g.standard_normal((6, 5)), g.standard_normal(5)
+    R = g.standard_normal((3, 5))
+
+    def loss():
+        outs, _ = O.column_linear_forward(X, A, b, n, gather_output=False)
+        return float(np.sum(R * O.row_linear_forward(outs, B, c, n, input_is_parallel=True)[1]))
+
+    outs, _ = O.column_linear_forward(X, A, b, n, gather_output=False)
+    dH, dBs, dcs = [], [], []
+    for r in range(n):
+        dHr, dBr, dc = O.row_linear_backward(outs[r], O.split_rows(B, n, r), R)
+        dH.append(dHr); dBs.append(dBr); dcs.append(dc)
+    dX = np.zeros_like(X); dAs, dbs = [], []
+    for r in range(n):
+        dXr, dAr, dbr = O.column_linear_backward(X, O.split_columns(A, n, r), dH[r])
+        dX += dXr; dAs.append(dAr); dbs.append(dbr)
+    _fd_check(loss, [X, A, b, B, c],
+              [dX, np.concatenate(dAs, axis=1), np.concatenate(dbs), np.concatenate(dBs, axis=0), dcs[0]],
+              h=1e-6, tol=1e-6)
+    assert all(np.array_equal(d, dcs[0]) for d in dcs)   # the replicated bias: same gradient on every shard
