@@ -232,6 +232,54 @@ tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, i
                            void* dX_r, float* dE_r, tps_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The two linear layers on their own (page "5-megatron", sections
+ * ColumnParallelLinear and RowParallelLinear), math layout Y = X A + b, one
+ * shard per call; dt is TPS_BF16 or TPS_F32 for every matrix and bias.
+ *
+ * column_linear_fwd: Y_r = X A_r (+ b_r).  X [M x h_in] (the f operator's
+ *   copy: the same X on every shard), A_r [h_in x n_r] (columns of A), b_r
+ *   [n_r] (its slice of the bias; NULL for no bias, also for skip_bias_add,
+ *   where the caller keeps the bias).  Y_r [M x n_r] with row stride ldy
+ *   (>= n_r, multiple of 8): with gather_output, Y_r is the shard's column
+ *   slice of the gathered [M x sum n_r] output (the all-gather is the
+ *   layout).
+ * column_linear_bwd: for dY_r [M x n_r] with row stride lddy (the split of a
+ *   gathered gradient is a column slice): dX_r = dY_r A_r^T [M x h_in], a
+ *   partial that the f backward sums over shards (shard_reduce);
+ *   dA_r = X^T dY_r [h_in x n_r]; db_r [n_r] fp32 = column sums of dY_r
+ *   (NULL: not computed).
+ * row_linear_fwd: Y_r = X_r B_r [M x h_out], a partial.  X_r [M x k_r] with
+ *   row stride ldx: the shard's column slice of the full input X when the
+ *   input is not parallel (the scatter is the layout), or its own [M x k_r]
+ *   input; B_r [k_r x h_out] (rows of B).  The sum over shards, plus the
+ *   bias once, is shard_reduce_bias (or shard_reduce without bias).
+ * row_linear_bwd: for the full dY [M x h_out] (the all-reduce's backward is
+ *   the identity): dX_r = dY B_r^T written with row stride lddx (a column
+ *   slice of the gathered dX when the input was scattered); dB_r = X_r^T dY
+ *   [k_r x h_out]; db [h_out] fp32 = column sums of dY (the replicated
+ *   bias's gradient; NULL: not computed).
+ * shard_reduce_bias: out[m,n] = sum over parts (shard order, fp32) + bias[n],
+ *   one rounding; parts: host array of n_parts (1..8) device pointers to
+ *   [M x N] of dt; bias [N] of dt; N a multiple of 8.  out may be parts[0].
+ * Dimensions: all > 0 and < 2^31; h_in, n_r, k_r, h_out multiples of 8; every
+ * pointer 16-byte aligned.  Outputs must not alias inputs (except as noted).
+ * Errors: TPS_EINVAL before anything is enqueued.  db_r/db are written by a
+ * fixed-order reduction (reproducible).
+ * ------------------------------------------------------------------------ */
+tps_status column_linear_fwd(tps_dtype dt, int64_t M, int64_t h_in, int64_t n_r, const void* X,
+                             const void* A_r, const void* b_r, void* Y, int64_t ldy, tps_stream_t stream);
+tps_status column_linear_bwd(tps_dtype dt, int64_t M, int64_t h_in, int64_t n_r, const void* X,
+                             const void* A_r, const void* dY, int64_t lddy, void* dX_r, void* dA_r,
+                             float* db_r, tps_stream_t stream);
+tps_status row_linear_fwd(tps_dtype dt, int64_t M, int64_t k_r, int64_t h_out, const void* X_r, int64_t ldx,
+                          const void* B_r, void* Y_r, tps_stream_t stream);
+tps_status row_linear_bwd(tps_dtype dt, int64_t M, int64_t k_r, int64_t h_out, const void* X_r, int64_t ldx,
+                          const void* B_r, const void* dY, void* dX_r, int64_t lddx, void* dB_r, float* db,
+                          tps_stream_t stream);
+tps_status shard_reduce_bias(tps_dtype dt, int n_parts, const void* const* parts, const void* bias, void* out,
+                             int64_t M, int64_t N, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Vocab-parallel cross entropy on the tied logits (page "5-megatron",
  * section _VocabParallelCrossEntropy; page "notion 310f8c09", section
  * 交叉熵张量并行).  Per token t with target id y_t and logits split by vocab

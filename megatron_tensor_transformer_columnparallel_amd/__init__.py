@@ -15,5 +15,6 @@ from .binding import (  # noqa: F401
     vocab_embed_fwd, vocab_embed_bwd, vocab_embed_bwd_workspace,
     tied_logits, tied_logits_bwd,
     vocab_ce_stats, vocab_ce_combine, vocab_ce_bwd,
+    column_linear_fwd, column_linear_bwd, row_linear_fwd, row_linear_bwd, shard_reduce_bias,
     layernorm_fwd, layernorm_bwd, layernorm_bwd_workspace, layernorm_bwd_residual,
 )

@@ -42,6 +42,11 @@ SIGNATURES = {
     "vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tied_logits": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "column_linear_fwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "column_linear_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
+    "row_linear_fwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "row_linear_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "shard_reduce_bias": (_i32, [_i32, _i32, ctypes.POINTER(_vp), _vp, _vp, _i64, _i64, _vp]),
     "vocab_ce_stats": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "vocab_ce_combine": (_i32, [_i32, ctypes.POINTER(_vp), _i64, _vp, _vp, _vp]),
     "vocab_ce_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -286,6 +291,80 @@ def tied_logits_bwd(X, E_r, dL_r, dX_r, dE_r, stream=None):
     assert dL_r.shape == (T, v_rows) and dL_r.stride(1) == 1 and dE_r.dtype == torch.float32
     _check(lib.tied_logits_bwd(dt, T, H, v_rows, dL_r.stride(0), _p(X), _p(E_r), _p(dL_r), _p(dX_r), _p(dE_r),
                                _stream(stream)), "tied_logits_bwd")
+
+
+# ------------------------------------------------------------------ column / row parallel linear
+
+def column_linear_fwd(X, A_r, Y, b_r=None, stream=None):
+    """Y (a [M x n_r] view; may be a column slice of the gathered output) <- X A_r (+ b_r)."""
+    dt = _dt(X)
+    _same(dt, A_r, Y, *([b_r] if b_r is not None else []))
+    _contig(X, A_r)
+    M, h = X.shape
+    n = A_r.shape[1]
+    assert A_r.shape == (h, n) and Y.shape == (M, n) and Y.stride(1) == 1
+    if b_r is not None:
+        _contig(b_r)
+        assert b_r.numel() == n
+    _check(lib.column_linear_fwd(dt, M, h, n, _p(X), _p(A_r), _p(b_r), _p(Y), Y.stride(0), _stream(stream)),
+           "column_linear_fwd")
+
+
+def column_linear_bwd(X, A_r, dY, dX_r, dA_r, db_r=None, stream=None):
+    """dX_r (partial), dA_r, db_r (fp32, optional) for dY [M x n_r] (may be a column slice)."""
+    dt = _dt(X)
+    _same(dt, A_r, dY, dX_r, dA_r)
+    _contig(X, A_r, dX_r, dA_r)
+    M, h = X.shape
+    n = A_r.shape[1]
+    assert dY.shape == (M, n) and dY.stride(1) == 1 and dX_r.shape == (M, h) and dA_r.shape == (h, n)
+    if db_r is not None:
+        _contig(db_r)
+        assert db_r.dtype == torch.float32 and db_r.numel() == n
+    _check(lib.column_linear_bwd(dt, M, h, n, _p(X), _p(A_r), _p(dY), dY.stride(0), _p(dX_r), _p(dA_r), _p(db_r),
+                                 _stream(stream)), "column_linear_bwd")
+
+
+def row_linear_fwd(X_r, B_r, Y_r, stream=None):
+    """Y_r (partial) <- X_r B_r; X_r [M x k_r] may be a column slice of the full input."""
+    dt = _dt(X_r)
+    _same(dt, B_r, Y_r)
+    _contig(B_r, Y_r)
+    M, k = X_r.shape
+    h = B_r.shape[1]
+    assert X_r.stride(1) == 1 and B_r.shape == (k, h) and Y_r.shape == (M, h)
+    _check(lib.row_linear_fwd(dt, M, k, h, _p(X_r), X_r.stride(0), _p(B_r), _p(Y_r), _stream(stream)),
+           "row_linear_fwd")
+
+
+def row_linear_bwd(X_r, B_r, dY, dX_r, dB_r, db=None, stream=None):
+    """dX_r (may be a column slice of the gathered dX), dB_r, db (fp32, optional) for the full dY."""
+    dt = _dt(X_r)
+    _same(dt, B_r, dY, dX_r, dB_r)
+    _contig(B_r, dY, dB_r)
+    M, k = X_r.shape
+    h = B_r.shape[1]
+    assert X_r.stride(1) == 1 and dX_r.shape == (M, k) and dX_r.stride(1) == 1 and dY.shape == (M, h)
+    assert dB_r.shape == (k, h)
+    if db is not None:
+        _contig(db)
+        assert db.dtype == torch.float32 and db.numel() == h
+    _check(lib.row_linear_bwd(dt, M, k, h, _p(X_r), X_r.stride(0), _p(B_r), _p(dY), _p(dX_r), dX_r.stride(0),
+                              _p(dB_r), _p(db), _stream(stream)), "row_linear_bwd")
+
+
+def shard_reduce_bias(parts, bias, out, stream=None):
+    """out [M x N] <- sum(parts) + bias (fp32 sum in shard order, one rounding)."""
+    if not 1 <= len(parts) <= 8:
+        raise ValueError("1..8 parts")
+    dt = _dt(out)
+    _same(dt, bias, *parts)
+    _contig(out, bias, *parts)
+    M, N = out.shape
+    assert bias.numel() == N and all(p.shape == (M, N) for p in parts)
+    arr = (_vp * len(parts))(*[_p(p) for p in parts])
+    _check(lib.shard_reduce_bias(dt, len(parts), arr, _p(bias), _p(out), M, N, _stream(stream)),
+           "shard_reduce_bias")
 
 
 # ------------------------------------------------------------------ vocab-parallel cross entropy

@@ -33,7 +33,9 @@ def test_header_declares_the_path():
     for must in ["tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "shard_reduce",
                  "vocab_embed_fwd", "vocab_embed_bwd", "tied_logits", "tied_logits_bwd",
                  "layernorm_fwd", "layernorm_bwd", "tps_partition",
-                 "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_bwd"]:
+                 "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_bwd",
+                 "column_linear_fwd", "column_linear_bwd", "row_linear_fwd", "row_linear_bwd",
+                 "shard_reduce_bias"]:
         assert must in names
 
 
@@ -97,6 +99,17 @@ ALIGNED = 1 << 20  # a fake, 16-byte aligned address: validation fails before an
     ("vocab_ce_bwd", (1, 16, 150, 152, 0, ALIGNED, ALIGNED, None, ALIGNED, ALIGNED, None)),         # null lse
     ("vocab_ce_bwd", (1, 16, 150, 152, 0, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED + 2, None)),  # misaligned dL
     ("vocab_ce_bwd", (0, 16, 150, 150, 0, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None)),      # fp32 ldl % 4
+    ("column_linear_fwd", (1, 8, 64, 128, ALIGNED, ALIGNED, None, ALIGNED, 120, None)),             # ldy < n_r
+    ("column_linear_fwd", (1, 8, 60, 128, ALIGNED, ALIGNED, None, ALIGNED, 128, None)),             # h_in % 8
+    ("column_linear_fwd", (1, 0, 64, 128, ALIGNED, ALIGNED, None, ALIGNED, 128, None)),             # M = 0
+    ("column_linear_fwd", (1, 8, 64, 128, None, ALIGNED, None, ALIGNED, 128, None)),                # null X
+    ("column_linear_fwd", (1, 8, 64, 128, ALIGNED, ALIGNED, ALIGNED + 2, ALIGNED, 128, None)),      # bias align
+    ("column_linear_bwd", (1, 8, 64, 128, ALIGNED, ALIGNED, ALIGNED, 124, ALIGNED, ALIGNED, None, None)),  # lddy
+    ("column_linear_bwd", (3, 8, 64, 128, ALIGNED, ALIGNED, ALIGNED, 128, ALIGNED, ALIGNED, None, None)),  # dtype
+    ("row_linear_fwd", (1, 8, 64, 128, ALIGNED, 56, ALIGNED, ALIGNED, None)),                       # ldx < k_r
+    ("row_linear_fwd", (1, 8, 64, 124, ALIGNED, 64, ALIGNED, ALIGNED, None)),                       # h_out % 8
+    ("row_linear_bwd", (1, 8, 64, 128, ALIGNED, 64, ALIGNED, ALIGNED, ALIGNED, 60, ALIGNED, None, None)),  # lddx
+    ("row_linear_bwd", (1, 8, 64, 128, ALIGNED, 64, ALIGNED, ALIGNED, None, 64, ALIGNED, None, None)),    # null dX
 ])
 def test_validation_rejects_before_enqueue(tp, case):
     name, args = case
@@ -171,3 +184,13 @@ def test_vocab_ce_combine_validation(tp):
     assert lib.vocab_ce_combine(2, mis, 16, ALIGNED, ALIGNED, None) == tp.binding.TPS_EINVAL
     assert lib.vocab_ce_combine(2, ok, 16, None, ALIGNED, None) == tp.binding.TPS_EINVAL
     assert lib.tps_last_error().startswith(b"vocab_ce_combine")
+
+
+def test_shard_reduce_bias_validation(tp):
+    lib = tp.lib
+    arr = (ctypes.c_void_p * 9)(*([ALIGNED] * 9))
+    for n in (0, 9):
+        assert lib.shard_reduce_bias(1, n, arr, ALIGNED, ALIGNED, 4, 16, None) == tp.binding.TPS_EINVAL
+    assert lib.shard_reduce_bias(1, 2, arr, ALIGNED, ALIGNED, 4, 12, None) == tp.binding.TPS_EINVAL   # N % 8
+    assert lib.shard_reduce_bias(1, 2, arr, None, ALIGNED, 4, 16, None) == tp.binding.TPS_EINVAL      # null bias
+    assert lib.tps_last_error().startswith(b"shard_reduce_bias")
