@@ -242,6 +242,53 @@ def ce_bench(tp, torch, reps=20):
     return res
 
 
+def linear_bench(tp, torch, reps=10):
+    """The two linear layers on their own at the layer's MLP shard shape
+    (M = 2048 tokens, h = 4096, 4h split over 2 shards = 8192 columns each),
+    bf16 with biases: TFLOP/s of each call (GEMM FLOPs 2MNK; the bias and
+    bias-gradient work is counted in the time, not in the FLOPs)."""
+    M, h, n = 2048, 4096, 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4200)
+    bf = torch.bfloat16
+    r = lambda *sh: (torch.randn(sh, generator=g, device="cuda") * 0.02).to(bf)
+    X, A, b, dY = r(M, h), r(h, n), r(n), r(M, n)
+    Y, dX, dA = torch.empty((M, n), dtype=bf, device="cuda"), torch.empty((M, h), dtype=bf, device="cuda"), \
+        torch.empty((h, n), dtype=bf, device="cuda")
+    db = torch.empty(n, device="cuda")
+    B, c, dZ = r(n, h), r(h), r(M, h)
+    Z0, Z1, Z = (torch.empty((M, h), dtype=bf, device="cuda") for _ in range(3))
+    dB, dH = torch.empty((n, h), dtype=bf, device="cuda"), torch.empty((M, n), dtype=bf, device="cuda")
+    dc = torch.empty(h, device="cuda")
+    gf = 2 * M * h * n
+    res = {}
+    for name, fn, flops in [
+        ("column_linear_fwd", lambda: tp.column_linear_fwd(X, A, Y, b_r=b), gf),
+        ("column_linear_bwd", lambda: tp.column_linear_bwd(X, A, dY, dX, dA, db_r=db), 2 * gf),
+        ("row_linear_fwd + shard_reduce_bias (2 shards)",
+         lambda: (tp.row_linear_fwd(Y, B, Z0), tp.row_linear_fwd(Y, B, Z1), tp.shard_reduce_bias([Z0, Z1], c, Z)),
+         2 * gf),
+        ("row_linear_bwd", lambda: tp.row_linear_bwd(Y, B, dZ, dH, dB, db=dc), 2 * gf),
+    ]:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    res["shape"] = {"M": M, "h": h, "n_per_shard": n, "dtype": "bf16", "bias": True}
+    return res
+
+
 def cpu_baseline():
     """The fp64 oracle on a bounded sample of the step: one shard of one
     layer's MLP sublayer forward and backward at the full shape (M=2048,
@@ -294,6 +341,7 @@ def main():
     ap.add_argument("--no-embed", action="store_true", help="skip the embedding-kernel rates")
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer step")
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy kernel rates")
+    ap.add_argument("--no-linear", action="store_true", help="skip the standalone linear-layer rates")
     ap.add_argument("--calib", action="store_true", help="one 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -386,6 +434,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_ce:
         out["cross_entropy"] = ce_bench(tp, torch)
+        torch.cuda.empty_cache()
+    if not args.no_linear:
+        out["linear"] = linear_bench(tp, torch)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
