@@ -16,6 +16,9 @@ citations:
   row/column splits, MLP, attention by heads, embedding, cross entropy).
 * "notion 310f8c09" -- www.baty7811.com/blog/notion-310f8c09... (PP/DP/TP
   notes, tensor-parallel recap).
+* "zwxr 246059" -- www.zwxr.cn/news/246059 (Megatron's gradient
+  synchronisation across parallel modes; its section 4.3 sums the LayerNorm
+  gradients of sequence-parallel regions over the tensor-parallel group).
 
 Parity status of each function is listed in ``PINS`` below; a function with
 no independent pin says "parity unpinned".

@@ -36,6 +36,7 @@ __all__ = [
     "tied_logits", "tied_logits_backward",
     "vocab_ce_forward", "vocab_ce_backward",
     "column_linear_forward", "column_linear_backward", "row_linear_forward", "row_linear_backward",
+    "sp_reduce_scatter", "sp_all_gather", "sp_layernorm_param_grads",
     "layernorm_forward", "layernorm_backward",
     "param_count", "param_count_tied_unique",
     "round_to_bf16", "round_to_f32", "bf16_next_up",
@@ -67,6 +68,9 @@ PINS = {
     "row_linear_forward": "scalar-loop brute force; scattered and parallel inputs agree; "
                           "bias added once after the sum",
     "row_linear_backward": "central finite differences; gathered dX_r = unsharded dX",
+    "sp_reduce_scatter": "scalar-loop brute force; all_gather(reduce_scatter) = the all-reduce",
+    "sp_all_gather": "inverse of the row split; composition with reduce_scatter",
+    "sp_layernorm_param_grads": "summed shard gradients = the unsharded LayerNorm's; finite differences",
     "layernorm_forward": "mean 0 / variance 1 invariants and scalar-loop brute force",
     "layernorm_backward": "central finite differences",
     "param_count": "page value 2,827,821,056 for H=4096, L=12, V=50257",
@@ -402,6 +406,50 @@ def tied_logits_backward(X, E_r, dL_r):
     updated with their sum; the total is ``dE_r + vocab_embed_backward(...)``.
     """
     return dL_r @ E_r, dL_r.T @ X
+
+
+# ---------------------------------------------------------------------------
+# Sequence parallelism: activations outside the tensor-parallel GEMMs are
+# split along the sequence (rows), s/N per shard (page "5-megatron", the
+# schedule's note that the sequence component becomes s/N; page
+# "zwxr 246059", section 4.3: the LayerNorm gradients of sequence-parallel
+# regions are summed over the tensor-parallel group).  The row split follows
+# ``partition``.
+# ---------------------------------------------------------------------------
+
+def sp_reduce_scatter(parts, n, res=None):
+    """The reduce-scatter that replaces the g all-reduce: shard r receives its
+    rows of sum(parts) (shard order), plus its rows ``res[r]`` of the
+    residual stream when given.  Returns the list of row slices."""
+    total = shard_reduce(parts)
+    M = total.shape[0]
+    out = []
+    for r in range(n):
+        s, c = partition(M, n, r)
+        y = total[s:s + c].copy()
+        if res is not None:
+            y = np.asarray(res[r], dtype=np.float64) + y
+        out.append(y)
+    return out
+
+
+def sp_all_gather(slices):
+    """The all-gather before a column-parallel GEMM: the shards' row slices
+    concatenated in shard order."""
+    return np.concatenate([np.asarray(x, dtype=np.float64) for x in slices], axis=0)
+
+
+def sp_layernorm_param_grads(x_slices, gamma, mean_slices, rstd_slices, dy_slices):
+    """LayerNorm on sequence shards: each shard's (dx_r, dgamma_r, dbeta_r)
+    from its own rows, and the parameter gradients summed over shards in
+    shard order.  Returns (dx slices, dgamma, dbeta)."""
+    dxs, dg, db = [], 0.0, 0.0
+    for x, m, rs, dy in zip(x_slices, mean_slices, rstd_slices, dy_slices):
+        dx, g_r, b_r = layernorm_backward(x, gamma, m, rs, dy)
+        dxs.append(dx)
+        dg = dg + g_r
+        db = db + b_r
+    return dxs, dg, db
 
 
 # ---------------------------------------------------------------------------

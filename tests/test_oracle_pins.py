@@ -709,3 +709,44 @@ def test_linear_backward_finite_difference():
               [dX, np.concatenate(dAs, axis=1), np.concatenate(dbs), np.concatenate(dBs, axis=0), dcs[0]],
               h=1e-6, tol=1e-6)
     assert all(np.array_equal(d, dcs[0]) for d in dcs)   # the replicated bias: same gradient on every shard
+
+
+# ---------------------------------------------------------------- sequence parallelism
+
+@pytest.mark.parametrize("M,n", [(7, 2), (10, 3), (4, 4)])
+def test_sp_reduce_scatter_bruteforce_and_all_gather_is_the_all_reduce(M, n):
+    g = rng(50)
+    H = 5
+    parts = [g.standard_normal((M, H)) for _ in range(n)]
+    res = [g.standard_normal((O.partition(M, n, r)[1], H)) for r in range(n)]
+    sl = O.sp_reduce_scatter(parts, n, res)
+    for r in range(n):
+        s, c = O.partition(M, n, r)
+        for i in range(c):
+            for j in range(H):
+                want = res[r][i, j] + math.fsum(float(p[s + i, j]) for p in parts)
+                assert abs(sl[r][i, j] - want) <= 1e-13
+    # without the residual, gathering the scattered sums gives the all-reduce
+    assert np.allclose(O.sp_all_gather(O.sp_reduce_scatter(parts, n)), O.shard_reduce(parts), rtol=0, atol=1e-14)
+    # the gather inverts the row split
+    x = g.standard_normal((M, H))
+    assert np.array_equal(O.sp_all_gather([x[s:s + c] for s, c in (O.partition(M, n, r) for r in range(n))]), x)
+
+
+def test_sp_layernorm_grads_summed_equal_unsharded_and_fd():
+    g = rng(51)
+    M, H, n = 9, 6, 3
+    x, dy = g.standard_normal((M, H)), g.standard_normal((M, H))
+    gamma, beta = 1 + 0.1 * g.standard_normal(H), 0.1 * g.standard_normal(H)
+    _, mu, rs = O.layernorm_forward(x, gamma, beta)
+    dx, dg, db = O.layernorm_backward(x, gamma, mu, rs, dy)
+    rows = [O.partition(M, n, r) for r in range(n)]
+    dxs, dg2, db2 = O.sp_layernorm_param_grads([x[s:s + c] for s, c in rows], gamma,
+                                               [mu[s:s + c] for s, c in rows], [rs[s:s + c] for s, c in rows],
+                                               [dy[s:s + c] for s, c in rows])
+    assert np.allclose(np.concatenate(dxs), dx, rtol=1e-13, atol=1e-13)
+    assert np.allclose(dg2, dg, rtol=1e-13, atol=1e-13) and np.allclose(db2, db, rtol=1e-13, atol=1e-13)
+
+    def loss():
+        return float(np.sum(dy * O.layernorm_forward(x, gamma, beta)[0]))
+    _fd_check(loss, [gamma, beta], [dg2, db2], h=1e-6, tol=1e-6)
