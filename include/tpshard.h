@@ -232,6 +232,34 @@ tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, i
                            void* dX_r, float* dE_r, tps_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Sequence parallelism on one device (page "5-megatron": in sequence
+ * parallel regions the sequence component of an activation becomes s/N per
+ * shard; page "zwxr 246059", section 4.3: those regions' LayerNorm
+ * gradients are summed over the tensor-parallel group, which is
+ * shard_reduce over the shards' [H] fp32 dgamma / dbeta).  The M rows of an
+ * [M x H] activation are split as tps_partition(M, n_parts, r): shard r holds
+ * rows [start_r, start_r + count_r) in its own [count_r x H] buffer.
+ *
+ * shard_reduce_scatter: the reduce-scatter replacing the g all-reduce after a
+ *   row-parallel GEMM: outs[r] = res[r] + (sum over k of parts[k]) restricted
+ *   to shard r's rows (fp32, the residual first, then the parts in shard
+ *   order; one rounding to out_dt).  parts: n_parts full [M x H] partials of
+ *   part_dt; res: NULL, or n_parts residual slices of out_dt (res[r] may be
+ *   outs[r]); outs: n_parts slices of out_dt.
+ * shard_all_gather: out [M x H] = the shards' slices parts[r] stacked in shard
+ *   order (the all-gather before a column-parallel GEMM).
+ * Both: host arrays of n_parts (1..8) device pointers, 16-byte aligned;
+ * M > 0, H a positive multiple of 8; a shard with no rows (M < n_parts) is
+ * never touched and may pass NULL for its slice (and residual).
+ * Errors: TPS_EINVAL before anything is enqueued.
+ * ------------------------------------------------------------------------ */
+tps_status shard_reduce_scatter(tps_dtype part_dt, tps_dtype out_dt, int n_parts, const void* const* parts,
+                                const void* const* res, void* const* outs, int64_t M, int64_t H,
+                                tps_stream_t stream);
+tps_status shard_all_gather(tps_dtype dt, int n_parts, const void* const* parts, void* out, int64_t M, int64_t H,
+                            tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * The two linear layers on their own (page "5-megatron", sections
  * ColumnParallelLinear and RowParallelLinear), math layout Y = X A + b, one
  * shard per call; dt is TPS_BF16 or TPS_F32 for every matrix and bias.

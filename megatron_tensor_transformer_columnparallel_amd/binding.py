@@ -42,6 +42,9 @@ SIGNATURES = {
     "vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tied_logits": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "shard_reduce_scatter": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_vp), _i64, _i64, _vp]),
+    "shard_all_gather": (_i32, [_i32, _i32, ctypes.POINTER(_vp), _vp, _i64, _i64, _vp]),
     "column_linear_fwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
     "column_linear_bwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
     "row_linear_fwd": (_i32, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
@@ -291,6 +294,43 @@ def tied_logits_bwd(X, E_r, dL_r, dX_r, dE_r, stream=None):
     assert dL_r.shape == (T, v_rows) and dL_r.stride(1) == 1 and dE_r.dtype == torch.float32
     _check(lib.tied_logits_bwd(dt, T, H, v_rows, dL_r.stride(0), _p(X), _p(E_r), _p(dL_r), _p(dX_r), _p(dE_r),
                                _stream(stream)), "tied_logits_bwd")
+
+
+# ------------------------------------------------------------------ sequence parallelism
+
+def shard_reduce_scatter(parts, outs, res=None, stream=None):
+    """outs[r] <- (res[r] +) shard r's rows of sum(parts); rows split as tps_partition(M, n, r)."""
+    n = len(parts)
+    if not 1 <= n <= 8 or len(outs) != n or (res is not None and len(res) != n):
+        raise ValueError("1..8 parts, one output (and residual) per part")
+    pdt, odt = _dt(parts[0]), _dt(outs[0])
+    _same(pdt, *parts)
+    _same(odt, *outs, *(res or []))
+    _contig(*parts, *outs, *(res or []))
+    M, H = parts[0].shape
+    for r in range(n):
+        _, c = tps_partition(M, n, r)
+        assert parts[r].shape == (M, H) and outs[r].shape == (c, H)
+        if res is not None:
+            assert res[r].shape == (c, H)
+    arr = lambda ts: (_vp * n)(*[_p(t) for t in ts])
+    _check(lib.shard_reduce_scatter(pdt, odt, n, arr(parts), arr(res) if res is not None else None, arr(outs), M, H,
+                                    _stream(stream)), "shard_reduce_scatter")
+
+
+def shard_all_gather(parts, out, stream=None):
+    """out [M x H] <- the shards' row slices stacked in shard order."""
+    n = len(parts)
+    if not 1 <= n <= 8:
+        raise ValueError("1..8 parts")
+    dt = _dt(out)
+    _same(dt, *parts)
+    _contig(out, *parts)
+    M, H = out.shape
+    for r in range(n):
+        assert parts[r].shape == (tps_partition(M, n, r)[1], H)
+    arr = (_vp * n)(*[_p(t) for t in parts])
+    _check(lib.shard_all_gather(dt, n, arr, _p(out), M, H, _stream(stream)), "shard_all_gather")
 
 
 # ------------------------------------------------------------------ column / row parallel linear

@@ -35,7 +35,7 @@ def test_header_declares_the_path():
                  "layernorm_fwd", "layernorm_bwd", "tps_partition",
                  "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_bwd",
                  "column_linear_fwd", "column_linear_bwd", "row_linear_fwd", "row_linear_bwd",
-                 "shard_reduce_bias"]:
+                 "shard_reduce_bias", "shard_reduce_scatter", "shard_all_gather"]:
         assert must in names
 
 
@@ -194,3 +194,19 @@ def test_shard_reduce_bias_validation(tp):
     assert lib.shard_reduce_bias(1, 2, arr, ALIGNED, ALIGNED, 4, 12, None) == tp.binding.TPS_EINVAL   # N % 8
     assert lib.shard_reduce_bias(1, 2, arr, None, ALIGNED, 4, 16, None) == tp.binding.TPS_EINVAL      # null bias
     assert lib.tps_last_error().startswith(b"shard_reduce_bias")
+
+
+def test_sequence_parallel_exchange_validation(tp):
+    lib = tp.lib
+    arr = (ctypes.c_void_p * 9)(*([ALIGNED] * 9))
+    bad = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED + 4)
+    E = tp.binding.TPS_EINVAL
+    assert lib.shard_reduce_scatter(1, 1, 0, arr, None, arr, 8, 16, None) == E          # n_parts = 0
+    assert lib.shard_reduce_scatter(1, 1, 2, arr, None, arr, 8, 12, None) == E          # H % 8
+    assert lib.shard_reduce_scatter(1, 1, 2, arr, None, bad, 8, 16, None) == E          # misaligned slice
+    assert lib.shard_reduce_scatter(5, 1, 2, arr, None, arr, 8, 16, None) == E          # dtype
+    assert lib.tps_last_error().startswith(b"shard_reduce_scatter")
+    assert lib.shard_all_gather(1, 9, arr, ALIGNED, 8, 16, None) == E                   # n_parts = 9
+    assert lib.shard_all_gather(1, 2, arr, None, 8, 16, None) == E                      # null out
+    assert lib.shard_all_gather(1, 2, bad, ALIGNED, 8, 16, None) == E                   # misaligned part
+    assert lib.tps_last_error().startswith(b"shard_all_gather")
