@@ -242,6 +242,48 @@ def ce_bench(tp, torch, reps=20):
     return res
 
 
+def sp_bench(tp, torch, reps=20):
+    """HBM rates of the sequence-parallel exchanges at T = 8*2048 tokens,
+    H = 4096, 2 shards: the reduce-scatter of two bf16 partials onto the fp32
+    residual rows of each shard, and the all-gather of two bf16 row slices.
+    Three buffer sets rotated past the last-level cache."""
+    T, H, n = 8 * 2048, 4096, 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4300)
+    rows = [tp.tps_partition(T, n, r)[1] for r in range(n)]
+    sets = []
+    for _ in range(3):
+        parts = [torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(n)]
+        res = [torch.randn((c, H), generator=g, device="cuda") for c in rows]
+        outs = [torch.empty((c, H), device="cuda") for c in rows]
+        sl = [torch.randn((c, H), generator=g, device="cuda").to(torch.bfloat16) for c in rows]
+        full = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        sets.append((parts, res, outs, sl, full))
+    res_ = {}
+    for name, fn, nbytes in [
+        ("shard_reduce_scatter (2 bf16 partials + fp32 residual -> fp32)",
+         lambda s: tp.shard_reduce_scatter(s[0], s[2], res=s[1]), n * T * H * 2 + 2 * T * H * 4),
+        ("shard_all_gather (2 bf16 slices)", lambda s: tp.shard_all_gather(s[3], s[4]), 2 * T * H * 2),
+    ]:
+        for st in sets:
+            fn(st)
+        torch.cuda.synchronize()
+        ev = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(sets[i % 3])
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res_[name] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                      "bytes": nbytes}
+    res_["shape"] = {"T": T, "H": H, "shards": n}
+    return res_
+
+
 def linear_bench(tp, torch, reps=10):
     """The two linear layers on their own at the layer's MLP shard shape
     (M = 2048 tokens, h = 4096, 4h split over 2 shards = 8192 columns each),
@@ -342,6 +384,7 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the single-layer step")
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy kernel rates")
     ap.add_argument("--no-linear", action="store_true", help="skip the standalone linear-layer rates")
+    ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel exchange rates")
     ap.add_argument("--calib", action="store_true", help="one 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -437,6 +480,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_linear:
         out["linear"] = linear_bench(tp, torch)
+        torch.cuda.empty_cache()
+    if not args.no_sp:
+        out["sequence_parallel"] = sp_bench(tp, torch)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
