@@ -37,6 +37,7 @@ __all__ = [
     "vocab_ce_forward", "vocab_ce_backward",
     "column_linear_forward", "column_linear_backward", "row_linear_forward", "row_linear_backward",
     "sp_reduce_scatter", "sp_all_gather", "sp_layernorm_param_grads",
+    "philox4x32_10", "dropout_keep", "embedding_forward", "embedding_backward",
     "layernorm_forward", "layernorm_backward",
     "param_count", "param_count_tied_unique",
     "round_to_bf16", "round_to_f32", "bf16_next_up",
@@ -71,6 +72,10 @@ PINS = {
     "sp_reduce_scatter": "scalar-loop brute force; all_gather(reduce_scatter) = the all-reduce",
     "sp_all_gather": "inverse of the row split; composition with reduce_scatter",
     "sp_layernorm_param_grads": "summed shard gradients = the unsharded LayerNorm's; finite differences",
+    "philox4x32_10": "the generator's published known-answer vectors (tests/golden/philox4x32_10_kat.json)",
+    "dropout_keep": "p = 0 keeps all; kept fraction within 5 sigma of 1 - p; word/element mapping by brute force",
+    "embedding_forward": "p = 0 equals the scalar sum of the rows; out-of-range ids add zero rows",
+    "embedding_backward": "central finite differences at a fixed mask",
     "layernorm_forward": "mean 0 / variance 1 invariants and scalar-loop brute force",
     "layernorm_backward": "central finite differences",
     "param_count": "page value 2,827,821,056 for H=4096, L=12, V=50257",
@@ -406,6 +411,84 @@ def tied_logits_backward(X, E_r, dL_r):
     updated with their sum; the total is ``dE_r + vocab_embed_backward(...)``.
     """
     return dL_r @ E_r, dL_r.T @ X
+
+
+# ---------------------------------------------------------------------------
+# The full input embedding (page "5-megatron", section Embedding): the
+# vocab-parallel word embedding summed over shards, plus the position
+# embedding, plus the token-type embedding when used, then dropout.  The
+# dropout sits after the shard sum, where every shard holds the same values,
+# so it draws the same mask on every shard (page "5-megatron", section 模型并行:
+# seeds differ inside tensor-parallel regions and agree after the
+# all-reduce).  Its random numbers come from the counter-based generator
+# Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+# easy as 1, 2, 3", SC 2011), keyed by a 64-bit seed and counted by element.
+# ---------------------------------------------------------------------------
+
+_PHILOX_M = (np.uint64(0xD2511F53), np.uint64(0xCD9E8D57))
+_PHILOX_W = (np.uint64(0x9E3779B9), np.uint64(0xBB67AE85))
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32 with 10 rounds.  ``ctr``: array [..., 4] of uint32 words,
+    ``key``: two uint32 words.  Each round multiplies words 0 and 2 by the
+    two round multipliers into 64-bit products, and the new counter is
+    (hi(w2*M1) ^ c1 ^ k0, lo(w2*M1), hi(w0*M0) ^ c3 ^ k1, lo(w0*M0)); the key
+    then advances by the two Weyl constants.  Returns [..., 4] uint32."""
+    c = np.asarray(ctr, dtype=np.uint64) & _U32
+    c0, c1, c2, c3 = c[..., 0], c[..., 1], c[..., 2], c[..., 3]
+    k0, k1 = np.uint64(key[0]) & _U32, np.uint64(key[1]) & _U32
+    for _ in range(10):
+        p0, p1 = _PHILOX_M[0] * c0, _PHILOX_M[1] * c2
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _U32,
+                          (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & _U32)
+        k0, k1 = (k0 + _PHILOX_W[0]) & _U32, (k1 + _PHILOX_W[1]) & _U32
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def dropout_keep(n, p, seed):
+    """Keep mask of n elements (flat index e): the words of Philox4x32-10 at
+    counter (e // 4 low word, e // 4 high word, 0, 0) with key (seed low,
+    seed high); element e takes word e % 4 and is dropped when that word is
+    below floor(p * 2^32) (p a float32; p = 0 drops nothing)."""
+    n = int(n)
+    nb = (n + 3) // 4
+    blk = np.arange(nb, dtype=np.uint64)
+    ctr = np.stack([blk & _U32, blk >> np.uint64(32), np.zeros(nb, np.uint64), np.zeros(nb, np.uint64)], axis=-1)
+    words = philox4x32_10(ctr, (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF)).reshape(-1)[:n]
+    thr = min(int(float(np.float32(p)) * 4294967296.0), 0xFFFFFFFF)
+    return words.astype(np.uint64) >= np.uint64(thr)
+
+
+def embedding_forward(word_parts, PE, pos, p, seed, TE=None, tt=None):
+    """out[t] = dropout(sum_r word_parts[r][t] + PE[pos[t]] (+ TE[tt[t]])):
+    kept elements are scaled by 1 / (1 - p).  A position or token-type id
+    outside its table contributes a zero row (the vocabulary's masking rule).
+    Returns (out, keep mask [T x H])."""
+    x = shard_reduce(word_parts)
+    T, H = x.shape
+    for table, ids in ((PE, pos), (TE, tt)):
+        if table is None:
+            continue
+        ids = np.asarray(ids, dtype=np.int64)
+        ok = (ids >= 0) & (ids < table.shape[0])
+        rows = np.zeros((T, H))
+        rows[ok] = np.asarray(table, dtype=np.float64)[ids[ok]]
+        x = x + rows
+    keep = dropout_keep(T * H, p, seed).reshape(T, H)
+    return np.where(keep, x / (1.0 - float(np.float32(p))), 0.0), keep
+
+
+def embedding_backward(dout, keep, p, pos, pos_rows, tt=None, tt_rows=0):
+    """Gradients of ``embedding_forward``: dX = dout * keep / (1 - p) is the
+    word embedding's upstream gradient (vocab_embed_backward per shard), and
+    the position and token-type tables receive its rows summed by id.
+    Returns (dX, dPE, dTE or None)."""
+    dX = np.where(keep, np.asarray(dout, dtype=np.float64) / (1.0 - float(np.float32(p))), 0.0)
+    dPE = vocab_embed_backward(pos, dX, 0, pos_rows)
+    dTE = vocab_embed_backward(tt, dX, 0, tt_rows) if tt is not None else None
+    return dX, dPE, dTE
 
 
 # ---------------------------------------------------------------------------

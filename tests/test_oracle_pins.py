@@ -750,3 +750,66 @@ def test_sp_layernorm_grads_summed_equal_unsharded_and_fd():
     def loss():
         return float(np.sum(dy * O.layernorm_forward(x, gamma, beta)[0]))
     _fd_check(loss, [gamma, beta], [dg2, db2], h=1e-6, tol=1e-6)
+
+
+# ---------------------------------------------------------------- full embedding, dropout generator
+
+def test_philox_known_answer_vectors():
+    for case in golden("philox4x32_10_kat.json")["cases"]:
+        ctr = [int(x, 16) for x in case["ctr"]]
+        key = [int(x, 16) for x in case["key"]]
+        out = O.philox4x32_10(np.array([ctr], dtype=np.uint64), key)[0]
+        assert [int(x) for x in out] == [int(x, 16) for x in case["out"]]
+
+
+def test_dropout_keep_mapping_and_rate():
+    seed = 0x1234_5678_9ABC_DEF0
+    n = 10
+    keep = O.dropout_keep(n, 0.5, seed)
+    thr = int(float(np.float32(0.5)) * 2 ** 32)
+    for e in range(n):      # element e uses word e % 4 of the block e // 4
+        w = O.philox4x32_10(np.array([[e // 4, 0, 0, 0]], dtype=np.uint64),
+                            (seed & 0xFFFFFFFF, seed >> 32))[0][e % 4]
+        assert keep[e] == (int(w) >= thr)
+    assert O.dropout_keep(1000, 0.0, seed).all()
+    for p in (0.1, 0.5, 0.9):
+        n = 200_000
+        k = O.dropout_keep(n, p, 77).mean()
+        assert abs(k - (1 - p)) <= 5 * math.sqrt(p * (1 - p) / n)
+
+
+def test_embedding_forward_closed_form_and_masking():
+    g = rng(60)
+    T, H, V, P, n = 6, 4, 10, 5, 2
+    E = g.standard_normal((V, H))
+    PE, TE = g.standard_normal((P, H)), g.standard_normal((3, H))
+    ids = np.array([0, 3, 9, 5, 2, 7])
+    pos = np.array([0, 1, 2, 3, 4, 7])      # 7 lies outside the position table: a zero row
+    tt = np.array([0, 1, 2, 1, 0, 1])
+    parts = [O.vocab_embed_forward(ids, E[s:s + c], s) for s, c in (O.partition(V, n, r) for r in range(n))]
+    out, keep = O.embedding_forward(parts, PE, pos, 0.0, 5, TE, tt)
+    assert keep.all()
+    for t in range(T):
+        for h in range(H):
+            want = E[ids[t], h] + (PE[pos[t], h] if pos[t] < P else 0.0) + TE[tt[t], h]
+            assert abs(out[t, h] - want) <= 1e-14
+    out2, keep2 = O.embedding_forward(parts, PE, pos, 0.3, 5, TE, tt)
+    assert np.allclose(out2[keep2], (out / 0.7)[keep2], rtol=1e-6) and np.all(out2[~keep2] == 0)
+
+
+def test_embedding_backward_finite_difference():
+    g = rng(61)
+    T, H, V, P, n, p = 5, 3, 8, 6, 2, 0.25
+    E, PE, TE = g.standard_normal((V, H)), g.standard_normal((P, H)), g.standard_normal((2, H))
+    ids, pos, tt = g.integers(0, V, T), g.integers(0, P, T), g.integers(0, 2, T)
+    R = g.standard_normal((T, H))
+    sc = [O.partition(V, n, r) for r in range(n)]
+
+    def loss():
+        parts = [O.vocab_embed_forward(ids, E[s:s + c], s) for s, c in sc]
+        return float(np.sum(R * O.embedding_forward(parts, PE, pos, p, 9, TE, tt)[0]))
+    parts = [O.vocab_embed_forward(ids, E[s:s + c], s) for s, c in sc]
+    _, keep = O.embedding_forward(parts, PE, pos, p, 9, TE, tt)
+    dX, dPE, dTE = O.embedding_backward(R, keep, p, pos, P, tt, 2)
+    dE = np.concatenate([O.vocab_embed_backward(ids, dX, s, c) for s, c in sc])
+    _fd_check(loss, [E, PE, TE], [dE, dPE, dTE], h=1e-6, tol=1e-6)
