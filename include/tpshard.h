@@ -232,6 +232,44 @@ tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, i
                            void* dX_r, float* dE_r, tps_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The full input embedding (page "5-megatron", section Embedding) and
+ * dropout.  Dropout uses the counter-based generator Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC
+ * 2011): element e of a call (flat index) takes word e % 4 of Philox4x32-10
+ * at counter (low and high words of e / 4, 0, 0) with key (low and high
+ * words of seed), and is dropped when that word is below floor(p * 2^32);
+ * kept elements are scaled by 1 / (1 - p) (fp32).  The same (seed, element)
+ * always gives the same decision, so a backward regenerates the mask.  Per
+ * the pages, callers use one seed for every shard after a shard sum (the
+ * mask must agree) and a different seed per shard inside a tensor-parallel
+ * region.
+ *
+ * embedding_fwd: out[t] = dropout(sum over shards of word_parts[r][t]
+ *   + PE[pos[t]] + TE[tt[t]]), the sum in fp32 in shard order.
+ *   word_parts: host array of n_parts (1..8) device pointers to the shards'
+ *   vocab_embed_fwd outputs [T x H] of dt; PE [pos_rows x H] of dt; pos [T]
+ *   int32; TE [tt_rows x H] of dt with tt [T] int32, or TE = NULL (no
+ *   token types); an id outside its table adds a zero row.  out [T x H] of
+ *   out_dt.  p in [0, 1) (0: no dropout, no generator).
+ * dropout_apply: y[e] = keep(e) ? x[e] / (1 - p) : 0 over n elements of
+ *   in_dt -> out_dt (y may be x when the dtypes match).  With the forward's
+ *   p and seed applied to the output gradient it is the dropout backward;
+ *   the result is then the gradient of the summed embedding, i.e. the dY of
+ *   vocab_embed_bwd for every shard's word table, and, with pos (tt) as the
+ *   ids, v_start 0 and pos_rows (tt_rows) rows, the position (token-type)
+ *   table's gradient through vocab_embed_bwd.
+ * Dimensions: T >= 0, H a positive multiple of 8; pointers 16-byte aligned.
+ * Errors: TPS_EINVAL (bad dtype, p outside [0, 1), null or misaligned
+ * pointers, bad sizes) before anything is enqueued.
+ * ------------------------------------------------------------------------ */
+tps_status embedding_fwd(tps_dtype dt, tps_dtype out_dt, int n_parts, const void* const* word_parts,
+                         const void* PE, int64_t pos_rows, const int32_t* pos, const void* TE, int64_t tt_rows,
+                         const int32_t* tt, float p, uint64_t seed, void* out, int64_t T, int64_t H,
+                         tps_stream_t stream);
+tps_status dropout_apply(tps_dtype in_dt, tps_dtype out_dt, int64_t n, const void* x, float p, uint64_t seed,
+                         void* y, tps_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Sequence parallelism on one device (page "5-megatron": in sequence
  * parallel regions the sequence component of an activation becomes s/N per
  * shard; page "zwxr 246059", section 4.3: those regions' LayerNorm

@@ -16,6 +16,6 @@ from .binding import (  # noqa: F401
     tied_logits, tied_logits_bwd,
     vocab_ce_stats, vocab_ce_combine, vocab_ce_bwd,
     column_linear_fwd, column_linear_bwd, row_linear_fwd, row_linear_bwd, shard_reduce_bias,
-    shard_reduce_scatter, shard_all_gather,
+    shard_reduce_scatter, shard_all_gather, embedding_fwd, dropout_apply,
     layernorm_fwd, layernorm_bwd, layernorm_bwd_workspace, layernorm_bwd_residual,
 )

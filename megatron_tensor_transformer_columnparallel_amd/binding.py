@@ -42,6 +42,9 @@ SIGNATURES = {
     "vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tied_logits": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "embedding_fwd": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), _vp, _i64, _vp, _vp, _i64, _vp, _f32,
+                             ctypes.c_uint64, _vp, _i64, _i64, _vp]),
+    "dropout_apply": (_i32, [_i32, _i32, _i64, _vp, _f32, ctypes.c_uint64, _vp, _vp]),
     "shard_reduce_scatter": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                     ctypes.POINTER(_vp), _i64, _i64, _vp]),
     "shard_all_gather": (_i32, [_i32, _i32, ctypes.POINTER(_vp), _vp, _i64, _i64, _vp]),
@@ -294,6 +297,34 @@ def tied_logits_bwd(X, E_r, dL_r, dX_r, dE_r, stream=None):
     assert dL_r.shape == (T, v_rows) and dL_r.stride(1) == 1 and dE_r.dtype == torch.float32
     _check(lib.tied_logits_bwd(dt, T, H, v_rows, dL_r.stride(0), _p(X), _p(E_r), _p(dL_r), _p(dX_r), _p(dE_r),
                                _stream(stream)), "tied_logits_bwd")
+
+
+# ------------------------------------------------------------------ full embedding, dropout
+
+def embedding_fwd(word_parts, PE, pos, out, p=0.0, seed=0, TE=None, tt=None, stream=None):
+    """out <- dropout(sum(word_parts) + PE[pos] (+ TE[tt])) with Philox4x32-10 keyed by seed."""
+    n = len(word_parts)
+    if not 1 <= n <= 8:
+        raise ValueError("1..8 word partials")
+    dt = _dt(word_parts[0])
+    _same(dt, PE, *word_parts, *([TE] if TE is not None else []))
+    _contig(out, PE, pos, *word_parts, *([TE, tt] if TE is not None else []))
+    T, H = out.shape
+    assert all(w.shape == (T, H) for w in word_parts) and PE.shape[1] == H and pos.dtype == torch.int32
+    if TE is not None:
+        assert TE.shape[1] == H and tt is not None and tt.dtype == torch.int32
+    arr = (_vp * n)(*[_p(w) for w in word_parts])
+    _check(lib.embedding_fwd(dt, _dt(out), n, arr, _p(PE), PE.shape[0], _p(pos), _p(TE),
+                             TE.shape[0] if TE is not None else 0, _p(tt), float(p), int(seed), _p(out), T, H,
+                             _stream(stream)), "embedding_fwd")
+
+
+def dropout_apply(x, y, p, seed, stream=None):
+    """y <- keep ? x / (1 - p) : 0 (the mask from seed and element index); also the backward."""
+    _contig(x, y)
+    assert x.numel() == y.numel()
+    _check(lib.dropout_apply(_dt(x), _dt(y), x.numel(), _p(x), float(p), int(seed), _p(y), _stream(stream)),
+           "dropout_apply")
 
 
 # ------------------------------------------------------------------ sequence parallelism

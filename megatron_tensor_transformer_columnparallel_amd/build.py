@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
-SOURCES = ["runtime.hip", "reduce.hip", "embed.hip", "mlp.hip", "attn.hip", "layernorm.hip", "ce.hip", "linear.hip", "sp.hip"]
+SOURCES = ["runtime.hip", "reduce.hip", "embed.hip", "mlp.hip", "attn.hip", "layernorm.hip", "ce.hip", "linear.hip", "sp.hip", "embedding.hip"]
 ARCH = "gfx950"
 
 

@@ -35,7 +35,8 @@ def test_header_declares_the_path():
                  "layernorm_fwd", "layernorm_bwd", "tps_partition",
                  "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_bwd",
                  "column_linear_fwd", "column_linear_bwd", "row_linear_fwd", "row_linear_bwd",
-                 "shard_reduce_bias", "shard_reduce_scatter", "shard_all_gather"]:
+                 "shard_reduce_bias", "shard_reduce_scatter", "shard_all_gather",
+                 "embedding_fwd", "dropout_apply"]:
         assert must in names
 
 
@@ -210,3 +211,21 @@ def test_sequence_parallel_exchange_validation(tp):
     assert lib.shard_all_gather(1, 2, arr, None, 8, 16, None) == E                      # null out
     assert lib.shard_all_gather(1, 2, bad, ALIGNED, 8, 16, None) == E                   # misaligned part
     assert lib.tps_last_error().startswith(b"shard_all_gather")
+
+
+def test_embedding_and_dropout_validation(tp):
+    lib = tp.lib
+    arr = (ctypes.c_void_p * 2)(ALIGNED, ALIGNED)
+    E = tp.binding.TPS_EINVAL
+    args = [1, 1, 2, arr, ALIGNED, 64, ALIGNED, None, 0, None, 0.1, 7, ALIGNED, 16, 64, None]
+    for i, bad in [(10, 1.0), (10, -0.5), (14, 60), (5, 0), (4, None), (12, ALIGNED + 2), (2, 9)]:
+        a = list(args)
+        a[i] = bad
+        if i == 4:
+            a[4] = None
+        assert lib.embedding_fwd(*a) == E, (i, bad)
+    assert lib.tps_last_error().startswith(b"embedding_fwd")
+    assert lib.dropout_apply(1, 1, 16, ALIGNED, 1.0, 3, ALIGNED, None) == E                      # p = 1
+    assert lib.dropout_apply(1, 1, 16, ALIGNED + 8, 0.5, 3, ALIGNED, None) == E                  # misaligned
+    assert lib.dropout_apply(1, 1, -1, ALIGNED, 0.5, 3, ALIGNED, None) == E                      # n < 0
+    assert lib.tps_last_error().startswith(b"dropout_apply")
