@@ -242,6 +242,48 @@ def ce_bench(tp, torch, reps=20):
     return res
 
 
+def full_embedding_bench(tp, torch, reps=20):
+    """HBM rates of the full input embedding at T = 8*2048 tokens, H = 4096,
+    2 shards, 2048 positions, dropout p = 0.1, fp32 output (the residual
+    stream): the fused shard sum + position rows + dropout, and the dropout
+    backward on an fp32 gradient.  Three buffer sets rotated."""
+    T, H, P, n, p = 8 * 2048, 4096, 2048, 2, 0.1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4400)
+    pos = (torch.arange(T, device="cuda", dtype=torch.int32) % P).contiguous()
+    PE = (torch.randn((P, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    sets = []
+    for _ in range(3):
+        parts = [torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(n)]
+        out = torch.empty((T, H), device="cuda")
+        dout = torch.randn((T, H), generator=g, device="cuda")
+        dx = torch.empty((T, H), device="cuda")
+        sets.append((parts, out, dout, dx))
+    res = {}
+    for name, fn, nbytes in [
+        ("embedding_fwd (2 bf16 shard partials + position rows + dropout -> fp32)",
+         lambda s: tp.embedding_fwd(s[0], PE, pos, s[1], p=p, seed=11), n * T * H * 2 + P * H * 2 + 4 * T + T * H * 4),
+        ("dropout_apply (fp32 gradient)", lambda s: tp.dropout_apply(s[2], s[3], p, 11), 2 * T * H * 4),
+    ]:
+        for st in sets:
+            fn(st)
+        torch.cuda.synchronize()
+        ev = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(sets[i % 3])
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes": nbytes}
+    res["shape"] = {"T": T, "H": H, "positions": P, "shards": n, "p": p}
+    return res
+
+
 def sp_bench(tp, torch, reps=20):
     """HBM rates of the sequence-parallel exchanges at T = 8*2048 tokens,
     H = 4096, 2 shards: the reduce-scatter of two bf16 partials onto the fp32
@@ -385,6 +427,7 @@ def main():
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy kernel rates")
     ap.add_argument("--no-linear", action="store_true", help="skip the standalone linear-layer rates")
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel exchange rates")
+    ap.add_argument("--no-full-embed", action="store_true", help="skip the full-embedding and dropout rates")
     ap.add_argument("--calib", action="store_true", help="one 512 MiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -483,6 +526,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_sp:
         out["sequence_parallel"] = sp_bench(tp, torch)
+        torch.cuda.empty_cache()
+    if not args.no_full_embed:
+        out["full_embedding"] = full_embedding_bench(tp, torch)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
