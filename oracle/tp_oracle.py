@@ -37,7 +37,7 @@ __all__ = [
     "vocab_ce_forward", "vocab_ce_backward",
     "column_linear_forward", "column_linear_backward", "row_linear_forward", "row_linear_backward",
     "sp_reduce_scatter", "sp_all_gather", "sp_layernorm_param_grads",
-    "philox4x32_10", "dropout_keep", "embedding_forward", "embedding_backward",
+    "philox4x32_10", "dropout_keep", "dropout_keep_at", "embedding_forward", "embedding_backward",
     "layernorm_forward", "layernorm_backward",
     "param_count", "param_count_tied_unique",
     "round_to_bf16", "round_to_f32", "bf16_next_up",
@@ -74,6 +74,7 @@ PINS = {
     "sp_layernorm_param_grads": "summed shard gradients = the unsharded LayerNorm's; finite differences",
     "philox4x32_10": "the generator's published known-answer vectors (tests/golden/philox4x32_10_kat.json)",
     "dropout_keep": "p = 0 keeps all; kept fraction within 5 sigma of 1 - p; word/element mapping by brute force",
+    "dropout_keep_at": "indices past 2^34 (a nonzero high counter word) against direct generator calls; sampled rows of the embedding equal the full call's",
     "embedding_forward": "p = 0 equals the scalar sum of the rows; out-of-range ids add zero rows",
     "embedding_backward": "central finite differences at a fixed mask",
     "layernorm_forward": "mean 0 / variance 1 invariants and scalar-loop brute force",
@@ -447,25 +448,34 @@ def philox4x32_10(ctr, key):
     return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
 
 
-def dropout_keep(n, p, seed):
-    """Keep mask of n elements (flat index e): the words of Philox4x32-10 at
-    counter (e // 4 low word, e // 4 high word, 0, 0) with key (seed low,
-    seed high); element e takes word e % 4 and is dropped when that word is
-    below floor(p * 2^32) (p a float32; p = 0 drops nothing)."""
-    n = int(n)
-    nb = (n + 3) // 4
-    blk = np.arange(nb, dtype=np.uint64)
-    ctr = np.stack([blk & _U32, blk >> np.uint64(32), np.zeros(nb, np.uint64), np.zeros(nb, np.uint64)], axis=-1)
-    words = philox4x32_10(ctr, (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF)).reshape(-1)[:n]
+def dropout_keep_at(elems, p, seed):
+    """Keep decisions of the elements with flat indices ``elems`` (any shape):
+    element e takes word e % 4 of Philox4x32-10 at counter (e // 4 low word,
+    e // 4 high word, 0, 0) with key (seed low, seed high), and is dropped
+    when that word is below floor(p * 2^32) (p a float32; p = 0 drops
+    nothing)."""
+    e = np.asarray(elems, dtype=np.uint64)
+    blk = e >> np.uint64(2)
+    z = np.zeros(blk.shape, np.uint64)
+    ctr = np.stack([blk & _U32, blk >> np.uint64(32), z, z], axis=-1)
+    words = philox4x32_10(ctr, (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF))
+    w = np.take_along_axis(words, (e & np.uint64(3)).astype(np.int64)[..., None], axis=-1)[..., 0]
     thr = min(int(float(np.float32(p)) * 4294967296.0), 0xFFFFFFFF)
-    return words.astype(np.uint64) >= np.uint64(thr)
+    return w.astype(np.uint64) >= np.uint64(thr)
 
 
-def embedding_forward(word_parts, PE, pos, p, seed, TE=None, tt=None):
+def dropout_keep(n, p, seed):
+    """Keep mask of the n elements 0 .. n-1 of one call (``dropout_keep_at``)."""
+    return dropout_keep_at(np.arange(int(n), dtype=np.uint64), p, seed)
+
+
+def embedding_forward(word_parts, PE, pos, p, seed, TE=None, tt=None, tokens=None):
     """out[t] = dropout(sum_r word_parts[r][t] + PE[pos[t]] (+ TE[tt[t]])):
     kept elements are scaled by 1 / (1 - p).  A position or token-type id
     outside its table contributes a zero row (the vocabulary's masking rule).
-    Returns (out, keep mask [T x H])."""
+    ``tokens`` gives the rows' token indices in the full call when the rows
+    are a sample of it (the mask is keyed by flat index token * H + column);
+    by default row t is token t.  Returns (out, keep mask [T x H])."""
     x = shard_reduce(word_parts)
     T, H = x.shape
     for table, ids in ((PE, pos), (TE, tt)):
@@ -476,7 +486,8 @@ def embedding_forward(word_parts, PE, pos, p, seed, TE=None, tt=None):
         rows = np.zeros((T, H))
         rows[ok] = np.asarray(table, dtype=np.float64)[ids[ok]]
         x = x + rows
-    keep = dropout_keep(T * H, p, seed).reshape(T, H)
+    tok = np.arange(T, dtype=np.uint64) if tokens is None else np.asarray(tokens, dtype=np.uint64)
+    keep = dropout_keep_at(tok[:, None] * np.uint64(H) + np.arange(H, dtype=np.uint64)[None, :], p, seed)
     return np.where(keep, x / (1.0 - float(np.float32(p))), 0.0), keep
 
 

@@ -778,6 +778,32 @@ def test_dropout_keep_mapping_and_rate():
         assert abs(k - (1 - p)) <= 5 * math.sqrt(p * (1 - p) / n)
 
 
+def test_dropout_keep_at_high_counter_word_and_sampled_rows():
+    """Element indices past 2^34 put e // 4 above 2^32, so the counter's
+    second word is nonzero: each decision is checked against a direct call of
+    the generator at counter (e // 4 low, e // 4 high, 0, 0).  Sampled rows
+    of the full embedding (``tokens``) take the full call's rows and mask."""
+    seed = 0xFEDC_BA98_7654_3210
+    key = (seed & 0xFFFFFFFF, seed >> 32)
+    elems = np.array([2 ** 34 + 1, 2 ** 34 + 7, 3 * 2 ** 35 + 2, 2 ** 40 + 3, 5], dtype=np.uint64)
+    thr = int(float(np.float32(0.3)) * 2 ** 32)
+    keep = O.dropout_keep_at(elems, 0.3, seed)
+    for k, e in zip(keep, elems.tolist()):
+        b = e // 4
+        w = O.philox4x32_10(np.array([[b & 0xFFFFFFFF, b >> 32, 0, 0]], dtype=np.uint64), key)[0][e % 4]
+        assert k == (int(w) >= thr)
+    assert np.array_equal(O.dropout_keep_at(np.arange(40, dtype=np.uint64), 0.3, seed), O.dropout_keep(40, 0.3, seed))
+    g = rng(62)
+    T, H, P = 9, 8, 5
+    parts = [g.standard_normal((T, H)) for _ in range(2)]
+    PE = g.standard_normal((P, H))
+    pos = np.arange(T) % P
+    full, kf = O.embedding_forward(parts, PE, pos, 0.4, 3)
+    rows = np.array([7, 2, 8])
+    sub, ks = O.embedding_forward([x[rows] for x in parts], PE, pos[rows], 0.4, 3, tokens=rows)
+    assert np.array_equal(sub, full[rows]) and np.array_equal(ks, kf[rows])
+
+
 def test_embedding_forward_closed_form_and_masking():
     g = rng(60)
     T, H, V, P, n = 6, 4, 10, 5, 2
