@@ -46,20 +46,34 @@ tps_status lgemm(const T* A, const T* B, const GemmShape& s, const Epi& e, hipSt
   else return gemm_f32<AK, BKC>(A, B, s, e, st);
 }
 
-// db[n] = sum over m of dY[m, n] in fp32, rows in increasing order within
-// each of 32 row groups, the groups then added in order (fixed, so the
-// result is reproducible).  A workgroup owns 64 columns: 8 lanes of 8
-// columns (one 16-byte bf16 vector or two fp32 vectors) by 32 row groups.
+// db[n] = sum over m of dY[m, n] in fp32, in a fixed order (reproducible,
+// and identical wherever the same dY is reduced): a workgroup owns 64
+// columns (one 128-byte line of bf16 per row); its 1024 threads are 8 lanes
+// of 8 columns by 128 row groups, each group summing rows g, g + 128, ... in
+// increasing order with four rows' loads in flight; then, per column, each
+// run of 8 consecutive groups is summed in order, and the 16 runs in order.
+constexpr int kBgGroups = 128;
 template <typename T>
-__global__ void __launch_bounds__(256) bias_grad_kernel(const T* __restrict__ dY, int64_t ld, int64_t M, int64_t N,
-                                                        float* __restrict__ db) {
-  __shared__ float part[32][65];
+__global__ void __launch_bounds__(1024) bias_grad_kernel(const T* __restrict__ dY, int64_t ld, int64_t M, int64_t N,
+                                                         float* __restrict__ db) {
+  __shared__ float part[kBgGroups][65];
+  __shared__ float run[16][65];
   const int tid = threadIdx.x, cg = tid & 7, rg = tid >> 3;
   const int64_t n = (int64_t)blockIdx.x * 64 + cg * 8;
   const int nv = (int)(N - n < 8 ? (N - n > 0 ? N - n : 0) : 8);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (nv > 0) {
-    for (int64_t m = rg; m < M; m += 32) {
+    int64_t m = rg;
+    for (; m + 3 * kBgGroups < M; m += 4 * kBgGroups) {
+      float v0[8], v1[8], v2[8], v3[8];
+      load8<T>(dY + m * ld + n, v0, nv);
+      load8<T>(dY + (m + kBgGroups) * ld + n, v1, nv);
+      load8<T>(dY + (m + 2 * kBgGroups) * ld + n, v2, nv);
+      load8<T>(dY + (m + 3 * kBgGroups) * ld + n, v3, nv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = ((acc[i] + v0[i]) + v1[i] + v2[i]) + v3[i];
+    }
+    for (; m < M; m += kBgGroups) {
       float v[8];
       load8<T>(dY + m * ld + n, v, nv);
 #pragma unroll
@@ -69,20 +83,27 @@ __global__ void __launch_bounds__(256) bias_grad_kernel(const T* __restrict__ dY
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[rg][cg * 8 + i] = acc[i];
   __syncthreads();
+  const int col = tid & 63, r = tid >> 6;   // 16 runs of 8 groups
+  float sr = 0.f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) sr += part[r * 8 + g][col];
+  run[r][col] = sr;
+  __syncthreads();
   if (tid < 64) {
-    float s = 0.f;
-    for (int g = 0; g < 32; ++g) s += part[g][tid];
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += run[q][tid];
     const int64_t c = (int64_t)blockIdx.x * 64 + tid;
-    if (c < N) db[c] = s;
+    if (c < N) db[c] = t;
   }
 }
 
 tps_status bias_grad(tps_dtype dt, const void* dY, int64_t ld, int64_t M, int64_t N, float* db, hipStream_t st) {
   const dim3 grid((unsigned)ceil_div(N, 64));
   if (dt == TPS_BF16)
-    hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(dY), ld, M, N, db);
+    hipLaunchKernelGGL(bias_grad_kernel<bf16_t>, grid, dim3(1024), 0, st, static_cast<const bf16_t*>(dY), ld, M, N, db);
   else
-    hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(dY), ld, M, N, db);
+    hipLaunchKernelGGL(bias_grad_kernel<float>, grid, dim3(1024), 0, st, static_cast<const float*>(dY), ld, M, N, db);
   return check_launch("bias_grad_kernel");
 }
 
