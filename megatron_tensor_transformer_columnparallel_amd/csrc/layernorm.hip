@@ -54,49 +54,51 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-template <typename TX, typename TY>
+// NC chunks of 8 elements per thread (NC = ceil(H / 2048)).  Every load is
+// issued before the first reduction and none sits behind a branch: a chunk
+// that starts past the row's end re-reads the row's last 8 elements and is
+// masked out of the sums and the store.  gamma and beta come in with x.
+template <typename TX, typename TY, int NC>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, TY* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int64_t H,
                                                      float eps) {
   constexpr int V = kLnV;
-  constexpr int NCH = kLnNCH;
   __shared__ float red[8];
   const int64_t row = blockIdx.x;
   const TX* xr = x + row * H;
-  float v[NCH][V];
+  float v[NC][V], g[NC][V], b[NC][V];
+  bool ok[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
+    ok[i] = c < H;
+    const int64_t cc = ok[i] ? c : H - V;
+    LnVec<TX>::load(xr + cc, v[i]);
+    LnVec<float>::load(gamma + cc, g[i]);
+    LnVec<float>::load(beta + cc, b[i]);
+  }
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
-    if (c < H) {
-      LnVec<TX>::load(xr + c, v[i]);
+  for (int i = 0; i < NC; ++i)
 #pragma unroll
-      for (int e = 0; e < V; ++e) s += v[i][e];
-    }
-  }
+    for (int e = 0; e < V; ++e) s += ok[i] ? v[i][e] : 0.f;
   const float mu = block_sum(s, red) / (float)H;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
-    if (c < H) {
+  for (int i = 0; i < NC; ++i)
 #pragma unroll
-      for (int e = 0; e < V; ++e) { const float d = v[i][e] - mu; q += d * d; }
-    }
-  }
+    for (int e = 0; e < V; ++e) { const float d = v[i][e] - mu; q += ok[i] ? d * d : 0.f; }
   const float var = block_sum(q, red) / (float)H;
   const float rs = rsqrtf(var + eps);
   TY* yr = y + row * H;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int64_t c = ((int64_t)i * 256 + threadIdx.x) * V;
-    if (c < H) {
-      float o[V];
+    float o[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = (v[i][e] - mu) * rs * gamma[c + e] + beta[c + e];
-      LnVec<TY>::store(yr + c, o);
-    }
+    for (int e = 0; e < V; ++e) o[e] = (v[i][e] - mu) * rs * g[i][e] + b[i][e];
+    if (ok[i]) LnVec<TY>::store(yr + c, o);
   }
   if (threadIdx.x == 0) { mean[row] = mu; rstd[row] = rs; }
 }
@@ -351,8 +353,15 @@ static tps_status ln_checks(const char* fn, std::initializer_list<tps_dtype> dts
 template <typename TX, typename TY>
 static void launch_ln_fwd(int64_t M, int64_t H, float eps, const void* x, const float* g, const float* b, void* y,
                           float* mean, float* rstd, hipStream_t st) {
-  hipLaunchKernelGGL((ln_fwd_kernel<TX, TY>), dim3((unsigned)M), dim3(256), 0, st, static_cast<const TX*>(x), g, b,
-                     static_cast<TY*>(y), mean, rstd, H, eps);
+  const int nc = (int)ceil_div(H, 256 * kLnV);   // 1..4 (H <= 8192)
+#define TPS_LNF(NC)                                                                                             \
+  hipLaunchKernelGGL((ln_fwd_kernel<TX, TY, NC>), dim3((unsigned)M), dim3(256), 0, st, static_cast<const TX*>(x), g, \
+                     b, static_cast<TY*>(y), mean, rstd, H, eps)
+  if (nc == 1) TPS_LNF(1);
+  else if (nc == 2) TPS_LNF(2);
+  else if (nc == 3) TPS_LNF(3);
+  else TPS_LNF(4);
+#undef TPS_LNF
 }
 
 template <bool RES, typename TX, typename TDY, typename TDX>
