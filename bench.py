@@ -402,11 +402,12 @@ def cpu_baseline():
 
 # HBM traffic of one tied_logits call (both of its GEMM launches) from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over `bench.py --steps 2
-# --warmup 1 --no-cpu --no-embed --no-layer --calib`, divided by what the same
+# --warmup 1 --no-cpu --no-embed --no-layer --no-ce --no-linear --no-sp
+# --no-full-embed --calib`, divided by what the same
 # counters read for a plain copy (shard_reduce with one part over 512 MiB) per
 # byte moved.  Valid only for the GEMM source it was taken on (sha256 prefix
 # below); otherwise null.
-ROOFLINE_TRAFFIC = {"gemm_sha": "3488e65ee78570d0", "bytes_per_launch": 791722430}
+ROOFLINE_TRAFFIC = {"gemm_sha": "92025436c94f6fe9", "bytes_per_launch": 764966174}
 
 
 def _gemm_sha():
@@ -480,7 +481,7 @@ def main():
     traffic = ROOFLINE_TRAFFIC["bytes_per_launch"] if ROOFLINE_TRAFFIC["gemm_sha"] == _gemm_sha() else None
     roofline = {"kernel": "gemm_bf16_kernel via tied_logits "
                           f"({c.M}x{vr[0]}x{c.H} per shard: <256,256,64,2,4,2,NT,EpiStore> over 96 tile "
-                          "columns + <128,128,64,2,4,3,NT,EpiStore> over the last 553 columns)",
+                          "columns + <64,128,64,2,4,3,NT,EpiStore> over the last 553 columns)",
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_us": round(launch_ms * 1e3, 2), "flops_per_launch": per_launch_flops,

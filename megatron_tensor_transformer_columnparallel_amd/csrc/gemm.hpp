@@ -798,6 +798,9 @@ inline GemmAlt<Epi> no_alt(const Epi& e) {
 //     CU and cover each other's waits) above 256 tiles, three stages at most
 //     256 tiles, where one K tile in flight leaves the DMA latency exposed
 //     (2048x2048x4096: 62 -> 47 us);
+//   64x128, 8 waves of 32x32, three stages, when 128x128 tiles would fill
+//     fewer than half of the CUs (64..127 tiles): twice the tiles (the
+//     tied-logits leftover 2048x553x4096 NT: 28.9 -> 22.0 us);
 //   64x64 for problems too small for 64 tiles of 128x128.
 // Longest-first (lpt) launches always take 128x128 with three stages: one
 // workgroup per CU, so the CUs that finish short tiles pick up the next
@@ -847,6 +850,7 @@ inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s
   if (t256 >= 192 && !partial_round) return launch_mfma<256, 256, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, alt, st);
   if (t128x256 >= 192 && t128x256 <= 256) return launch_mfma<128, 256, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
   if (t128 > 256) return launch_mfma<128, 128, 64, 2, 4, 2, AK, BKC>(A, B, s, epi, alt, st);
+  if (t128 >= 64 && t128 < 128) return launch_mfma<64, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
   if (t128 >= 64) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
   return launch_mfma<64, 64, 64, 2, 2, 2, AK, BKC>(A, B, s, epi, alt, st);
 }
