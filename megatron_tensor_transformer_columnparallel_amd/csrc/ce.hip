@@ -16,8 +16,9 @@
 // and the pick, then the loss and log-sum-exp lse = m + log(sum).  The
 // backward (vocab_ce_bwd) reads each shard's logits once more and writes
 // dL = dloss * (exp(x - lse) - [column is the target]).  All three are bound
-// by HBM: one wavefront per token row, 16-byte vectors, every load issued
-// unconditionally at a clamped chunk so that a whole group is in flight.
+// by HBM: the statistics take one wavefront per token row, the backward one
+// workgroup per row; 16-byte vectors, every load issued unconditionally at a
+// clamped chunk so that a whole group is in flight.
 #include <math.h>
 
 #include "common.hpp"
@@ -150,7 +151,9 @@ __global__ void __launch_bounds__(256) ce_combine_kernel(StatPtrs st, int np, in
   lse[t] = m + ld;
 }
 
-// One wavefront per token row: dL = dloss * (exp(x - lse) - [column = target]).
+// One workgroup per token row (grid-stride over rows; consecutive lanes take
+// consecutive 16-byte chunks, so the row streams contiguously):
+// dL = dloss * (exp(x - lse) - [column = target]).
 // Columns past v_rows (up to the row stride) are neither used nor written.
 // The target's column is tested once per chunk; bf16 results are rounded to
 // nearest-even by the hardware pair conversion.
@@ -160,46 +163,47 @@ __global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, in
                                                      const float* __restrict__ lse,
                                                      const float* __restrict__ dloss, T* dL) {
   constexpr int VEC = 16 / sizeof(T);
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= ntok) return;
-  const int lane = threadIdx.x & 63;
-  const T* row = L + t * ldl;
-  T* drow = dL + t * ldl;
+  const int lane = threadIdx.x;
   const int nch = (v_rows + VEC - 1) / VEC;
-  const int64_t tl64 = (int64_t)targets[t] - v_start;
-  const int tl = (tl64 >= 0 && tl64 < v_rows) ? (int)tl64 : -VEC;   // owned column, or none
-  const float l = lse[t], g = dloss[t];
-  for (int c0 = lane; c0 < nch; c0 += 64 * kGroup) {
-    float v[kGroup][VEC];
+  // one workgroup per row at a time: its 256 lanes stream the row contiguously
+  for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
+    const T* row = L + t * ldl;
+    T* drow = dL + t * ldl;
+    const int64_t tl64 = (int64_t)targets[t] - v_start;
+    const int tl = (tl64 >= 0 && tl64 < v_rows) ? (int)tl64 : -VEC;   // owned column, or none
+    const float l = lse[t], g = dloss[t];
+    for (int c0 = lane; c0 < nch; c0 += 256 * kGroup) {
+      float v[kGroup][VEC];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) load_chunk<T>(row, c0 + k * 64, nch, v[k]);
+      for (int k = 0; k < kGroup; ++k) load_chunk<T>(row, c0 + k * 256, nch, v[k]);
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      const int c = c0 + k * 64;
-      if (c >= nch) continue;
-      float o[VEC];
+      for (int k = 0; k < kGroup; ++k) {
+        const int c = c0 + k * 256;
+        if (c >= nch) continue;
+        float o[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[e] = g * exp_shifted(v[k][e], l);
-      if (tl - c * VEC >= 0 && tl - c * VEC < VEC) {   // the chunk holding the owned target
+        for (int e = 0; e < VEC; ++e) o[e] = g * exp_shifted(v[k][e], l);
+        if (tl - c * VEC >= 0 && tl - c * VEC < VEC) {   // the chunk holding the owned target
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          if (c * VEC + e == tl) o[e] -= g;
-      }
-      if constexpr (sizeof(T) == 2) {
-        if (c * VEC + VEC <= v_rows) {
-          typedef float f2 __attribute__((ext_vector_type(2)));
-          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-          u32x4_t w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{o[2 * i], o[2 * i + 1]}, b2));
-          *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8) = w;
-        } else {
-          store8<bf16_t>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8, o, v_rows - c * VEC);
+          for (int e = 0; e < VEC; ++e)
+            if (c * VEC + e == tl) o[e] -= g;
         }
-      } else {
-        store4<float>(reinterpret_cast<float*>(drow) + (int64_t)c * 4, o,
-                      v_rows - c * VEC < VEC ? v_rows - c * VEC : VEC);
+        if constexpr (sizeof(T) == 2) {
+          if (c * VEC + VEC <= v_rows) {
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            u32x4_t w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{o[2 * i], o[2 * i + 1]}, b2));
+            *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8) = w;
+          } else {
+            store8<bf16_t>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8, o, v_rows - c * VEC);
+          }
+        } else {
+          store4<float>(reinterpret_cast<float*>(drow) + (int64_t)c * 4, o,
+                        v_rows - c * VEC < VEC ? v_rows - c * VEC : VEC);
+        }
       }
     }
   }
@@ -270,7 +274,7 @@ extern "C" tps_status vocab_ce_bwd(tps_dtype dt, int64_t T, int64_t v_rows, int6
     return set_error(TPS_EINVAL, "vocab_ce_bwd: L_r and dL_r must be 16-byte aligned");
   if (T == 0) return TPS_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)ceil_div(T, 4));
+  const dim3 grid((unsigned)(T < 65536 ? T : 65536));
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(ce_bwd_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
                        (int)v_rows, v_start, targets, lse, dloss, static_cast<bf16_t*>(dL_r));
