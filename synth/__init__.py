@@ -138,3 +138,33 @@ def embed_inputs(w: int, T: int, V: int, H: int, dtype: str, table_std: float,
 def logit_grad(w: int, shard: int, T: int, rows: int, dtype: str, base: int = 30) -> Tensor:
     """dL_r ~ N(0,1) for shard r (T x rows)."""
     return make(w, base + shard, (T, rows), 1.0, dtype)
+
+
+def gpt_inputs(w: int, L: int, M: int, H: int, width: int, f: int, V: int, shard_rows, ln_random: bool):
+    """Seeded inputs of the stacked model: token ids (uniform in [0, V)), the
+    table E ~ N(0, 0.02), per layer W_Q, W_K, W_V (H x width), W_O
+    (width x H), A (H x f), B (f x H) ~ N(0, 0.02) and the LayerNorm
+    parameters (gamma = 1, beta = 0, or with ``ln_random`` 1 + N(0, 0.1) and
+    N(0, 0.1) in fp32), and one logit gradient dL_r ~ N(0, 1) per entry of
+    ``shard_rows`` (the vocabulary rows of each shard).  All bf16 except the
+    LayerNorm parameters.  Returns (ids, E, layers, dL)."""
+    ids = uniform_ids(w, 0, M, V)
+    E = make(w, 1, (V, H), 0.02, "bf16")
+    layers = []
+    k = 2
+    for _ in range(L):
+        lw = {}
+        for name, sh in [("WQ", (H, width)), ("WK", (H, width)), ("WV", (H, width)),
+                         ("WO", (width, H)), ("A", (H, f)), ("B", (f, H))]:
+            lw[name] = make(w, k, sh, 0.02, "bf16")
+            k += 1
+        for name in ("g1", "b1", "g2", "b2"):
+            base = 1.0 if name.startswith("g") else 0.0
+            if ln_random:
+                lw[name] = Tensor((base + 0.1 * normal(w, k, (H,))).astype(np.float32), "f32")
+            else:
+                lw[name] = Tensor(np.full(H, base, np.float32), "f32")
+            k += 1
+        layers.append(lw)
+    dL = [make(w, 900 + r, (M, rows), 1.0, "bf16") for r, rows in enumerate(shard_rows)]
+    return ids, E, layers, dL

@@ -2,12 +2,9 @@
 pre-LN MLP] -> tied logits, every tensor-parallel shard executed on one GPU)
 against the fp64 oracle's gpt_forward/gpt_backward.
 
-Forward outputs (the logits) must meet the 1e-2 bf16 bar.  Gradients are
-held to the same bar, but in a deep stack the bf16 storage points that feed
-the MFMA GEMMs (LayerNorm outputs, QKV, P, dS, the bf16 copy of the residual
-gradient) accumulate to 1.0-1.8e-2 on the lowest layers and on the attention
-Q/K weights: such a case is reported as an explicit xfail with the measured
-values (never silently passed), and anything above 3e-2 fails outright.
+Every output is held to the bf16 bar max|err|/max|ref| <= 1e-2: the logits,
+the tied table's gradient and every parameter gradient of every layer.  All
+errors are printed before any assertion, so one run shows the whole picture.
 """
 
 import numpy as np
@@ -22,37 +19,19 @@ pytestmark = pytest.mark.gpu
 
 
 def build_model(w, shape, ln_random):
-    """Seeded inputs of one model: tokens, table, per-layer weights, LN params, dL."""
+    """Seeded inputs of one model (tokens, table, per-layer weights, LN params,
+    dL) and the device model built from them."""
     from megatron_tensor_transformer_columnparallel_amd.gpt import TPGPT
     c = shape
-    ids = synth.uniform_ids(w, 0, c.M, c.V)
-    E = synth.make(w, 1, (c.V, c.H), 0.02, "bf16")
-    host_layers, dev_layers = [], []
-    k = 2
-    for li in range(c.L):
-        hl = {}
-        for name, sh in [("WQ", (c.H, c.heads * c.d)), ("WK", (c.H, c.heads * c.d)), ("WV", (c.H, c.heads * c.d)),
-                         ("WO", (c.heads * c.d, c.H)), ("A", (c.H, c.f)), ("B", (c.f, c.H))]:
-            hl[name] = synth.make(w, k, sh, 0.02, "bf16")
-            k += 1
-        for name in ("g1", "b1", "g2", "b2"):
-            if ln_random:
-                base = 1.0 if name.startswith("g") else 0.0
-                hl[name] = synth.Tensor((base + 0.1 * synth.normal(w, k, (c.H,))).astype(np.float32), "f32")
-            else:
-                hl[name] = synth.Tensor(np.full(c.H, 1.0 if name.startswith("g") else 0.0, np.float32), "f32")
-            k += 1
-        host_layers.append(hl)
-        dev_layers.append({n: to_dev(t) for n, t in hl.items()})
+    vr = [O.partition(c.V, c.n, r) for r in range(c.n)]
+    ids, E, host_layers, dL = synth.gpt_inputs(w, c.L, c.M, c.H, c.heads * c.d, c.f, c.V, [n for _, n in vr],
+                                               ln_random)
+    dev_layers = [{n: to_dev(t) for n, t in hl.items()} for hl in host_layers]
     model = TPGPT(c, to_dev(E), dev_layers)
-    dL = [synth.logit_grad(w, r, c.M, model.vr[r][1], "bf16", base=900) for r in range(c.n)]
     return ids, E, host_layers, model, dL
 
 
-GRAD_FAIL = 3e-2   # regression guard for gradients (the bar itself is BF16_TOL)
-
-
-def run_and_compare(shape, w, ln_random, check_all=True):
+def run_and_compare(shape, w, ln_random):
     import megatron_tensor_transformer_columnparallel_amd  # noqa: F401
     c = shape
     ids, E, hl, model, dL = build_model(w, c, ln_random)
@@ -74,14 +53,10 @@ def run_and_compare(shape, w, ln_random, check_all=True):
         assert e <= BF16_TOL
     dE_ref, grads = O.gpt_backward(ids, E.f64, layers64, cache, [x.f64 for x in dL], c.b, c.s, c.heads, c.d, c.n)
     dE_got = np.concatenate([to_f64(x) for x in model.dE], axis=0)
-    over = []
-    e = rel_err(dE_got, dE_ref)
-    print(f"  dE err {e:.2e}", flush=True)
-    assert e <= GRAD_FAIL, ("dE", e)
-    if e > BF16_TOL:
-        over.append(f"dE {e:.2e}")
+    errs = {"dE": rel_err(dE_got, dE_ref)}
+    print(f"  dE err {errs['dE']:.2e}", flush=True)
     w = c.heads // c.n * c.d
-    for li in ([0, c.L - 1] if not check_all else range(c.L)):
+    for li in range(c.L):
         gs = model.grads[li]
         got = {
             "WQ": np.concatenate([to_f64(g["Wqkv"])[:, :w] for g in gs["sh"]], axis=1),
@@ -94,12 +69,12 @@ def run_and_compare(shape, w, ln_random, check_all=True):
         }
         for k, v in got.items():
             e = rel_err(v, grads[li][k])
+            errs[f"layer {li} d{k}"] = e
             print(f"  layer {li} d{k} err {e:.2e}", flush=True)
-            assert e <= GRAD_FAIL, (li, k, e)
-            if e > BF16_TOL:
-                over.append(f"layer {li} d{k} {e:.2e}")
-    if over:
-        pytest.xfail("gradients above the 1e-2 bar (bf16 storage accumulation): " + ", ".join(over))
+    worst = max(errs, key=errs.get)
+    print(f"  worst gradient: {worst} {errs[worst]:.2e}", flush=True)
+    over = [f"{k} {e:.2e}" for k, e in errs.items() if e > BF16_TOL]
+    assert not over, "gradients above the 1e-2 bar: " + ", ".join(over)
 
 
 def test_gpt_small_all_outputs():
@@ -115,7 +90,7 @@ def test_gpt_workload5_full_size():
     from megatron_tensor_transformer_columnparallel_amd.gpt import GPTShape
     shape = GPTShape()
     say(f"stacked model, full workload {shape}")
-    run_and_compare(shape, 5, ln_random=False, check_all=False)
+    run_and_compare(shape, 5, ln_random=False)
 
 
 def test_gpt_small_with_vocab_cross_entropy():
