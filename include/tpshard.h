@@ -214,6 +214,25 @@ tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, 
                            void* ws, size_t ws_bytes, tps_stream_t stream);
 
 /*
+ * vocab_embed_bwd_noalloc: vocab_embed_bwd without a workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments (minus the
+ * workspace), same kernels and the same result bit for bit.  The sort keys
+ * live in a static device array inside the library (512 KiB on every GPU the
+ * library runs on, held until the process ends), so the call allocates
+ * nothing; the array's device address is looked up once per device on the
+ * first call.  Limit: T <= vocab_embed_bwd_noalloc_max_tokens() (65536);
+ * larger T returns TPS_EINVAL with nothing enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one device (different
+ * streams, or host threads) race and must be serialised by the caller.
+ * Errors as vocab_embed_bwd, plus TPS_EHIP when the array's address cannot be
+ * obtained.
+ */
+int64_t vocab_embed_bwd_noalloc_max_tokens(void);
+tps_status vocab_embed_bwd_noalloc(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
+                                   const int32_t* ids, const void* dY, float* dE_r, tps_stream_t stream);
+
+/*
  * tied_logits: L_r = X E_r^T.
  *   X [T x H], E_r [v_rows x H], L_r [T x v_rows] with row stride ldl
  *   (ldl >= v_rows, multiple of 8 for bf16 / 4 for fp32; columns v_rows..ldl-1

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     tp_attn_fwd, tp_attn_fwd_workspace, tp_attn_bwd, tp_attn_bwd_workspace,
     shard_reduce, shard_reduce_add,
     vocab_embed_fwd, vocab_embed_bwd, vocab_embed_bwd_workspace,
+    vocab_embed_bwd_noalloc, vocab_embed_bwd_noalloc_max_tokens,
     tied_logits, tied_logits_bwd,
     vocab_ce_stats, vocab_ce_combine, vocab_ce_bwd,
     column_linear_fwd, column_linear_bwd, row_linear_fwd, row_linear_bwd, shard_reduce_bias,

@@ -40,6 +40,8 @@ SIGNATURES = {
     "vocab_embed_fwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "vocab_embed_bwd_workspace": (_sz, [_i64, _i64]),
     "vocab_embed_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "vocab_embed_bwd_noalloc_max_tokens": (_i64, []),
+    "vocab_embed_bwd_noalloc": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tied_logits_bwd": (_i32, [_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "embedding_fwd": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_vp), _vp, _i64, _vp, _vp, _i64, _vp, _f32,
@@ -274,6 +276,22 @@ def vocab_embed_bwd(ids, dY, dE_r, v_start, ws, stream=None):
     assert dY.shape == (T, H)
     _check(lib.vocab_embed_bwd(dt, T, H, v_start, v_rows, _p(ids), _p(dY), _p(dE_r), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)), "vocab_embed_bwd")
+
+
+def vocab_embed_bwd_noalloc_max_tokens() -> int:
+    return lib.vocab_embed_bwd_noalloc_max_tokens()
+
+
+def vocab_embed_bwd_noalloc(ids, dY, dE_r, v_start, stream=None):
+    """vocab_embed_bwd with the library's static scratch instead of a workspace."""
+    assert ids.dtype == torch.int32 and dE_r.dtype == torch.float32
+    dt = _dt(dY)
+    _contig(ids, dY, dE_r)
+    T = ids.numel()
+    v_rows, H = dE_r.shape
+    assert dY.shape == (T, H)
+    _check(lib.vocab_embed_bwd_noalloc(dt, T, H, v_start, v_rows, _p(ids), _p(dY), _p(dE_r), _stream(stream)),
+           "vocab_embed_bwd_noalloc")
 
 
 def tied_logits(X, E_r, L_r, stream=None):

@@ -12,6 +12,8 @@
 // contiguous and ascending in t.  One wavefront per segment
 // head then adds that row's dY rows, in that order, to the row of dE_r in
 // fp32 with a plain read-modify-write (each row has exactly one owner).
+#include <mutex>
+
 #include "common.hpp"
 
 namespace tps {
@@ -469,21 +471,23 @@ extern "C" size_t vocab_embed_bwd_workspace(int64_t T, int64_t v_rows) {
   return (size_t)next_pow2(T) * sizeof(uint64_t);   // the sort keys
 }
 
-extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
-                                      const int32_t* ids, const void* dY, float* dE_r, void* ws,
-                                      size_t ws_bytes, tps_stream_t stream) {
-  tps_status s = embed_common_checks("vocab_embed_bwd", dt, T, H, v_start, v_rows);
+// Checks shared by both backward entry points (everything but the workspace).
+static tps_status embed_bwd_checks(const char* fn, tps_dtype dt, int64_t T, int64_t H, int64_t v_start,
+                                   int64_t v_rows, const int32_t* ids, const void* dY, const float* dE_r) {
+  tps_status s = embed_common_checks(fn, dt, T, H, v_start, v_rows);
   if (s != TPS_OK) return s;
-  if (T >= 0x7fffffffLL) return set_error(TPS_EINVAL, "vocab_embed_bwd: T must be < 2^31");
-  if (!ids || !dY || !dE_r) return set_error(TPS_EINVAL, "vocab_embed_bwd: null pointer");
-  if (!aligned16(dY) || !aligned16(dE_r)) return set_error(TPS_EINVAL, "vocab_embed_bwd: pointers must be 16-byte aligned");
-  if (T == 0) return TPS_OK;
-  if (!ws) return set_error(TPS_EINVAL, "vocab_embed_bwd: null workspace");
-  if (!aligned16(ws)) return set_error(TPS_EINVAL, "vocab_embed_bwd: workspace must be 16-byte aligned");
-  if (ws_bytes < vocab_embed_bwd_workspace(T, v_rows))
-    return set_error(TPS_EWORKSPACE, "vocab_embed_bwd: workspace too small");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint64_t* keys = static_cast<uint64_t*>(ws);
+  if (T >= 0x7fffffffLL) return set_error(TPS_EINVAL, std::string(fn) + ": T must be < 2^31");
+  if (!ids || !dY || !dE_r) return set_error(TPS_EINVAL, std::string(fn) + ": null pointer");
+  if (!aligned16(dY) || !aligned16(dE_r))
+    return set_error(TPS_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+  return TPS_OK;
+}
+
+// The sort into `keys` (next_pow2(T) entries, every one of them written
+// before it is read) and the accumulation.  T > 0.
+static tps_status embed_bwd_run(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
+                                const int32_t* ids, const void* dY, float* dE_r, uint64_t* keys, hipStream_t st) {
+  tps_status s;
   const int tbits = ceil_log2(T), rbits = ceil_log2(v_rows + 1);
   if (T <= kRadixMax && tbits + 8 <= 32 && v_rows <= 256LL * kRadixBuckets) {
     // one workgroup per bucket of at most 256 rows: one 8-bit pass each
@@ -513,4 +517,67 @@ extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_
     hipLaunchKernelGGL(embed_bwd_accum_kernel<float>, grid, dim3(256), 0, st, keys,
                        static_cast<const float*>(dY), dE_r, T, H);
   return check_launch("embed_bwd_accum_kernel");
+}
+
+extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
+                                      const int32_t* ids, const void* dY, float* dE_r, void* ws,
+                                      size_t ws_bytes, tps_stream_t stream) {
+  tps_status s = embed_bwd_checks("vocab_embed_bwd", dt, T, H, v_start, v_rows, ids, dY, dE_r);
+  if (s != TPS_OK) return s;
+  if (T == 0) return TPS_OK;
+  if (!ws) return set_error(TPS_EINVAL, "vocab_embed_bwd: null workspace");
+  if (!aligned16(ws)) return set_error(TPS_EINVAL, "vocab_embed_bwd: workspace must be 16-byte aligned");
+  if (ws_bytes < vocab_embed_bwd_workspace(T, v_rows))
+    return set_error(TPS_EWORKSPACE, "vocab_embed_bwd: workspace too small");
+  return embed_bwd_run(dt, T, H, v_start, v_rows, ids, dY, dE_r, static_cast<uint64_t*>(ws),
+                       static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- no-alloc variant
+//
+// The sort keys of vocab_embed_bwd_noalloc live in this file-scope device
+// array instead of a caller workspace: one copy per GPU the library runs on,
+// kept until the process ends.  Host code never passes the array's name to
+// a kernel (in host code it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and cached.
+constexpr int64_t kNoAllocMaxTokens = 65536;   // next_pow2(T) keys of 8 bytes: 512 KiB
+static __device__ __align__(256) uint64_t scratch[kNoAllocMaxTokens];
+
+static constexpr int kMaxDevices = 64;
+static uint64_t* g_scratch_ptr[kMaxDevices] = {};
+static std::mutex g_scratch_mu;
+
+static tps_status noalloc_scratch(uint64_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(TPS_EHIP, "vocab_embed_bwd_noalloc: no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(TPS_EHIP, std::string("vocab_embed_bwd_noalloc: hipGetSymbolAddress failed: ") +
+                                     hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint64_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return TPS_OK;
+}
+
+extern "C" int64_t vocab_embed_bwd_noalloc_max_tokens(void) { return kNoAllocMaxTokens; }
+
+extern "C" tps_status vocab_embed_bwd_noalloc(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
+                                              const int32_t* ids, const void* dY, float* dE_r,
+                                              tps_stream_t stream) {
+  tps_status s = embed_bwd_checks("vocab_embed_bwd_noalloc", dt, T, H, v_start, v_rows, ids, dY, dE_r);
+  if (s != TPS_OK) return s;
+  if (T > kNoAllocMaxTokens)
+    return set_error(TPS_EINVAL, "vocab_embed_bwd_noalloc: T = " + std::to_string(T) +
+                                     " exceeds the static scratch's limit of " + std::to_string(kNoAllocMaxTokens) +
+                                     " tokens (use vocab_embed_bwd with a workspace)");
+  if (T == 0) return TPS_OK;
+  uint64_t* keys = nullptr;
+  s = noalloc_scratch(&keys);
+  if (s != TPS_OK) return s;
+  return embed_bwd_run(dt, T, H, v_start, v_rows, ids, dY, dE_r, keys, static_cast<hipStream_t>(stream));
 }
