@@ -12,11 +12,13 @@ the logits' upstream gradient is drawn N(0,1).
 
 Prints one JSON line.  `value` = algorithmic TFLOP/s of the step (33.45
 TFLOP: GEMMs 2MNK, causal attention s(s+1)/2 score pairs, backward = 2x
-forward).  Also reported: the roofline of the dominant kernel (the MFMA
-GEMM, on its call tied_logits: whole rounds of 256x256 tiles plus one
-small-tile launch for the leftover columns), the single-layer step on its
-own, the vocab-parallel embedding kernels' HBM GB/s at T = 8*2048 tokens,
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+forward).  Also reported: the roofline of the dominant kernel instance
+(the GEMM template instance with the largest total kernel time in a traced
+step; its launches are timed with events on their own stream during the
+timed steps), every GEMM shape's rate and the attention + MLP kernel-time
+headline from one traced step, the single-layer step on its own, the
+vocab-parallel embedding kernels' HBM GB/s at T = 8*2048 tokens, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -396,25 +398,133 @@ def cpu_baseline():
     t = time.perf_counter() - t0
     flops = 6 * 2 * M * h * f
     return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": "one shard's MLP fwd+bwd at the layer shape (2048x4096 @ 4096x8192, GELU), fp64 numpy, "
                       f"{flops / 1e9:.1f} GFLOP in {t:.2f} s", "seconds": round(t, 2)}
 
 
-# HBM traffic of one tied_logits call (both of its GEMM launches) from two
-# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over `bench.py --steps 2
-# --warmup 1 --no-cpu --no-embed --no-layer --no-ce --no-linear --no-sp
-# --no-full-embed --calib`, divided by what the same
-# counters read for a plain copy (shard_reduce with one part over 512 MiB) per
-# byte moved.  Valid only for the GEMM source it was taken on (sha256 prefix
-# below); otherwise null.
-ROOFLINE_TRAFFIC = {"gemm_sha": "92025436c94f6fe9", "bytes_per_launch": 764966174}
+# ------------------------------------------------------------------ launch traces
+
+ATTN_MLP_APIS = ("tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd")
 
 
-def _gemm_sha():
+def parse_launch(name):
+    """'api:kernel[ <targs> MxNxK zB[ causal]]' -> (api, kernel, targs, (M, N, K, B) or None, causal)."""
+    api, rest = name.split(":", 1)
+    parts = rest.split(" ")
+    kernel = parts[0]
+    targs, shape, causal = "", None, False
+    if len(parts) >= 3 and "x" in parts[2]:
+        targs = parts[1]
+        M, N, K = (int(v) for v in parts[2].split("x"))
+        B = int(parts[3][1:]) if len(parts) > 3 and parts[3].startswith("z") else 1
+        shape = (M, N, K, B)
+        causal = "causal" in parts[4:]
+    return api, kernel, targs, shape, causal
+
+
+def launch_flops(shape, causal):
+    """Algorithmic FLOPs of one GEMM launch: 2MNK per problem; a causal
+    attention product (scores s x s, or a K-loop over s keys) counts only the
+    s(s+1)/2 (query, key) pairs."""
+    M, N, K, B = shape
+    if not causal:
+        return 2 * M * N * K * B
+    s = M
+    other = N if K == M else K
+    return B * 2 * other * (s * (s + 1) // 2)
+
+
+def instance_of(name):
+    """The kernel template instance of a launch (what a kernel profiler groups by)."""
+    api, kernel, targs, _, _ = parse_launch(name)
+    return kernel + targs
+
+
+def trace_one_step(tp, torch, step):
+    """Every library launch of one step, timed with events on its own stream."""
+    tp.trace_start("", 1 << 16)
+    step()
+    torch.cuda.synchronize()
+    tp.trace_stop()
+    recs = tp.trace_records()
+    tp.trace_clear()
+    return recs
+
+
+def step_breakdown(recs, layer_flops_total):
+    """Per-instance totals, per-GEMM-shape rates and the attention+MLP
+    kernel-time headline from one traced step."""
+    by_inst, by_shape = {}, {}
+    attn_mlp_ms = 0.0
+    total_ms = 0.0
+    for name, ms in recs:
+        api, kernel, targs, shape, causal = parse_launch(name)
+        total_ms += ms
+        inst = kernel + targs
+        e = by_inst.setdefault(inst, [0, 0.0])
+        e[0] += 1
+        e[1] += ms
+        if api in ATTN_MLP_APIS:
+            attn_mlp_ms += ms
+        if shape is not None:
+            key = f"{api} {kernel}{targs} {shape[0]}x{shape[1]}x{shape[2]}" + (f" z{shape[3]}" if shape[3] > 1 else "") \
+                + (" causal" if causal else "")
+            e2 = by_shape.setdefault(key, [0, 0.0, launch_flops(shape, causal)])
+            e2[0] += 1
+            e2[1] += ms
+    shapes = {}
+    for key, (n, ms, fl) in sorted(by_shape.items(), key=lambda kv: -kv[1][1]):
+        avg = ms / n
+        tf = fl / (avg * 1e-3) / 1e12
+        shapes[key] = {"launches": n, "avg_us": round(avg * 1e3, 2), "TFLOP/s": round(tf, 1),
+                       "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    top = sorted(by_inst.items(), key=lambda kv: -kv[1][1])
+    top_gemm = next(k for k, _ in top if "<" in k)
+    headline = layer_flops_total / (attn_mlp_ms * 1e-3) / 1e12
+    return {
+        "kernel_ms_per_step": round(total_ms, 3),
+        "top_instances": [{"instance": k, "launches": n, "ms": round(ms, 3), "share": round(ms / total_ms, 4)}
+                          for k, (n, ms) in top[:8]],
+        "gemm_shapes": shapes,
+        "attn_mlp_kernel_time": {
+            "TFLOP/s": round(headline, 1), "frac_of_bf16_peak": round(headline / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms": round(attn_mlp_ms, 3), "tflop": round(layer_flops_total / 1e12, 3),
+            "what": "sum of algorithmic FLOPs of every tp_mlp_* and tp_attn_* call of the step / sum of the "
+                    "kernel times of their launches"},
+    }, top_gemm
+
+
+def profile_traffic(instance):
+    """HBM bytes per launch of `instance` from the committed counter summary
+    (two rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by what
+    the same counters read for a plain copy), or None when the summary was
+    taken on another version of the GEMM source or another instance."""
     import hashlib
-    p = os.path.join(ROOT, "megatron_tensor_transformer_columnparallel_amd", "csrc", "gemm.hpp")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    path = os.path.join(ROOT, "profiles", "gemm_top_instance_traffic.md")
+    src = os.path.join(ROOT, "megatron_tensor_transformer_columnparallel_amd", "csrc", "gemm.hpp")
+    try:
+        text = open(path, encoding="utf-8").read()
+    except OSError:
+        return None
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    for line in text.splitlines():
+        if line.startswith("traffic-record:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("gemm_sha") == sha and rec.get("instance") == instance:
+                return int(rec["bytes_per_launch"])
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -459,8 +569,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # events around each tied_logits call (two GEMM launches: whole rounds + leftover columns)
-    model.logit_events = logit_events = []
+    # one traced step (untimed): per-launch kernel times -> the dominant
+    # kernel instance, the per-shape GEMM rates and the kernel-time headline
+    lflops = c.L * layer_flops(c.b, c.s, c.H, c.heads, c.d, c.f, c.n)
+    breakdown, top_inst = step_breakdown(trace_one_step(tp, torch, step), lflops)
+    # timed region: exactly `steps` steps; the dominant instance's launches
+    # are bracketed by events on their own stream (the library's tracer)
+    tp.trace_start(":" + top_inst.replace("<", " <", 1), 1 << 16)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -470,22 +585,22 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    model.logit_events = None
+    tp.trace_stop()
+    roof_recs = tp.trace_records()
+    tp.trace_clear()
     ms = t0.elapsed_time(t1) / args.steps
     value = flops / (ms * 1e-3) / 1e12
 
-    launch_ms = sum(a.elapsed_time(b) for a, b in logit_events) / len(logit_events)
-    vr = [n for _, n in model.vr]
-    per_launch_flops = sum(2 * c.M * c.H * n for n in vr) // len(vr)
+    fl = [launch_flops(parse_launch(n)[3], parse_launch(n)[4]) for n, _ in roof_recs]
+    launch_ms = sum(m for _, m in roof_recs) / len(roof_recs)
+    per_launch_flops = sum(fl) / len(fl)
     achieved = per_launch_flops / (launch_ms * 1e-3) / 1e12
-    traffic = ROOFLINE_TRAFFIC["bytes_per_launch"] if ROOFLINE_TRAFFIC["gemm_sha"] == _gemm_sha() else None
-    roofline = {"kernel": "gemm_bf16_kernel via tied_logits "
-                          f"({c.M}x{vr[0]}x{c.H} per shard: <256,256,64,2,4,2,NT,EpiStore> over 96 tile "
-                          "columns + <64,128,64,2,4,3,NT,EpiStore> over the last 553 columns)",
-                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "avg_launch_us": round(launch_ms * 1e3, 2), "flops_per_launch": per_launch_flops,
-                "launches_timed": len(logit_events), "launches_per_call": 2}
+    roofline = {"kernel": top_inst, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": profile_traffic(top_inst), "avg_launch_us": round(launch_ms * 1e3, 2),
+                "flops_per_launch": int(per_launch_flops), "launches_timed": len(roof_recs),
+                "shapes": sorted({parse_launch(n)[0] + " " + "x".join(map(str, parse_launch(n)[3][:3]))
+                                  for n, _ in roof_recs})}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
@@ -495,7 +610,7 @@ def main():
                       "global_batch": 1, "seq_len": 2048, "parallelism": "tp2-emulated-on-1-gpu"},
            "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
            "gflop_per_step": round(flops / 1e9, 1), "wall_s_timed": round(wall, 3),
-           "roofline": roofline}
+           "roofline": roofline, "step_kernels": breakdown}
     del model
     torch.cuda.empty_cache()
     if not args.no_layer:

@@ -440,6 +440,28 @@ tps_status layernorm_bwd_residual(tps_dtype x_dt, tps_dtype dy_dt, int64_t M, in
                                   void* out_copy, float* dgamma, float* dbeta, void* ws,
                                   size_t ws_bytes, tps_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Launch tracing (measurement support, not part of the method).
+ * While tracing is on, every kernel launch the library makes whose name
+ * contains `filter` (an empty string or NULL: every launch) is bracketed by
+ * a pair of timing events recorded on the launch's own stream, for at most
+ * `max_records` launches.  A launch's name is "<entry point>:<kernel>" plus,
+ * for the GEMM kernel, its template arguments and "MxNxK z<problems>".
+ * tps_trace_start creates the events (host-side objects, no device memory)
+ * and discards earlier records; tps_trace_stop stops recording and keeps the
+ * records; tps_trace_get(i) returns record i's name (truncated to name_cap
+ * bytes including the terminating 0) and its duration in milliseconds,
+ * waiting for the launch to finish; tps_trace_clear releases the events.
+ * Tracing is process-wide and not meant for concurrent use from several
+ * threads.  Errors: TPS_EINVAL for max_records outside [1, 2^20] or a bad
+ * record index, TPS_EHIP when an event call fails.
+ * ------------------------------------------------------------------------ */
+tps_status tps_trace_start(const char* filter, int max_records);
+tps_status tps_trace_stop(void);
+int tps_trace_count(void);
+tps_status tps_trace_get(int i, char* name, int name_cap, float* ms);
+tps_status tps_trace_clear(void);
+
 #ifdef __cplusplus
 }
 #endif

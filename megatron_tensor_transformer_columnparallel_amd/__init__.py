@@ -19,4 +19,5 @@ from .binding import (  # noqa: F401
     column_linear_fwd, column_linear_bwd, row_linear_fwd, row_linear_bwd, shard_reduce_bias,
     shard_reduce_scatter, shard_all_gather, embedding_fwd, dropout_apply,
     layernorm_fwd, layernorm_bwd, layernorm_bwd_workspace, layernorm_bwd_residual,
+    trace_start, trace_stop, trace_records, trace_clear,
 )

@@ -62,6 +62,11 @@ SIGNATURES = {
     "layernorm_bwd_workspace": (_sz, [_i64, _i64]),
     "layernorm_bwd": (_i32, [_i32, _i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
+    "tps_trace_start": (_i32, [ctypes.c_char_p, _i32]),
+    "tps_trace_stop": (_i32, []),
+    "tps_trace_count": (_i32, []),
+    "tps_trace_get": (_i32, [_i32, ctypes.c_char_p, _i32, ctypes.POINTER(_f32)]),
+    "tps_trace_clear": (_i32, []),
     "layernorm_bwd_residual": (_i32, [_i32, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
 }
@@ -532,3 +537,30 @@ def layernorm_bwd_residual(x, gamma, mean, rstd, dy, res, out, dgamma, dbeta, ws
                                       _p(out), _p(out_copy), _p(dgamma),
                                       _p(dbeta), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "layernorm_bwd_residual")
+
+
+# ---------------------------------------------------------------- launch tracing
+
+def trace_start(filter: str = "", max_records: int = 65536):
+    """Record timing events around every library kernel launch whose name
+    contains ``filter`` (see tps_trace_start)."""
+    _check(lib.tps_trace_start(filter.encode(), max_records), "tps_trace_start")
+
+
+def trace_stop():
+    _check(lib.tps_trace_stop(), "tps_trace_stop")
+
+
+def trace_records():
+    """[(name, ms)] of the recorded launches (waits for each to finish)."""
+    out = []
+    buf = ctypes.create_string_buffer(512)
+    ms = ctypes.c_float()
+    for i in range(lib.tps_trace_count()):
+        _check(lib.tps_trace_get(i, buf, len(buf), ctypes.byref(ms)), "tps_trace_get")
+        out.append((buf.value.decode(), ms.value))
+    return out
+
+
+def trace_clear():
+    _check(lib.tps_trace_clear(), "tps_trace_clear")

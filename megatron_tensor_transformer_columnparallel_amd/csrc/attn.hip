@@ -359,6 +359,7 @@ extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int
 extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d, int causal,
                                   const void* X, const void* Wqkv_i, const void* Wo_i, void* QKV_i, void* O_i,
                                   float* lse_i, void* Z_i, void* ws, size_t ws_bytes, tps_stream_t stream) {
+  ApiScope api_scope_("tp_attn_fwd");
   TPS_TRY(attn_checks("tp_attn_fwd", dt, b, sq, h, hs, d, {X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, ws}));
   const AttnFwdWs L = attn_fwd_ws_layout(b, sq, hs);
   if (ws_bytes < L.total) return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
@@ -385,9 +386,12 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   s.skip_pad = 1;   // scores are read only up to the diagonal
   TPS_TRY((gemm_bf16<true, true>(qkv, qkv + w, s, EpiScore{S2, ldp, sp, (int)hs, causal ? 1 : 0, scale_log2}, st)));
   // P = softmax rows of S (bf16), lse
-  hipLaunchKernelGGL(attn_softmax_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, S2, P, lse_i,
-                     b * hs * sq, (int)sq, ldp, causal ? 1 : 0);
-  TPS_TRY(check_launch("attn_softmax_kernel"));
+  TPS_TRY(([&]() {
+    TraceScope trace_(st, "attn_softmax_kernel");
+    hipLaunchKernelGGL(attn_softmax_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, S2, P, lse_i,
+                       b * hs * sq, (int)sq, ldp, causal ? 1 : 0);
+    return check_launch("attn_softmax_kernel");
+  }()));
   // O = P V                                (NN)  [sq x d] per head, K = keys <= query
   GemmShape s2 = shape(sq, d, sq, ldp, w3);
   s2.batch = (int)(b * hs); s2.batch_inner = (int)hs;
@@ -410,6 +414,7 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
                                   const void* X, const void* Wqkv_i, const void* Wo_i, const void* QKV_i,
                                   const void* O_i, const float* lse_i, const void* dZ, void* dX_i, void* dWqkv_i,
                                   void* dWo_i, void* ws, size_t ws_bytes, tps_stream_t stream) {
+  ApiScope api_scope_("tp_attn_bwd");
   TPS_TRY(attn_checks("tp_attn_bwd", dt, b, sq, h, hs, d,
                       {X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dZ, dX_i, dWqkv_i, dWo_i, ws}));
   const AttnWs L = attn_ws_layout(b, sq, hs, d);
@@ -450,9 +455,12 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   s2.skip_pad = 1;   // dP is read only up to the diagonal
   TPS_TRY((gemm_bf16<true, true>(dO, qkv + 2 * w, s2, EpiStore<float>{dP, ldp, hs * sp, sp}, st)));
   // dS = P * (dP - delta) * scale with delta from the same P and dP
-  hipLaunchKernelGGL(attn_ds_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, P, dP, dS,
-                     b * hs * sq, (int)sq, ldp, causal ? 1 : 0, scale);
-  TPS_TRY(check_launch("attn_ds_kernel"));
+  TPS_TRY(([&]() {
+    TraceScope trace_(st, "attn_ds_kernel");
+    hipLaunchKernelGGL(attn_ds_kernel, dim3((unsigned)ceil_div(b * hs * sq, 4)), dim3(256), 0, st, P, dP, dS,
+                       b * hs * sq, (int)sq, ldp, causal ? 1 : 0, scale);
+    return check_launch("attn_ds_kernel");
+  }()));
   // dV = P^T dO                            (TN)  [sq x d] per head, K = queries >= key
   // dK = dS^T Q                            (TN)  [sq x d] per head
   // One launch, longest K ranges first: the short tiles of either fill the

@@ -229,6 +229,7 @@ using namespace tps;
 extern "C" tps_status vocab_ce_stats(tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start,
                                      const void* L_r, const int32_t* targets, float* stats_r,
                                      tps_stream_t stream) {
+  ApiScope api_scope_("vocab_ce_stats");
   tps_status s = ce_row_checks("vocab_ce_stats", dt, T, v_rows, ldl, v_start);
   if (s != TPS_OK) return s;
   if (!L_r || !targets || !stats_r) return set_error(TPS_EINVAL, "vocab_ce_stats: null pointer");
@@ -237,6 +238,7 @@ extern "C" tps_status vocab_ce_stats(tps_dtype dt, int64_t T, int64_t v_rows, in
   if (T == 0) return TPS_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)ceil_div(T, 4));
+  TraceScope trace_(st, "ce_stats_kernel");
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(ce_stats_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
                        (int)v_rows, v_start, targets, stats_r);
@@ -248,6 +250,7 @@ extern "C" tps_status vocab_ce_stats(tps_dtype dt, int64_t T, int64_t v_rows, in
 
 extern "C" tps_status vocab_ce_combine(int n_parts, const float* const* stats, int64_t T, float* loss, float* lse,
                                        tps_stream_t stream) {
+  ApiScope api_scope_("vocab_ce_combine");
   if (n_parts < 1 || n_parts > 8) return set_error(TPS_EINVAL, "vocab_ce_combine: n_parts must be 1..8");
   if (T < 0) return set_error(TPS_EINVAL, "vocab_ce_combine: T < 0");
   if (!stats || !loss || !lse) return set_error(TPS_EINVAL, "vocab_ce_combine: null pointer");
@@ -259,6 +262,7 @@ extern "C" tps_status vocab_ce_combine(int n_parts, const float* const* stats, i
   }
   if (T == 0) return TPS_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  TraceScope trace_(st, "ce_combine_kernel");
   hipLaunchKernelGGL(ce_combine_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st, sp, n_parts, T, loss,
                      lse);
   return check_launch("ce_combine_kernel");
@@ -267,6 +271,7 @@ extern "C" tps_status vocab_ce_combine(int n_parts, const float* const* stats, i
 extern "C" tps_status vocab_ce_bwd(tps_dtype dt, int64_t T, int64_t v_rows, int64_t ldl, int64_t v_start,
                                    const void* L_r, const int32_t* targets, const float* lse, const float* dloss,
                                    void* dL_r, tps_stream_t stream) {
+  ApiScope api_scope_("vocab_ce_bwd");
   tps_status s = ce_row_checks("vocab_ce_bwd", dt, T, v_rows, ldl, v_start);
   if (s != TPS_OK) return s;
   if (!L_r || !targets || !lse || !dloss || !dL_r) return set_error(TPS_EINVAL, "vocab_ce_bwd: null pointer");
@@ -275,6 +280,7 @@ extern "C" tps_status vocab_ce_bwd(tps_dtype dt, int64_t T, int64_t v_rows, int6
   if (T == 0) return TPS_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(T < 65536 ? T : 65536));
+  TraceScope trace_(st, "ce_bwd_kernel");
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(ce_bwd_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(L_r), ldl, T,
                        (int)v_rows, v_start, targets, lse, dloss, static_cast<bf16_t*>(dL_r));

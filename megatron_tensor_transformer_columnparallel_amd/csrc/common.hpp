@@ -194,6 +194,37 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 tps_status set_error(tps_status s, const std::string& msg);
 tps_status check_launch(const char* what);
 
+// Launch tracing (measurement support; see tps_trace_start in tpshard.h).
+// ApiScope names the entry point that the launches of its lifetime belong
+// to; TraceScope brackets one kernel launch with a pair of timing events on
+// the launch's stream while tracing is on and the launch's name matches the
+// filter.  Both cost one flag test when tracing is off.
+extern bool g_trace_on;
+struct ApiScope {
+  const char* prev;
+  explicit ApiScope(const char* api);
+  ~ApiScope();
+};
+struct TraceScope {
+  int slot = -1;
+  hipStream_t stream = nullptr;
+  TraceScope() = default;
+  TraceScope(hipStream_t st, const char* kernel, const char* detail = nullptr) {
+    if (g_trace_on) begin(st, kernel, detail);
+  }
+  TraceScope(const TraceScope&) = delete;
+  TraceScope& operator=(const TraceScope&) = delete;
+  ~TraceScope() {
+    if (slot >= 0) end();
+  }
+  void begin(hipStream_t st, const char* kernel, const char* detail);
+  void end();
+};
+
+// "<v1,v2,...>" from the "[A = v1, B = v2, ...]" part of a template
+// function's __PRETTY_FUNCTION__ (namespace and element-type spelled short).
+std::string template_args(const char* pretty);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t elem_bytes(tps_dtype dt) { return dt == TPS_BF16 ? 2 : 4; }

@@ -446,6 +446,7 @@ static tps_status embed_common_checks(const char* fn, tps_dtype dt, int64_t T, i
 
 extern "C" tps_status vocab_embed_fwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
                                       const int32_t* ids, const void* E_r, void* Y_r, tps_stream_t stream) {
+  ApiScope api_scope_("vocab_embed_fwd");
   tps_status s = embed_common_checks("vocab_embed_fwd", dt, T, H, v_start, v_rows);
   if (s != TPS_OK) return s;
   if (!ids || !E_r || !Y_r) return set_error(TPS_EINVAL, "vocab_embed_fwd: null pointer");
@@ -453,6 +454,7 @@ extern "C" tps_status vocab_embed_fwd(tps_dtype dt, int64_t T, int64_t H, int64_
   if (T == 0) return TPS_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)ceil_div(T, 4));
+  TraceScope trace_(st, "embed_fwd_kernel");
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(embed_fwd_kernel<bf16_t>, grid, dim3(256), 0, st, ids, static_cast<const bf16_t*>(E_r),
                        static_cast<bf16_t*>(Y_r), T, H, v_start, v_rows);
@@ -493,6 +495,7 @@ static tps_status embed_bwd_run(tps_dtype dt, int64_t T, int64_t H, int64_t v_st
     // one workgroup per bucket of at most 256 rows: one 8-bit pass each
     const int brows = (int)ceil_div(v_rows, kRadixBuckets);
     const int nb = (int)ceil_div(v_rows, brows);
+    TraceScope trace_(st, "embed_radix_sort_kernel");
     hipLaunchKernelGGL(embed_radix_sort_kernel, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ids, keys,
                        (int)T, v_start, (int)v_rows, tbits, ceil_log2(brows), brows);
     s = check_launch("embed_radix_sort_kernel");
@@ -510,6 +513,7 @@ static tps_status embed_bwd_run(tps_dtype dt, int64_t T, int64_t H, int64_t v_st
   }
   if (s != TPS_OK) return s;
   const dim3 grid((unsigned)ceil_div(T, 4));
+  TraceScope trace_(st, "embed_bwd_accum_kernel");
   if (dt == TPS_BF16)
     hipLaunchKernelGGL(embed_bwd_accum_kernel<bf16_t>, grid, dim3(256), 0, st, keys,
                        static_cast<const bf16_t*>(dY), dE_r, T, H);
@@ -522,6 +526,7 @@ static tps_status embed_bwd_run(tps_dtype dt, int64_t T, int64_t H, int64_t v_st
 extern "C" tps_status vocab_embed_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
                                       const int32_t* ids, const void* dY, float* dE_r, void* ws,
                                       size_t ws_bytes, tps_stream_t stream) {
+  ApiScope api_scope_("vocab_embed_bwd");
   tps_status s = embed_bwd_checks("vocab_embed_bwd", dt, T, H, v_start, v_rows, ids, dY, dE_r);
   if (s != TPS_OK) return s;
   if (T == 0) return TPS_OK;
@@ -569,6 +574,7 @@ extern "C" int64_t vocab_embed_bwd_noalloc_max_tokens(void) { return kNoAllocMax
 extern "C" tps_status vocab_embed_bwd_noalloc(tps_dtype dt, int64_t T, int64_t H, int64_t v_start, int64_t v_rows,
                                               const int32_t* ids, const void* dY, float* dE_r,
                                               tps_stream_t stream) {
+  ApiScope api_scope_("vocab_embed_bwd_noalloc");
   tps_status s = embed_bwd_checks("vocab_embed_bwd_noalloc", dt, T, H, v_start, v_rows, ids, dY, dE_r);
   if (s != TPS_OK) return s;
   if (T > kNoAllocMaxTokens)

@@ -154,6 +154,7 @@ extern "C" tps_status embedding_fwd(tps_dtype dt, tps_dtype out_dt, int n_parts,
                                     const void* PE, int64_t pos_rows, const int32_t* pos, const void* TE,
                                     int64_t tt_rows, const int32_t* tt, float p, uint64_t seed, void* out,
                                     int64_t T, int64_t H, tps_stream_t stream) {
+  ApiScope api_scope_("embedding_fwd");
   const char* fn = "embedding_fwd";
   if (!dt_ok(dt) || !dt_ok(out_dt)) return set_error(TPS_EINVAL, "embedding_fwd: bad dtype");
   if (n_parts < 1 || n_parts > 8) return set_error(TPS_EINVAL, "embedding_fwd: n_parts must be 1..8");
@@ -189,6 +190,7 @@ extern "C" tps_status embedding_fwd(tps_dtype dt, tps_dtype out_dt, int n_parts,
 
 extern "C" tps_status dropout_apply(tps_dtype in_dt, tps_dtype out_dt, int64_t n, const void* x, float p,
                                     uint64_t seed, void* y, tps_stream_t stream) {
+  ApiScope api_scope_("dropout_apply");
   const char* fn = "dropout_apply";
   if (!dt_ok(in_dt) || !dt_ok(out_dt)) return set_error(TPS_EINVAL, "dropout_apply: bad dtype");
   if (n < 0) return set_error(TPS_EINVAL, "dropout_apply: n < 0");

@@ -774,6 +774,14 @@ inline tps_status launch_mfma(const bf16_t* A, const bf16_t* B, const GemmShape&
   const int64_t span_a = (AK ? BM : BK) * lda * 2, span_b = (BKC ? BN : BK) * ldb * 2;
   if (span_a >= (1LL << 32) || span_b >= (1LL << 32))
     return set_error(TPS_EINVAL, "gemm: leading dimension too large for 32-bit tile offsets");
+  TraceScope tr;
+  if (g_trace_on) {
+    static const std::string inst = template_args(__PRETTY_FUNCTION__);
+    const std::string detail = inst + " " + std::to_string(s.M) + "x" + std::to_string(s.N) + "x" +
+                               std::to_string(s.K) + " z" + std::to_string(s.batch * s.groups) +
+                               (s.kmode || s.skip_upper ? " causal" : "");
+    tr.begin(st, "gemm_bf16_kernel", detail.c_str());
+  }
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, WM, WN, NS, AK, BKC, Epi>), dim3((unsigned)tiles),
                      dim3(WM * WN * 64), 0, st, A, B, s, epi, alt);
   return check_launch("gemm_bf16_kernel");

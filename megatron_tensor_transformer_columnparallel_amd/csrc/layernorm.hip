@@ -354,6 +354,7 @@ template <typename TX, typename TY>
 static void launch_ln_fwd(int64_t M, int64_t H, float eps, const void* x, const float* g, const float* b, void* y,
                           float* mean, float* rstd, hipStream_t st) {
   const int nc = (int)ceil_div(H, 256 * kLnV);   // 1..4 (H <= 8192)
+  TraceScope trace_(st, "ln_fwd_kernel");
 #define TPS_LNF(NC)                                                                                             \
   hipLaunchKernelGGL((ln_fwd_kernel<TX, TY, NC>), dim3((unsigned)M), dim3(256), 0, st, static_cast<const TX*>(x), g, \
                      b, static_cast<TY*>(y), mean, rstd, H, eps)
@@ -372,6 +373,7 @@ static void launch_ln_bwd(int64_t M, int64_t H, const void* x, const float* g, c
   const TDY* dyp = static_cast<const TDY*>(dy);
   TDX* dxp = static_cast<TDX*>(dx);
   constexpr int64_t W1 = (int64_t)kLnBwdThreads * kLnV;   // 4096
+  TraceScope trace_(st, H == W1 ? "ln_bwd_rows_kernel" : "ln_bwd_kernel");
   if (H == W1)
     hipLaunchKernelGGL((ln_bwd_rows_kernel<1, RES, TX, TDY, TDX>), grid, dim3(kLnBwdThreads), 0, st, xp, g, mean,
                        rstd, dyp, dxp, part, M, res, copy);
@@ -387,6 +389,7 @@ using namespace tps;
 extern "C" tps_status layernorm_fwd(tps_dtype x_dt, tps_dtype y_dt, int64_t M, int64_t H, float eps, const void* x,
                                     const float* gamma, const float* beta, void* y, float* mean, float* rstd,
                                     tps_stream_t stream) {
+  ApiScope api_scope_("layernorm_fwd");
   tps_status s = ln_checks("layernorm_fwd", {x_dt, y_dt}, M, H, {x, gamma, beta, y, mean, rstd});
   if (s != TPS_OK) return s;
   if (!(eps >= 0.f)) return set_error(TPS_EINVAL, "layernorm_fwd: eps must be >= 0");
@@ -408,6 +411,7 @@ extern "C" tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype d
                                     const void* x, const float* gamma, const float* mean, const float* rstd,
                                     const void* dy, void* dx, float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
                                     tps_stream_t stream) {
+  ApiScope api_scope_("layernorm_bwd");
   tps_status s = ln_checks("layernorm_bwd", {x_dt, dy_dt, dx_dt}, M, H, {x, gamma, mean, rstd, dy, dx, dgamma, dbeta, ws});
   if (s != TPS_OK) return s;
   if (ws_bytes < layernorm_bwd_workspace(M, H)) return set_error(TPS_EWORKSPACE, "layernorm_bwd: workspace too small");
@@ -427,6 +431,7 @@ extern "C" tps_status layernorm_bwd(tps_dtype x_dt, tps_dtype dy_dt, tps_dtype d
   s = check_launch("ln_bwd_kernel");
   if (s != TPS_OK) return s;
   const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
+  TraceScope trace_(st, "ln_param_reduce_kernel");
   hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(2 * H, 32)), dim3(256), 0, st, part, dgamma,
                      dbeta, nblk, H);
   return check_launch("ln_param_reduce_kernel");
@@ -437,6 +442,7 @@ extern "C" tps_status layernorm_bwd_residual(tps_dtype x_dt, tps_dtype dy_dt, in
                                              const void* dy, const float* res, float* out, void* out_copy,
                                              float* dgamma, float* dbeta, void* ws, size_t ws_bytes,
                                              tps_stream_t stream) {
+  ApiScope api_scope_("layernorm_bwd_residual");
   tps_status s = ln_checks("layernorm_bwd_residual", {x_dt, dy_dt}, M, H,
                            {x, gamma, mean, rstd, dy, res, out, dgamma, dbeta, ws});
   if (s != TPS_OK) return s;
@@ -458,6 +464,7 @@ extern "C" tps_status layernorm_bwd_residual(tps_dtype x_dt, tps_dtype dy_dt, in
   s = check_launch("ln_bwd_kernel");
   if (s != TPS_OK) return s;
   const int64_t nblk = ceil_div(M, kLnRowsPerBlock);
+  TraceScope trace_(st, "ln_param_reduce_kernel");
   hipLaunchKernelGGL(ln_param_reduce_kernel, dim3((unsigned)ceil_div(2 * H, 32)), dim3(256), 0, st, part, dgamma,
                      dbeta, nblk, H);
   return check_launch("ln_param_reduce_kernel");

@@ -197,6 +197,7 @@ using namespace tps;
 extern "C" tps_status column_linear_fwd(tps_dtype dt, int64_t M, int64_t h_in, int64_t n_r, const void* X,
                                         const void* A_r, const void* b_r, void* Y, int64_t ldy,
                                         tps_stream_t stream) {
+  ApiScope api_scope_("column_linear_fwd");
   const char* fn = "column_linear_fwd";
   TPS_LTRY(dims_ok(fn, dt, M, h_in, n_r));
   TPS_LTRY(ptrs_ok(fn, {X, A_r, Y}));
@@ -214,6 +215,7 @@ extern "C" tps_status column_linear_fwd(tps_dtype dt, int64_t M, int64_t h_in, i
 extern "C" tps_status column_linear_bwd(tps_dtype dt, int64_t M, int64_t h_in, int64_t n_r, const void* X,
                                         const void* A_r, const void* dY, int64_t lddy, void* dX_r, void* dA_r,
                                         float* db_r, tps_stream_t stream) {
+  ApiScope api_scope_("column_linear_bwd");
   const char* fn = "column_linear_bwd";
   TPS_LTRY(dims_ok(fn, dt, M, h_in, n_r));
   TPS_LTRY(ptrs_ok(fn, {X, A_r, dY, dX_r, dA_r}));
@@ -235,6 +237,7 @@ extern "C" tps_status column_linear_bwd(tps_dtype dt, int64_t M, int64_t h_in, i
 
 extern "C" tps_status row_linear_fwd(tps_dtype dt, int64_t M, int64_t k_r, int64_t h_out, const void* X_r,
                                      int64_t ldx, const void* B_r, void* Y_r, tps_stream_t stream) {
+  ApiScope api_scope_("row_linear_fwd");
   const char* fn = "row_linear_fwd";
   TPS_LTRY(dims_ok(fn, dt, M, k_r, h_out));
   TPS_LTRY(ptrs_ok(fn, {X_r, B_r, Y_r}));
@@ -251,6 +254,7 @@ extern "C" tps_status row_linear_fwd(tps_dtype dt, int64_t M, int64_t k_r, int64
 extern "C" tps_status row_linear_bwd(tps_dtype dt, int64_t M, int64_t k_r, int64_t h_out, const void* X_r,
                                      int64_t ldx, const void* B_r, const void* dY, void* dX_r, int64_t lddx,
                                      void* dB_r, float* db, tps_stream_t stream) {
+  ApiScope api_scope_("row_linear_bwd");
   const char* fn = "row_linear_bwd";
   TPS_LTRY(dims_ok(fn, dt, M, k_r, h_out));
   TPS_LTRY(ptrs_ok(fn, {X_r, B_r, dY, dX_r, dB_r}));
@@ -273,6 +277,7 @@ extern "C" tps_status row_linear_bwd(tps_dtype dt, int64_t M, int64_t k_r, int64
 
 extern "C" tps_status shard_reduce_bias(tps_dtype dt, int n_parts, const void* const* parts, const void* bias,
                                         void* out, int64_t M, int64_t N, tps_stream_t stream) {
+  ApiScope api_scope_("shard_reduce_bias");
   const char* fn = "shard_reduce_bias";
   if (dt != TPS_F32 && dt != TPS_BF16) return set_error(TPS_EINVAL, "shard_reduce_bias: bad dtype");
   if (n_parts < 1 || n_parts > 8) return set_error(TPS_EINVAL, "shard_reduce_bias: n_parts must be 1..8");

@@ -73,6 +73,7 @@ using namespace tps;
 
 extern "C" tps_status tp_mlp_fwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i, const void* X, const void* A_i,
                                  const void* B_i, void* P_i, void* H_i, void* Z_i, tps_stream_t stream) {
+  ApiScope api_scope_("tp_mlp_fwd");
   TPS_TRY(mlp_checks("tp_mlp_fwd", dt, M, h, f_i, {X, A_i, B_i, P_i, H_i, Z_i}));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dt == TPS_BF16)
@@ -91,6 +92,7 @@ extern "C" size_t tp_mlp_bwd_workspace(tps_dtype dt, int64_t M, int64_t h, int64
 extern "C" tps_status tp_mlp_bwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i, const void* X, const void* A_i,
                                  const void* B_i, const void* P_i, const void* H_i, const void* dZ, void* dX_i,
                                  void* dA_i, void* dB_i, void* ws, size_t ws_bytes, tps_stream_t stream) {
+  ApiScope api_scope_("tp_mlp_bwd");
   TPS_TRY(mlp_checks("tp_mlp_bwd", dt, M, h, f_i, {X, A_i, B_i, P_i, H_i, dZ, dX_i, dA_i, dB_i, ws}));
   if (ws_bytes < tp_mlp_bwd_workspace(dt, M, h, f_i))
     return set_error(TPS_EWORKSPACE, "tp_mlp_bwd: workspace too small");
@@ -124,6 +126,7 @@ static tps_status logits_checks(const char* fn, tps_dtype dt, int64_t T, int64_t
 
 extern "C" tps_status tied_logits(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, int64_t ldl, const void* X,
                                   const void* E_r, void* L_r, tps_stream_t stream) {
+  ApiScope api_scope_("tied_logits");
   TPS_TRY(logits_checks("tied_logits", dt, T, H, v_rows, ldl, {X, E_r, L_r}));
   hipStream_t st = static_cast<hipStream_t>(stream);
   // L_r = X E_r^T                          (NT)  [T x v_rows], K = H
@@ -138,6 +141,7 @@ extern "C" tps_status tied_logits(tps_dtype dt, int64_t T, int64_t H, int64_t v_
 extern "C" tps_status tied_logits_bwd(tps_dtype dt, int64_t T, int64_t H, int64_t v_rows, int64_t ldl,
                                       const void* X, const void* E_r, const void* dL_r, void* dX_r, float* dE_r,
                                       tps_stream_t stream) {
+  ApiScope api_scope_("tied_logits_bwd");
   TPS_TRY(logits_checks("tied_logits_bwd", dt, T, H, v_rows, ldl, {X, E_r, dL_r, dX_r, dE_r}));
   hipStream_t st = static_cast<hipStream_t>(stream);
   // dX_r = dL_r E_r                        (NN)  [T x H], K = v_rows

@@ -89,6 +89,7 @@ __global__ void __launch_bounds__(256) shard_reduce_add_kernel(const Tr* res, Pa
 template <typename Tr, typename Tp, typename To>
 static void launch_add(tps_dtype copy_dt, const void* res, const PartPtrs& pp, int np, void* out, void* copy,
                        int64_t n, dim3 grid, hipStream_t st) {
+  TraceScope trace_(st, "shard_reduce_add_kernel");
   if (copy_dt == TPS_BF16)
     hipLaunchKernelGGL((shard_reduce_add_kernel<Tr, Tp, To, bf16_t>), grid, dim3(256), 0, st,
                        static_cast<const Tr*>(res), pp, np, static_cast<To*>(out), static_cast<bf16_t*>(copy), n);
@@ -113,6 +114,7 @@ static bool ok_dt(tps_dtype d) { return d == TPS_F32 || d == TPS_BF16; }
 extern "C" tps_status shard_reduce_add(tps_dtype res_dt, const void* res, tps_dtype part_dt, int n_parts,
                                        const void* const* parts, tps_dtype out_dt, void* out, tps_dtype copy_dt,
                                        void* out_copy, int64_t n, tps_stream_t stream) {
+  ApiScope api_scope_("shard_reduce_add");
   if (!ok_dt(res_dt) || !ok_dt(part_dt) || !ok_dt(out_dt) || !ok_dt(copy_dt))
     return set_error(TPS_EINVAL, "shard_reduce_add: bad dtype");
   if (n_parts < 1 || n_parts > 7) return set_error(TPS_EINVAL, "shard_reduce_add: n_parts must be in [1, 7]");
@@ -141,6 +143,7 @@ extern "C" tps_status shard_reduce_add(tps_dtype res_dt, const void* res, tps_dt
 extern "C" tps_status shard_reduce(tps_dtype in_dt, tps_dtype out_dt, int n_parts,
                                    const void* const* parts, void* out, int64_t n,
                                    tps_stream_t stream) {
+  ApiScope api_scope_("shard_reduce");
   if ((in_dt != TPS_F32 && in_dt != TPS_BF16) || (out_dt != TPS_F32 && out_dt != TPS_BF16))
     return set_error(TPS_EINVAL, "shard_reduce: bad dtype");
   if (n_parts < 1 || n_parts > 8) return set_error(TPS_EINVAL, "shard_reduce: n_parts must be in [1, 8]");
@@ -158,6 +161,7 @@ extern "C" tps_status shard_reduce(tps_dtype in_dt, tps_dtype out_dt, int n_part
   const int64_t nvec = n / 8;
   int64_t blocks = ceil_div(nvec > 0 ? nvec : 1, 256);
   if (blocks > 65536) blocks = 65536;
+  TraceScope trace_(st, "shard_reduce_kernel");
 #define TPS_RED(TI, TO) \
   hipLaunchKernelGGL((shard_reduce_kernel<TI, TO>), dim3((unsigned)blocks), dim3(256), 0, st, pp, n_parts, \
                      static_cast<TO*>(out), n)

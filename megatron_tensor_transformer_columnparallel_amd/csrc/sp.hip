@@ -121,6 +121,7 @@ using namespace tps;
 extern "C" tps_status shard_reduce_scatter(tps_dtype part_dt, tps_dtype out_dt, int n_parts,
                                            const void* const* parts, const void* const* res, void* const* outs,
                                            int64_t M, int64_t H, tps_stream_t stream) {
+  ApiScope api_scope_("shard_reduce_scatter");
   const char* fn = "shard_reduce_scatter";
   if (!dt_ok(part_dt) || !dt_ok(out_dt)) return set_error(TPS_EINVAL, "shard_reduce_scatter: bad dtype");
   tps_status s = common(fn, n_parts, M, H);
@@ -152,6 +153,7 @@ extern "C" tps_status shard_reduce_scatter(tps_dtype part_dt, tps_dtype out_dt, 
 
 extern "C" tps_status shard_all_gather(tps_dtype dt, int n_parts, const void* const* parts, void* out, int64_t M,
                                        int64_t H, tps_stream_t stream) {
+  ApiScope api_scope_("shard_all_gather");
   const char* fn = "shard_all_gather";
   if (!dt_ok(dt)) return set_error(TPS_EINVAL, "shard_all_gather: bad dtype");
   tps_status s = common(fn, n_parts, M, H);

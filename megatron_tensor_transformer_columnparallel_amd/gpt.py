@@ -128,8 +128,6 @@ class TPGPT:
         self.ce_stats = [_emp((M, 4), f32) for _ in range(c.n)]
         self.ce_loss, self.ce_lse = _emp((M,), f32), _emp((M,), f32)
         self.ce_dloss = torch.full((M,), 1.0 / M, dtype=f32, device="cuda")   # gradient of the mean loss
-        # when a list, (start, end) torch.cuda.Events around each tied_logits call are appended to it
-        self.logit_events = None
 
     def logits_view(self, r):
         return self.logits[r][:, :self.vr[r][1]]
@@ -155,13 +153,7 @@ class TPGPT:
         self.x_out = x
         tp.shard_reduce([x], self.x_bf)                                            # round to bf16
         for r in range(cf.n):
-            if self.logit_events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
             tp.tied_logits(self.x_bf, self.E[r], self.logits_view(r))
-            if self.logit_events is not None:
-                e1.record()
-                self.logit_events.append((e0, e1))
 
     def loss(self, targets, dloss=None):
         """Vocab-parallel cross entropy of the logits of the last forward

@@ -229,3 +229,10 @@ def test_embedding_and_dropout_validation(tp):
     assert lib.dropout_apply(1, 1, 16, ALIGNED + 8, 0.5, 3, ALIGNED, None) == E                  # misaligned
     assert lib.dropout_apply(1, 1, -1, ALIGNED, 0.5, 3, ALIGNED, None) == E                      # n < 0
     assert lib.tps_last_error().startswith(b"dropout_apply")
+
+
+def test_trace_rejects_bad_record_counts(tp):
+    for n in (0, -1, (1 << 20) + 1):
+        with pytest.raises(tp.TpsError):
+            tp.trace_start("", n)
+    assert tp.lib.tps_trace_count() == 0
