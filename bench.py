@@ -481,11 +481,23 @@ def step_breakdown(recs, layer_flops_total):
                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     top = sorted(by_inst.items(), key=lambda kv: -kv[1][1])
     top_gemm = next(k for k, _ in top if "<" in k)
+    # attention core per call (one shard): every launch of tp_attn_* except
+    # the four dense projections (QKV, output, and their backward products)
+    core = {}
+    for name, ms in recs:
+        api, kernel, targs, shape, causal = parse_launch(name)
+        if api in ("tp_attn_fwd", "tp_attn_bwd") and (shape is None or causal):
+            e = core.setdefault(api, {}).setdefault(kernel + targs + ("" if shape is None else " causal x%d" % shape[3]),
+                                                   [0, 0.0])
+            e[0] += 1
+            e[1] += ms
     headline = layer_flops_total / (attn_mlp_ms * 1e-3) / 1e12
     return {
         "kernel_ms_per_step": round(total_ms, 3),
         "top_instances": [{"instance": k, "launches": n, "ms": round(ms, 3), "share": round(ms / total_ms, 4)}
-                          for k, (n, ms) in top[:8]],
+                          for k, (n, ms) in top[:12]],
+        "attention_core_us_per_call": {api: {k: round(ms / n * 1e3, 2) for k, (n, ms) in d.items()}
+                                       for api, d in core.items()},
         "gemm_shapes": shapes,
         "attn_mlp_kernel_time": {
             "TFLOP/s": round(headline, 1), "frac_of_bf16_peak": round(headline / PEAK_BF16_TFLOPS, 4),

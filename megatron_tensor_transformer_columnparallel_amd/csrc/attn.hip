@@ -20,6 +20,7 @@
 // skip the causally-zero blocks.
 #include <string>
 
+#include "flash_attn.hpp"
 #include "gemm.hpp"
 
 namespace tps {
@@ -349,11 +350,69 @@ static tps_status attn_checks(const char* fn, tps_dtype dt, int64_t b, int64_t s
 
 using namespace tps;
 
+// Which forward core a call takes.  The flash kernel is compiled for head
+// dims 64..512.  Up to 256 each wave keeps 32 query rows (Q fragments and
+// the fp32 output accumulator fit one wave's registers), and every K or V
+// fragment read from LDS feeds two MFMAs.  At 512 a wave can keep only 16
+// rows, so each fragment feeds one MFMA and the kernel is bound by LDS
+// bandwidth: at sq = 2048 with 4 heads it took 55 us plus 26 us to merge the
+// key chunks, against 61 us for the score GEMM, row softmax and PV GEMM.  So
+// head dim 512 takes the flash kernel only past sq = 4096, where the stored
+// scores and probabilities (6 bytes per query-key pair and head) would need
+// gigabytes.
+static bool use_flash(int64_t d, int64_t sq) {
+  if (d == 64 || d == 128 || d == 256) return true;
+  return d == 512 && sq > 4096;
+}
+
+// Compute units of the current device (the flash forward sizes its work
+// items so that one round of them fills the chip).
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
+
 extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d) {
   (void)dt;
   (void)h;
   if (b <= 0 || sq <= 0 || hs <= 0 || d <= 0) return 0;
+  if (use_flash(d, sq)) {
+    // the query has no causal argument: cover the larger of the two plans
+    // (without the mask every block has all keys, so more chunks)
+    const int cus = device_cus();
+    return std::max(flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 1, cus), (int)d),
+                    flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 0, cus), (int)d));
+  }
   return attn_fwd_ws_layout(b, sq, hs).total;
+}
+
+// Flash forward core: O and lse from QKV (see flash_attn.hpp).
+// Row blocks per wave: two (32 rows, four waves of up to 512 registers) up
+// to head dim 256; at 512 the 32 x 512 fp32 accumulator plus the Q
+// fragments do not fit one wave's registers, so waves take 16 rows (eight
+// waves of 256 registers).
+template <int D>
+static tps_status flash_fwd_core(const bf16_t* qkv, bf16_t* o, float* lse, void* ws, const flash::Plan& p,
+                                 hipStream_t st) {
+  const int total = p.items_per_z * p.nz;
+  float* part = static_cast<float*>(ws);
+  {
+    TraceScope trace_(st, "attn_fwd_flash_kernel");
+    constexpr int QB = D >= 512 ? 1 : 2;
+    hipLaunchKernelGGL((flash::attn_fwd_flash_kernel<D, QB>), dim3((unsigned)total),
+                       dim3(flash::Shape<D, QB>::THREADS), 0, st, qkv, o, lse, part, p, total);
+    TPS_TRY(check_launch("attn_fwd_flash_kernel"));
+  }
+  const int mz = flash::plan_merges_per_z(p);
+  if (mz == 0) return TPS_OK;
+  TraceScope trace_(st, "attn_fwd_merge_kernel");
+  hipLaunchKernelGGL((flash::attn_fwd_merge_kernel<D>), dim3((unsigned)(mz * p.nz * flash::merge_groups<D>())),
+                     dim3(flash::kMergeThreads), 0, st, part, o, lse, p, total, mz);
+  return check_launch("attn_fwd_merge_kernel");
 }
 
 extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d, int causal,
@@ -361,9 +420,28 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
                                   float* lse_i, void* Z_i, void* ws, size_t ws_bytes, tps_stream_t stream) {
   ApiScope api_scope_("tp_attn_fwd");
   TPS_TRY(attn_checks("tp_attn_fwd", dt, b, sq, h, hs, d, {X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i, ws}));
-  const AttnFwdWs L = attn_fwd_ws_layout(b, sq, hs);
-  if (ws_bytes < L.total) return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
+  if (ws_bytes < tp_attn_fwd_workspace(dt, b, sq, h, hs, d))
+    return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_flash(d, sq)) {
+    const int64_t M = b * sq, w = hs * d, w3 = 3 * w;
+    bf16_t* qkv = (bf16_t*)QKV_i;
+    bf16_t* o = (bf16_t*)O_i;
+    // QKV_i = X Wqkv_i                       (NN)
+    TPS_TRY((gemm_bf16<true, false>((const bf16_t*)X, (const bf16_t*)Wqkv_i, shape(M, w3, h, h, w3),
+                                    EpiStore<bf16_t>{qkv, w3, 0, 0}, st)));
+    const flash::Plan p = flash::make_plan(b, sq, hs, (int)d, causal ? 1 : 0, device_cus());
+    if (ws_bytes < flash::plan_workspace(p, (int)d))
+      return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
+    if (d == 64) TPS_TRY(flash_fwd_core<64>(qkv, o, lse_i, ws, p, st));
+    else if (d == 128) TPS_TRY(flash_fwd_core<128>(qkv, o, lse_i, ws, p, st));
+    else if (d == 256) TPS_TRY(flash_fwd_core<256>(qkv, o, lse_i, ws, p, st));
+    else TPS_TRY(flash_fwd_core<512>(qkv, o, lse_i, ws, p, st));
+    // Z_i = O_i Wo_i                         (NN)
+    return gemm_bf16<true, false>(o, (const bf16_t*)Wo_i, shape(M, h, w, w, h),
+                                  EpiStore<bf16_t>{(bf16_t*)Z_i, h, 0, 0}, st);
+  }
+  const AttnFwdWs L = attn_fwd_ws_layout(b, sq, hs);
   const int64_t M = b * sq, w = hs * d, w3 = 3 * w;
   const bf16_t* x = (const bf16_t*)X;
   bf16_t* qkv = (bf16_t*)QKV_i;
