@@ -52,9 +52,16 @@ backward
   ``wgrad``    the weight gradients dW_QKV, dW_O, dA, dB as stored outputs
 
 ``delta`` selects how the softmax backward's row term is formed:
-  ``"o"``  delta_i = sum_j dO_ij O_ij (the oracle's form, with O as stored);
-  ``"p"``  delta_i = sum_j P_ij dP_ij / sum_j P_ij with the P that forms dS,
-           which makes every row of dS sum to zero for that P.
+  ``"o"``   delta_i = sum_j dO_ij O_ij (the oracle's form, with O as stored);
+  ``"o32"`` the same sum with O before the ``o`` rounding (a kernel that
+            keeps an fp32 copy of O for this sum);
+  ``"p"``   delta_i = sum_j P_ij dP_ij / sum_j P_ij with the P that forms dS,
+            which makes every row of dS sum to zero for that P.
+``p_fwd_form`` selects which probabilities ``p_fwd`` rounds:
+  ``"normalised"``    P = exp(S - max) / l, then O = round(P) V;
+  ``"unnormalised"``  E = exp(S - max), O = (round(E) V) / l with l the sum of
+                      the unrounded E (a kernel that normalises O once at the
+                      end of its pass over the keys).
 ``ds_center`` (only with ``ds``): dQ is formed as dS_q (K - kbar) + r kbar
 with kbar the mean key of the head and r the exact row sums of the rounded
 dS_q: the same value in exact arithmetic, but the rounding error of dS_q
@@ -78,15 +85,18 @@ POINTS = ("ln_out", "qkv", "p_fwd", "o", "part_fwd", "mlp_pre", "mlp_h", "x_fina
 class Rounding:
     """Which storage points round to bf16, and the softmax-backward options."""
 
-    def __init__(self, points=(), delta="o", ds_center=False):
+    def __init__(self, points=(), delta="o", ds_center=False, p_fwd_form="normalised"):
         unknown = set(points) - set(POINTS)
         if unknown:
             raise ValueError(f"unknown storage points {sorted(unknown)}")
-        if delta not in ("o", "p"):
-            raise ValueError("delta must be 'o' or 'p'")
+        if delta not in ("o", "o32", "p"):
+            raise ValueError("delta must be 'o', 'o32' or 'p'")
+        if p_fwd_form not in ("normalised", "unnormalised"):
+            raise ValueError("p_fwd_form must be 'normalised' or 'unnormalised'")
         self.points = frozenset(points)
         self.delta = delta
         self.ds_center = bool(ds_center)
+        self.p_fwd_form = p_fwd_form
 
     def __call__(self, name, x):
         return to_bf16_via_f32(x) if name in self.points else x
@@ -122,8 +132,11 @@ def head_forward(Q, K, V, rnd, causal=True):
     mx = S.max(axis=1, keepdims=True)
     E = np.exp(S - mx)
     l = E.sum(axis=1, keepdims=True)
-    P = E / l
-    O = rnd("p_fwd", P) @ V
+    if rnd.p_fwd_form == "unnormalised":
+        O = (rnd("p_fwd", E) @ V) / l
+    else:
+        P = E / l
+        O = rnd("p_fwd", P) @ V
     lse = (mx + np.log(l))[:, 0]
     return O, lse
 
@@ -131,7 +144,8 @@ def head_forward(Q, K, V, rnd, causal=True):
 def head_backward(Q, K, V, O, dO, lse, rnd, causal=True):
     """``attention_head_backward`` with its storage points.
 
-    O is the stored forward output; lse the forward's log-sum-exp.  When a
+    O is the forward output the row term reads (stored, or its fp32 copy
+    with ``delta="o32"``); lse the forward's log-sum-exp.  When a
     point of the recomputed probabilities is rounded, P is recomputed from
     lse as exp(S - lse) (what a kernel that keeps only lse does); otherwise
     the oracle's own normalisation is used.
@@ -147,7 +161,7 @@ def head_backward(Q, K, V, O, dO, lse, rnd, causal=True):
     dV = rnd("p_bwd", P).T @ dO
     dP = dO @ V.T
     Pd = rnd("p_ds", P)
-    if rnd.delta == "o":
+    if rnd.delta in ("o", "o32"):
         delta = (dO * O).sum(axis=1, keepdims=True)
     else:
         den = Pd.sum(axis=1, keepdims=True)
@@ -173,7 +187,8 @@ def head_backward(Q, K, V, O, dO, lse, rnd, causal=True):
 # ---------------------------------------------------------------------------
 
 def attention_shard_forward(X, Wqkv, Wo, b, s, nh, d, rnd, causal=True):
-    """``attention_layer_forward`` with ``qkv``, ``p_fwd``, ``o`` and ``part_fwd``."""
+    """``attention_layer_forward`` with ``qkv``, ``p_fwd``, ``o`` and ``part_fwd``.
+    Returns QKV, O (as stored), lse, Z and O before the ``o`` rounding."""
     QKV = rnd("qkv", X @ _f64(Wqkv))
     w = nh * d
     O = np.zeros((b * s, w))
@@ -185,13 +200,16 @@ def attention_shard_forward(X, Wqkv, Wo, b, s, nh, d, rnd, causal=True):
             K = QKV[rows, w + j * d:w + (j + 1) * d]
             V = QKV[rows, 2 * w + j * d:2 * w + (j + 1) * d]
             O[rows, j * d:(j + 1) * d], lse[bi, j] = head_forward(Q, K, V, rnd, causal)
+    O32 = O
     O = rnd("o", O)
     Z = rnd("part_fwd", O @ _f64(Wo))
-    return QKV, O, lse, Z
+    return QKV, O, lse, Z, O32
 
 
-def attention_shard_backward(X, Wqkv, Wo, QKV, O, lse, dZ, b, s, nh, d, rnd, causal=True):
-    """``attention_layer_backward`` from the stored QKV, O and lse."""
+def attention_shard_backward(X, Wqkv, Wo, QKV, O, lse, dZ, b, s, nh, d, rnd, causal=True, O32=None):
+    """``attention_layer_backward`` from the stored QKV, O and lse (and, for
+    ``delta="o32"``, the unrounded O32)."""
+    Od = O32 if rnd.delta == "o32" else O
     w = nh * d
     dWo = rnd("wgrad", O.T @ dZ)
     dO = rnd("do", dZ @ _f64(Wo).T)
@@ -202,7 +220,7 @@ def attention_shard_backward(X, Wqkv, Wo, QKV, O, lse, dZ, b, s, nh, d, rnd, cau
             cq = slice(j * d, (j + 1) * d)
             ck = slice(w + j * d, w + (j + 1) * d)
             cv = slice(2 * w + j * d, 2 * w + (j + 1) * d)
-            dq, dk, dv = head_backward(QKV[rows, cq], QKV[rows, ck], QKV[rows, cv], O[rows, cq], dO[rows, cq],
+            dq, dk, dv = head_backward(QKV[rows, cq], QKV[rows, ck], QKV[rows, cv], Od[rows, cq], dO[rows, cq],
                                        lse[bi, j], rnd, causal)
             dQKV[rows, cq], dQKV[rows, ck], dQKV[rows, cv] = dq, dk, dv
     dQKV = rnd("dqkv", dQKV)
@@ -259,7 +277,7 @@ def gpt_forward(ids, E, layers, b, s, nheads, d, n, rnd, eps=1e-5, causal=True):
         mouts = [mlp_shard_forward(y2, split_columns(lw["A"], n, r), split_rows(lw["B"], n, r), rnd)
                  for r in range(n)]
         cache["ln"].append((y1, mu1, rs1, x2, y2, mu2, rs2))
-        cache["attn"].append([(o[0], o[1], o[2]) for o in outs])
+        cache["attn"].append([(o[0], o[1], o[2], o[4] if rnd.delta == "o32" else None) for o in outs])
         cache["mlp"].append([(o[0], o[1]) for o in mouts])
         x = x2 + shard_reduce([o[2] for o in mouts])
     cache["x_out"] = x
@@ -307,10 +325,10 @@ def gpt_backward_layers(ids, E, layers, cache, dlogits, b, s, nheads, d, n, rnd,
         dx2c = rnd("dx_copy", dx2)
         ares = []
         for r in range(n):
-            QKV, O, lse = cache["attn"][li][r]
+            QKV, O, lse, O32 = cache["attn"][li][r]
             ares.append(attention_shard_backward(y1, shard_qkv_weight(lw["WQ"], lw["WK"], lw["WV"], n, r, d),
                                                  shard_out_weight(lw["WO"], n, r, d), QKV, O, lse, dx2c,
-                                                 b, s, hs, d, rnd, causal))
+                                                 b, s, hs, d, rnd, causal, O32))
         dy1 = shard_reduce([o[0] for o in ares])
         dx_in_ln, dg1, db1 = layernorm_backward(x_in, _f64(lw["g1"]), mu1, rs1, dy1)
         dx = dx2 + dx_in_ln

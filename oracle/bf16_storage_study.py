@@ -7,11 +7,14 @@ TEST INFRASTRUCTURE ONLY: it imports only ``oracle`` and ``synth``.
         exact fp64 forward + backward (no storage point rounded; identical to
         oracle.gpt_forward/gpt_backward); saves the logits and every gradient
         to DIR as fp32 .npy (about 11 GB at the full size)
-    python -m oracle.bf16_storage_study emu  DIR  POINTS  [--delta o|p] [--ds-center]
+    python -m oracle.bf16_storage_study emu  DIR  POINTS  [--delta o|o32|p] [--ds-center]
+                                       [--p-fwd-form normalised|unnormalised] [--json OUT]
         the same model with the comma-separated storage points rounded to
         bf16 (``all`` = every point, ``all-X-Y`` = every point except X and
         Y); prints max|err|/max|ref| of the logits, the table gradient and
-        every parameter gradient of every layer against DIR's reference
+        every parameter gradient of every layer against DIR's reference, and
+        with ``--json`` also writes them, with the options and the command,
+        to OUT
 
 The inputs are the stacked-model workload's seeded draws (``synth.gpt_inputs``
 with workload seed 5: 12 layers, H = 4096, 8 heads of 512, MLP 16384, V =
@@ -96,8 +99,10 @@ def main(argv=None):
     ap.add_argument("mode", choices=["ref", "emu"])
     ap.add_argument("dir")
     ap.add_argument("points", nargs="?", default="none")
-    ap.add_argument("--delta", default="o", choices=["o", "p"])
+    ap.add_argument("--delta", default="o", choices=["o", "o32", "p"])
     ap.add_argument("--ds-center", action="store_true")
+    ap.add_argument("--p-fwd-form", default="normalised", choices=["normalised", "unnormalised"])
+    ap.add_argument("--json", default=None)
     ap.add_argument("--small", action="store_true")
     a = ap.parse_args(argv)
     c = SMALL if a.small else FULL
@@ -108,7 +113,7 @@ def main(argv=None):
         run(c, B.Rounding(), sink)
         return
     pts = parse_points(a.points)
-    rnd = B.Rounding(pts, delta=a.delta, ds_center=a.ds_center)
+    rnd = B.Rounding(pts, delta=a.delta, ds_center=a.ds_center, p_fwd_form=a.p_fwd_form)
     errs = {}
 
     def sink(name, arr):
@@ -117,17 +122,32 @@ def main(argv=None):
         errs[name] = float(np.max(np.abs(np.asarray(arr, dtype=np.float64) - ref)) / (den if den > 0 else 1.0))
         print(f"  {name} {errs[name]:.3e}", flush=True)
 
-    print(f"points={sorted(pts)} delta={a.delta} ds_center={a.ds_center}", flush=True)
+    print(f"points={sorted(pts)} delta={a.delta} ds_center={a.ds_center} p_fwd_form={a.p_fwd_form}", flush=True)
     run(c, rnd, sink)
     grads = {k: v for k, v in errs.items() if not k.startswith("logits")}
     worst = max(grads, key=grads.get)
     over = sorted(k for k, v in grads.items() if v > 1e-2)
-    summary = {"points": sorted(pts), "delta": a.delta, "ds_center": a.ds_center,
+    summary = {"points": sorted(pts), "delta": a.delta, "ds_center": a.ds_center, "p_fwd_form": a.p_fwd_form,
                "worst": [worst, grads[worst]], "over_1e-2": len(over),
                "mean": float(np.mean(list(grads.values()))),
                "logits": max(v for k, v in errs.items() if k.startswith("logits")), "errors": errs}
     print("SUMMARY " + json.dumps({k: v for k, v in summary.items() if k != "errors"}), flush=True)
     print("OVER " + " ".join(f"{k}={grads[k]:.2e}" for k in over), flush=True)
+    if a.json:
+        args = list(argv if argv is not None else sys.argv[1:])
+        args[args.index(a.dir)] = "DIR"
+        small = " --small" if a.small else ""
+        cmd = (f"python -m oracle.bf16_storage_study ref DIR{small} && "
+               "python -m oracle.bf16_storage_study " + " ".join(args))
+        with open(a.json, "w") as f:
+            what = ("max|err|/max|ref| of the logits and of every gradient of the stacked model (page "
+                    "'5-megatron', section 训练一般流程: two LayerNorms per layer, tied embedding; split as on "
+                    "page 'Megtron张量/模型并行', sections MLP层 / Self-Attention层) computed by "
+                    "oracle.bf16_storage with the listed storage points rounded to bf16, against the same "
+                    "model in fp64 (oracle.gpt_forward / gpt_backward)")
+            json.dump(dict(summary, model="small" if a.small else "full", command=cmd, what=what), f, indent=1,
+                      sort_keys=True, ensure_ascii=False)
+            f.write("\n")
 
 
 if __name__ == "__main__":

@@ -100,6 +100,46 @@ def test_delta_from_p_equals_delta_from_o_without_rounding(case):
         assert rel(got[k], ref[k]) < 1e-10, k
 
 
+def test_new_forms_equal_the_oracle_without_rounding(case):
+    # the fp32-copy row term and the end-normalised forward compute the
+    # oracle's values when nothing is rounded (only the order of operations
+    # differs)
+    ids, E, lay, dL, ref = case
+    for rnd in (B.Rounding(delta="o32"), B.Rounding(p_fwd_form="unnormalised"),
+                B.Rounding(delta="o32", p_fwd_form="unnormalised")):
+        got = flat(*run_emu(ids, E, lay, dL, rnd))
+        for k in ref:
+            assert rel(got[k], ref[k]) < 1e-10, (rnd.delta, rnd.p_fwd_form, k)
+
+
+def test_o32_row_term_reads_the_unrounded_output(case):
+    # with O rounded, "o" forms the row term from the rounded O and "o32" from
+    # the unrounded one: the forward is the same, dW_QKV (which reads O only
+    # through the row term) differs, dW_O (which reads the stored O) does not
+    ids, E, lay, dL, ref = case
+    a = flat(*run_emu(ids, E, lay, dL, B.Rounding(["o"], delta="o")))
+    b = flat(*run_emu(ids, E, lay, dL, B.Rounding(["o"], delta="o32")))
+    assert all(np.array_equal(a[k], b[k]) for k in a if k.startswith("logits"))
+    top = max(int(k[1:].split(".")[0]) for k in a if k.startswith("L"))
+    assert not np.array_equal(a[f"L{top}.WQ"], b[f"L{top}.WQ"])
+    # dW_O reads the stored O directly: the same in both
+    assert np.array_equal(a[f"L{top}.WO"], b[f"L{top}.WO"])
+
+
+def test_unnormalised_form_rounds_other_values():
+    g = np.random.default_rng(11)
+    s, d = 40, 16
+    Q, K, V = (g.standard_normal((s, d)) for _ in range(3))
+    O0, l0 = O.attention_head_forward(Q, K, V)
+    a, la = B.head_forward(Q, K, V, B.Rounding(["p_fwd"]))
+    b, lb = B.head_forward(Q, K, V, B.Rounding(["p_fwd"], p_fwd_form="unnormalised"))
+    assert np.array_equal(la, lb) and rel(la, l0) < 1e-14
+    assert not np.array_equal(a, b)
+    # both are one bf16 rounding of the probabilities away from the exact O
+    for got in (a, b):
+        assert 1e-6 < rel(got, O0) < 2 ** -7
+
+
 def test_head_backward_centred_keys_exact():
     g = np.random.default_rng(3)
     s, d = 12, 8
@@ -134,3 +174,7 @@ def test_rounding_equals_the_oracles_on_fp32_values():
 def test_unknown_point_rejected():
     with pytest.raises(ValueError):
         B.Rounding(["no_such_point"])
+    with pytest.raises(ValueError):
+        B.Rounding(delta="q")
+    with pytest.raises(ValueError):
+        B.Rounding(p_fwd_form="other")
