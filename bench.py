@@ -539,6 +539,62 @@ def cpu_model():
     return "unknown"
 
 
+ATTN_CORE_SHAPES = [(1, 2048, 8, 128), (1, 2048, 4, 256), (2, 2048, 16, 64), (1, 8192, 2, 128), (1, 2048, 4, 512)]
+
+
+def attn_core_sweep(tp, torch, reps=5):
+    """Per-kernel times (library tracer, mean over `reps` calls after one
+    untimed call) of one attention shard's forward and backward at
+    ATTN_CORE_SHAPES (batch, sequence, heads of the shard, head dim; causal),
+    and the attention-core rates: the forward counted as 4 d FLOP per causal
+    (query, key) pair and head, the backward as twice that."""
+    rows = []
+    for b, sq, hs, d in ATTN_CORE_SHAPES:
+        h = max(512, hs * d)
+        M, w = b * sq, hs * d
+        g = torch.Generator(device="cuda").manual_seed(1)
+        X = torch.randn((M, h), device="cuda", generator=g).to(torch.bfloat16)
+        Wqkv = (0.02 * torch.randn((h, 3 * w), device="cuda", generator=g)).to(torch.bfloat16)
+        Wo = (0.02 * torch.randn((w, h), device="cuda", generator=g)).to(torch.bfloat16)
+        dZ = torch.randn((M, h), device="cuda", generator=g).to(torch.bfloat16)
+        QKV = torch.empty((M, 3 * w), device="cuda", dtype=torch.bfloat16)
+        O = torch.empty((M, w), device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty((b * hs * sq,), device="cuda", dtype=torch.float32)
+        Z = torch.empty((M, h), device="cuda", dtype=torch.bfloat16)
+        gX, gW, gWo = torch.empty_like(X), torch.empty_like(Wqkv), torch.empty_like(Wo)
+        wsf = torch.empty((tp.tp_attn_fwd_workspace(torch.bfloat16, b, sq, h, hs, d),), device="cuda",
+                          dtype=torch.uint8)
+        wsb = torch.empty((tp.tp_attn_bwd_workspace(torch.bfloat16, b, sq, h, hs, d),), device="cuda",
+                          dtype=torch.uint8)
+        for it in range(reps + 1):
+            if it == 1:
+                tp.trace_clear()
+                tp.trace_start("", 1 << 16)
+            tp.tp_attn_fwd(X, Wqkv, Wo, QKV, O, lse, Z, b, sq, hs, d, True, ws=wsf)
+            tp.tp_attn_bwd(X, Wqkv, Wo, QKV, O, lse, dZ, gX, gW, gWo, wsb, b, sq, hs, d, True)
+        torch.cuda.synchronize()
+        tp.trace_stop()
+        per = {}
+        for name, ms in tp.trace_records():
+            per[name] = per.get(name, 0.0) + ms * 1e3 / reps
+        tp.trace_clear()
+        # the attention core: everything but the four projection GEMMs
+        # (QKV and O products, and their weight and input gradients: z1)
+        core = {"fwd": 0.0, "bwd": 0.0}
+        for name, us in per.items():
+            if "gemm_bf16_kernel" in name and name.endswith(" z1"):
+                continue
+            core["fwd" if name.startswith("tp_attn_fwd") else "bwd"] += us
+        fl = 4 * d * b * hs * sq * (sq + 1) // 2
+        rows.append({"shape": {"b": b, "s": sq, "heads": hs, "d": d},
+                     "workspace_mib": {"fwd": round(wsf.numel() / 2**20, 1), "bwd": round(wsb.numel() / 2**20, 1)},
+                     "kernels_us": {k: round(v, 2) for k, v in per.items()},
+                     "core_fwd_us": round(core["fwd"], 1), "core_fwd_tflops": round(fl / core["fwd"] / 1e6, 1),
+                     "core_bwd_us": round(core["bwd"], 1), "core_bwd_tflops": round(2 * fl / core["bwd"] / 1e6, 1)})
+        del X, Wqkv, Wo, dZ, QKV, O, lse, Z, gX, gW, gWo, wsf, wsb
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,6 +608,8 @@ def main():
     ap.add_argument("--no-sp", action="store_true", help="skip the sequence-parallel exchange rates")
     ap.add_argument("--no-full-embed", action="store_true", help="skip the full-embedding and dropout rates")
     ap.add_argument("--calib", action="store_true", help="one 512 MiB copy first (counter calibration)")
+    ap.add_argument("--attn-cores", action="store_true",
+                    help="only time the attention cores at a few shapes (one JSON line per shape, no metric)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs every tensor-parallel shard on ONE GPU "
@@ -563,6 +621,10 @@ def main():
     import megatron_tensor_transformer_columnparallel_amd as tp
 
     torch.cuda.set_device(0)
+    if args.attn_cores:
+        for row in attn_core_sweep(tp, torch):
+            print(json.dumps(row), flush=True)
+        return
     c, model, ids, dl = gpt_model(tp, torch)
     flops = c.flops()
 

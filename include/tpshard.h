@@ -127,9 +127,13 @@ tps_status tp_mlp_bwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i,
  *                           of exp(S), i.e. P = exp(S - lse) row by row
  *   Z_i    [b*sq x h]     output: this shard's partial
  *   ws     caller scratch of at least tp_attn_fwd_workspace(...) bytes
- *          (16-byte aligned); holds the scores and probabilities of every
- *          (batch, head), b*hs*sq*round_up(sq, 8)*6 bytes, and is free again
- *          when the stream has passed the call.
+ *          (16-byte aligned), free again when the stream has passed the
+ *          call.  Head dims 64, 128, 256 (and 512 past 4096 positions) take
+ *          the flash kernel: fp32 partial outputs of split query blocks,
+ *          about one 128 x d block per compute unit (O(sq d), covering the
+ *          causal and the non-causal plan).  Other head dims keep the scores
+ *          and probabilities of every (batch, head), b*hs*sq*round_up(sq, 8)*6
+ *          bytes.
  * Supported: dt = TPS_BF16, d a multiple of 8; TPS_EUNSUPPORTED for fp32.
  * TPS_EWORKSPACE if ws_bytes is too small (nothing is enqueued).
  * ------------------------------------------------------------------------ */
@@ -145,7 +149,18 @@ size_t tp_attn_bwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int
  * tp_attn_bwd: dWo_i = O_i^T dZ; dO = dZ Wo_i^T; per head dQ, dK, dV of the
  * softmax attention; dWqkv_i = X^T dQKV; dX_i = dQKV Wqkv_i^T (partial).
  * dZ [b*sq x h] is the full upstream gradient.  Outputs dX_i [b*sq x h],
- * dWqkv_i [h x 3*hs*d], dWo_i [hs*d x h].
+ * dWqkv_i [h x 3*hs*d], dWo_i [hs*d x h].  The probabilities are recomputed
+ * from QKV_i and lse_i; each row's softmax term sum_j P dP is taken from the
+ * same P and dP that form dS (page "Megtron张量/模型并行", section
+ * Self-Attention层, for the per-head computation).
+ * ws: caller scratch of at least tp_attn_bwd_workspace(...) bytes (16-byte
+ * aligned; the query covers both masks).  Head dims 64, 128, 256 take the
+ * flash kernels: dO, dQKV (bf16), one fp32 row term per query and head and
+ * fp32 partials of split blocks for about one work item per compute unit,
+ * O(sq d).  Other head dims store P (bf16), dP (fp32) and dS (bf16) per
+ * (query, key) and head, O(sq^2).
+ * TPS_EWORKSPACE if ws_bytes is below this call's need (nothing is enqueued);
+ * TPS_EINVAL for 3*hs*d > 2^25 on the flash path.
  */
 tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d,
                        int causal, const void* X, const void* Wqkv_i, const void* Wo_i,

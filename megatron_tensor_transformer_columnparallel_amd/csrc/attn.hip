@@ -21,6 +21,7 @@
 #include <string>
 
 #include "flash_attn.hpp"
+#include "flash_bwd.hpp"
 #include "gemm.hpp"
 
 namespace tps {
@@ -310,6 +311,30 @@ static AttnWs attn_ws_layout(int64_t b, int64_t sq, int64_t hs, int64_t d) {
   return w;
 }
 
+// Flash backward workspace: dO and dQKV (bf16, row-major like O and QKV),
+// Delta (fp32, [b][hs][sq]), the per-item row sums of the Delta phase
+// (fp32 pairs), and the fp32 partials of split blocks: dQ ([item][128][d])
+// and dK, dV ([item][rows][2 d]).  The item counts come from the work plans,
+// about one item per CU, so the partials are bounded by the CU count times a
+// block, not by the sequence length.
+struct AttnFlashBwdWs {
+  size_t dO, dQKV, delta, rd, qpart, kvpart, total;
+};
+static AttnFlashBwdWs attn_flash_bwd_ws_layout(int64_t b, int64_t sq, int64_t hs, int64_t d,
+                                               const flash::BwdWork& wq, const flash::BwdWork& wk) {
+  AttnFlashBwdWs w;
+  const size_t M = (size_t)(b * sq);
+  const size_t iq = (size_t)flash::work_total(wq), ik = (size_t)flash::work_total(wk);
+  w.dO = 0;
+  w.dQKV = align256(w.dO + M * hs * d * 2);
+  w.delta = align256(w.dQKV + M * 3 * hs * d * 2);
+  w.rd = align256(w.delta + (size_t)b * hs * sq * 4);
+  w.qpart = align256(w.rd + iq * wq.bb * 2 * 4);
+  w.kvpart = align256(w.qpart + iq * wq.bb * d * 4);
+  w.total = align256(w.kvpart + ik * wk.bb * 2 * d * 4);
+  return w;
+}
+
 // Forward workspace: the log2-domain scores S2 (fp32) and the probabilities
 // P (bf16), both [b][hs][sq][ldp].
 struct AttnFwdWs {
@@ -364,6 +389,11 @@ static bool use_flash(int64_t d, int64_t sq) {
   if (d == 64 || d == 128 || d == 256) return true;
   return d == 512 && sq > 4096;
 }
+
+// Which backward core: the flash kernels are compiled for head dims 64..256
+// (at 512 a wave cannot hold the fragments and both accumulators of 32 keys;
+// the score / dS GEMM path keeps O(sq^2) workspace there).
+static bool use_flash_bwd(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
 // Compute units of the current device (the flash forward sizes its work
 // items so that one round of them fills the chip).
@@ -481,11 +511,86 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
                                 st);
 }
 
+// The two work plans of a flash backward call (query blocks over keys for
+// the Delta and dQ phases, key blocks over queries for the dK/dV phase).
+template <int D>
+static void flash_bwd_works(int64_t b, int64_t sq, int64_t hs, int causal, int cus, flash::BwdWork& wq,
+                            flash::BwdWork& wk) {
+  wq = flash::make_bwd_work(b, sq, hs, flash::BwdShape<D, false>::BB, causal, 0, cus);
+  wk = flash::make_bwd_work(b, sq, hs, flash::BwdShape<D, true>::BB, causal, 1, cus);
+}
+static void flash_bwd_works_d(int64_t d, int64_t b, int64_t sq, int64_t hs, int causal, int cus, flash::BwdWork& wq,
+                              flash::BwdWork& wk) {
+  if (d == 64) flash_bwd_works<64>(b, sq, hs, causal, cus, wq, wk);
+  else if (d == 128) flash_bwd_works<128>(b, sq, hs, causal, cus, wq, wk);
+  else flash_bwd_works<256>(b, sq, hs, causal, cus, wq, wk);
+}
+
 extern "C" size_t tp_attn_bwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d) {
   (void)dt;
   (void)h;
   if (b <= 0 || sq <= 0 || hs <= 0 || d <= 0) return 0;
+  if (use_flash_bwd(d)) {
+    // the query has no causal argument: cover both plans
+    const int cus = device_cus();
+    size_t need = 0;
+    for (int causal = 0; causal < 2; ++causal) {
+      flash::BwdWork wq, wk;
+      flash_bwd_works_d(d, b, sq, hs, causal, cus, wq, wk);
+      need = std::max(need, attn_flash_bwd_ws_layout(b, sq, hs, d, wq, wk).total);
+    }
+    return need;
+  }
   return attn_ws_layout(b, sq, hs, d).total;
+}
+
+// Flash backward core: Delta partials, then dQ (and Delta), then dK and dV,
+// then the merges of split blocks (see flash_bwd.hpp).
+template <int D>
+static tps_status flash_bwd_core(const bf16_t* qkv, const bf16_t* dO, const float* lse, bf16_t* dqkv, char* ws,
+                                 const AttnFlashBwdWs& L, const flash::BwdPlan& p, const flash::BwdWork& wq,
+                                 const flash::BwdWork& wk, hipStream_t st) {
+  using SQ = flash::BwdShape<D, false>;
+  using SK = flash::BwdShape<D, true>;
+  float* delta = (float*)(ws + L.delta);
+  float* rd = (float*)(ws + L.rd);
+  float* qpart = (float*)(ws + L.qpart);
+  float* kvpart = (float*)(ws + L.kvpart);
+  const unsigned nq = (unsigned)flash::work_total(wq), nk = (unsigned)flash::work_total(wk);
+  {
+    TraceScope trace_(st, "attn_bwd_delta_kernel");
+    hipLaunchKernelGGL((flash::attn_bwd_q_kernel<D, 0>), dim3(nq), dim3(SQ::THREADS), 0, st, qkv, dO, lse, dqkv,
+                       delta, rd, qpart, p, wq);
+    TPS_TRY(check_launch("attn_bwd_delta_kernel"));
+  }
+  {
+    TraceScope trace_(st, "attn_bwd_dq_kernel");
+    hipLaunchKernelGGL((flash::attn_bwd_q_kernel<D, 1>), dim3(nq), dim3(SQ::THREADS), 0, st, qkv, dO, lse, dqkv,
+                       delta, rd, qpart, p, wq);
+    TPS_TRY(check_launch("attn_bwd_dq_kernel"));
+  }
+  {
+    TraceScope trace_(st, "attn_bwd_dkv_kernel");
+    hipLaunchKernelGGL((flash::attn_bwd_kv_kernel<D>), dim3(nk), dim3(SK::THREADS), 0, st, qkv, dO, lse, delta, dqkv,
+                       kvpart, p, wk);
+    TPS_TRY(check_launch("attn_bwd_dkv_kernel"));
+  }
+  const int mq = flash::work_merges_per_z(wq), mk = flash::work_merges_per_z(wk);
+  if (mq > 0) {
+    TraceScope trace_(st, "attn_bwd_merge_kernel");
+    constexpr int rows = flash::kMergeThreads / (D / 4) >= 1 ? flash::kMergeThreads / (D / 4) : 1;
+    hipLaunchKernelGGL((flash::attn_bwd_merge_kernel<D, false>), dim3((unsigned)(mq * wq.nz * (wq.bb / rows))),
+                       dim3(flash::kMergeThreads), 0, st, qpart, dqkv, p, wq, mq);
+    TPS_TRY(check_launch("attn_bwd_merge_kernel"));
+  }
+  if (mk > 0) {
+    TraceScope trace_(st, "attn_bwd_merge_kernel");
+    constexpr int rows = flash::kMergeThreads / (D / 2) >= 1 ? flash::kMergeThreads / (D / 2) : 1;
+    hipLaunchKernelGGL((flash::attn_bwd_merge_kernel<D, true>), dim3((unsigned)(mk * wk.nz * (wk.bb / rows))),
+                       dim3(flash::kMergeThreads), 0, st, kvpart, dqkv, p, wk, mk);
+    TPS_TRY(check_launch("attn_bwd_merge_kernel"));
+  }
+  return TPS_OK;
 }
 
 extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d, int causal,
@@ -495,6 +600,37 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   ApiScope api_scope_("tp_attn_bwd");
   TPS_TRY(attn_checks("tp_attn_bwd", dt, b, sq, h, hs, d,
                       {X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dZ, dX_i, dWqkv_i, dWo_i, ws}));
+  if (use_flash_bwd(d)) {
+    const char* fn = "tp_attn_bwd";
+    // the kernels' per-lane tile offsets (32 rows of QKV) are 32-bit
+    TPS_REQ(3 * hs * d <= (1LL << 25), "3 hs d must be <= 2^25");
+    flash::BwdWork wq, wk;
+    flash_bwd_works_d(d, b, sq, hs, causal ? 1 : 0, device_cus(), wq, wk);
+    const AttnFlashBwdWs L = attn_flash_bwd_ws_layout(b, sq, hs, d, wq, wk);
+    if (ws_bytes < L.total) return set_error(TPS_EWORKSPACE, "tp_attn_bwd: workspace too small");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t M = b * sq, w = hs * d, w3 = 3 * w;
+    char* base = static_cast<char*>(ws);
+    bf16_t* dO = (bf16_t*)(base + L.dO);
+    bf16_t* dQKV = (bf16_t*)(base + L.dQKV);
+    const bf16_t* qkv = (const bf16_t*)QKV_i;
+    const bf16_t* dz = (const bf16_t*)dZ;
+    // dWo_i = O_i^T dZ                     (TN)  [w x h], K = M
+    TPS_TRY((gemm_bf16<false, false>((const bf16_t*)O_i, dz, shape(w, h, M, w, h),
+                                     EpiStore<bf16_t>{(bf16_t*)dWo_i, h, 0, 0}, st)));
+    // dO = dZ Wo_i^T                       (NT)  [M x w], K = h
+    TPS_TRY((gemm_bf16<true, true>(dz, (const bf16_t*)Wo_i, shape(M, w, h, h, h), EpiStore<bf16_t>{dO, w, 0, 0}, st)));
+    const flash::BwdPlan p = flash::make_bwd_plan(b, sq, hs, (int)d, causal ? 1 : 0);
+    if (d == 64) TPS_TRY(flash_bwd_core<64>(qkv, dO, lse_i, dQKV, base, L, p, wq, wk, st));
+    else if (d == 128) TPS_TRY(flash_bwd_core<128>(qkv, dO, lse_i, dQKV, base, L, p, wq, wk, st));
+    else TPS_TRY(flash_bwd_core<256>(qkv, dO, lse_i, dQKV, base, L, p, wq, wk, st));
+    // dWqkv_i = X^T dQKV                   (TN)  [h x 3w], K = M
+    TPS_TRY((gemm_bf16<false, false>((const bf16_t*)X, dQKV, shape(h, w3, M, h, w3),
+                                     EpiStore<bf16_t>{(bf16_t*)dWqkv_i, w3, 0, 0}, st)));
+    // dX_i = dQKV Wqkv_i^T                 (NT)  [M x h], K = 3w
+    return gemm_bf16<true, true>(dQKV, (const bf16_t*)Wqkv_i, shape(M, h, w3, w3, w3),
+                                 EpiStore<bf16_t>{(bf16_t*)dX_i, h, 0, 0}, st);
+  }
   const AttnWs L = attn_ws_layout(b, sq, hs, d);
   if (ws_bytes < L.total) return set_error(TPS_EWORKSPACE, "tp_attn_bwd: workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -143,6 +143,23 @@ def test_workspace_queries_and_too_small_workspace(tp):
     assert ws >= 2048 * 4 * 512 * 2 + 4 * 2048 * 4 + 2 * 4 * 2048 * 2048 * 2 + 2048 * 3 * 2048 * 2
     st = lib.tp_attn_bwd(1, 1, 2048, 4096, 4, 512, 1, *([ALIGNED] * 11), ws - 1, None)
     assert st == tp.binding.TPS_EWORKSPACE
+    # backward through the flash kernels (head dims 64..256): dO and dQKV
+    # (bf16), one fp32 row term per query and head, and fp32 partials of
+    # split blocks for about one work item per CU whatever the sequence
+    # length; nothing per (query, key) pair
+    for b, sq, hs, d in [(1, 8192, 2, 128), (2, 300, 3, 64), (1, 32768, 4, 256), (1, 131072, 1, 64)]:
+        wb = lib.tp_attn_bwd_workspace(1, b, sq, 4096, hs, d)
+        need = b * sq * hs * d * 2 + b * sq * 3 * hs * d * 2 + b * hs * sq * 4
+        items = 3 * max(256, b * hs * -(-sq // 64))   # rounds of CU items, at least one per block
+        assert need <= wb <= need + items * 128 * (3 * d + 2) * 4 + 8 * 256, (b, sq, hs, d, wb, need)
+        if sq >= 8192:   # against the score path's bf16 P, fp32 dP and bf16 dS per (query, key) and head
+            assert wb < b * hs * sq * sq * 8 // 10
+    # the query covers both masks' plans; a call checks its own plan's need,
+    # which always includes dO and dQKV
+    small = 300 * 2 * 64 * 2 + 300 * 3 * 2 * 64 * 2 - 1
+    for causal in (0, 1):
+        st = lib.tp_attn_bwd(1, 1, 300, 4096, 2, 64, causal, *([ALIGNED] * 11), small, None)
+        assert st == tp.binding.TPS_EWORKSPACE
     # forward through the flash kernel (head dims up to 256, and 512 past 4096
     # positions): fp32 partial outputs of the key chunks, about one 128-row
     # item per compute unit whatever the sequence length (no per-(query, key)

@@ -1,9 +1,15 @@
-"""GPU parity of the flash-style attention forward: O and the log-sum-exp
-against the fp64 oracle, at sizes where the work is split into key chunks
-(the merge path), for head dims 64, 128 and 256 and for head dim 512 past
-4096 positions (shorter sequences at 512 take the score / softmax / PV
-path, also checked here), and at a sequence of 8192 whose score matrix is
-never stored (sampled rows, checked one by one)."""
+"""GPU parity of the flash-style attention kernels.
+
+Forward: O and the log-sum-exp against the fp64 oracle, at sizes where the
+work is split into key chunks (the merge path), for head dims 64, 128 and
+256 and for head dim 512 past 4096 positions (shorter sequences at 512 take
+the score / softmax / PV path, also checked here), and at a sequence of
+8192 whose score matrix is never stored (sampled rows, checked one by one).
+
+Backward (head dims 64, 128, 256): dX, dW_QKV (its Q, K and V column blocks
+separately) and dW_O against the oracle at sizes spanning several 128-row
+blocks and 32-row tiles with ragged ends, causal and not, and at a
+sequence of 8192 against the full oracle with a workspace of O(s d)."""
 
 import numpy as np
 import pytest
@@ -99,3 +105,62 @@ def test_flash_forward_long_sequence_sampled_rows(tp):
             assert abs(l[j, i] - li[0]) <= 1e-2 * max(1.0, abs(li[0])), (j, i, l[j, i], li[0])
     print(f"  sampled O rows err {worst:.2e}", flush=True)
     assert worst <= BF16_TOL
+
+
+def _bwd_case(tp, w, b, sq, h, hs, d, causal):
+    inp = synth.attn_inputs(w, b * sq, h, hs, d, "bf16")
+    Wqkv, Wo = _weights(inp, hs, d)
+    M, wd = b * sq, hs * d
+    X, dZ = to_dev(inp["X"]), to_dev(inp["dZ"])
+    dW, dWo_ = to_dev(Wqkv), to_dev(Wo)
+    QKV, Ob = empty((M, 3 * wd), torch.bfloat16), empty((M, wd), torch.bfloat16)
+    lse, Z = empty((b * hs * sq,), torch.float32), empty((M, h), torch.bfloat16)
+    tp.tp_attn_fwd(X, dW, dWo_, QKV, Ob, lse, Z, b, sq, hs, d, causal)
+    gX, gW, gWo = empty((M, h), torch.bfloat16), empty(tuple(Wqkv.shape), torch.bfloat16), empty(tuple(Wo.shape), torch.bfloat16)
+    nws = tp.tp_attn_bwd_workspace(torch.bfloat16, b, sq, h, hs, d)
+    ws = empty((nws,), torch.uint8)
+    tp.tp_attn_bwd(X, dW, dWo_, QKV, Ob, lse, dZ, gX, gW, gWo, ws, b, sq, hs, d, causal)
+    torch.cuda.synchronize()
+    QKV_r, O_r, lse_r, Z_r = O.attention_layer_forward(inp["X"].f64, Wqkv.f64, Wo.f64, b, sq, hs, d, causal)
+    dX_r, dW_r, dWo_r = O.attention_layer_backward(inp["X"].f64, Wqkv.f64, Wo.f64, QKV_r, O_r, inp["dZ"].f64,
+                                                   b, sq, hs, d, causal)
+    got_w = to_f64(gW)
+    errs = {"dX": rel_err(to_f64(gX), dX_r), "dWo": rel_err(to_f64(gWo), dWo_r)}
+    for k, part in enumerate("QKV"):
+        c = slice(k * wd, (k + 1) * wd)
+        errs[f"dW{part}"] = rel_err(got_w[:, c], dW_r[:, c])
+    for k, e in errs.items():
+        print(f"  {k} err {e:.2e}", flush=True)
+    return errs, nws
+
+
+@pytest.mark.parametrize("w,b,sq,h,hs,d,causal", [
+    (301, 1, 1100, 256, 2, 64, True),    # many 128-query blocks and 32-key tiles, ragged end
+    (302, 2, 700, 256, 3, 128, True),    # batch 2, 3 heads
+    (303, 1, 1100, 256, 2, 256, False),  # head dim 256 (16-row waves), non-causal
+    (304, 1, 333, 256, 1, 256, True),    # 64-key blocks of the dK/dV kernel, ragged
+    (305, 3, 129, 128, 2, 128, False),   # one row past a block, batch 3
+    (306, 2, 31, 128, 2, 64, True),      # shorter than one tile
+])
+def test_flash_backward_matches_oracle(tp, w, b, sq, h, hs, d, causal):
+    say(f"flash backward b={b} sq={sq} h={h} hs={hs} d={d} causal={causal}")
+    errs, _ = _bwd_case(tp, w, b, sq, h, hs, d, causal)
+    over = [f"{k} {e:.2e}" for k, e in errs.items() if e > BF16_TOL]
+    assert not over, over
+
+
+def test_flash_backward_long_sequence(tp):
+    """sq = 8192, two heads of 128, causal: every output of the backward
+    against the full fp64 oracle; the workspace is dO, dQKV, one fp32 row
+    term per query and head and the fp32 partials of about one work item per
+    CU (the score-path backward would need 1 GiB)."""
+    b, sq, h, hs, d = 1, 8192, 256, 2, 128
+    say(f"flash backward long sequence b={b} sq={sq} h={h} hs={hs} d={d}")
+    errs, nws = _bwd_case(tp, 307, b, sq, h, hs, d, True)
+    pairs = b * hs * sq * sq * (2 + 4 + 2)    # bf16 P, fp32 dP, bf16 dS per (query, key) and head
+    print(f"  workspace {nws / 2**20:.1f} MiB (per-pair storage would be {pairs / 2**20:.0f} MiB)", flush=True)
+    items = 3 * max(256, b * hs * sq // 64)
+    assert nws <= b * sq * hs * d * 8 + b * hs * sq * 4 + items * 128 * (3 * d + 2) * 4 + 2048
+    assert nws < pairs // 10
+    over = [f"{k} {e:.2e}" for k, e in errs.items() if e > BF16_TOL]
+    assert not over, over
