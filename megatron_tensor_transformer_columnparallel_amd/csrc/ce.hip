@@ -31,12 +31,9 @@ struct StatPtrs {
   const float* p[8];
 };
 
-// Chunk c (VEC elements) of a row as fp32, read at chunk min(c, nch - 1):
-// the last chunk holding a valid column, inside the row's stride (a multiple
-// of VEC).  Callers mask what lies past the row.
+// Chunk cc (VEC elements, wholly inside the row's stride) of a row as fp32.
 template <typename T>
-__device__ __forceinline__ void load_chunk(const T* row, int c, int nch, float* v) {
-  const int cc = c < nch ? c : nch - 1;
+__device__ __forceinline__ void load_whole_chunk(const T* row, int cc, float* v) {
   if constexpr (sizeof(T) == 2) {
     const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + (int64_t)cc * 8);
 #pragma unroll
@@ -46,6 +43,14 @@ __device__ __forceinline__ void load_chunk(const T* row, int c, int nch, float* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = w[i];
   }
+}
+
+// Chunk c of a row, read at chunk min(c, nch - 1): the last chunk holding a
+// valid column, inside the row's stride (a multiple of VEC).  Callers mask
+// what lies past the row.
+template <typename T>
+__device__ __forceinline__ void load_chunk(const T* row, int c, int nch, float* v) {
+  load_whole_chunk<T>(row, c < nch ? c : nch - 1, v);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -88,7 +93,34 @@ __global__ void __launch_bounds__(256) ce_stats_kernel(const T* __restrict__ L, 
   const bool own = tl >= 0 && tl < v_rows;
   const float xt = Elem<T>::to_f32(row[tl < 0 ? 0 : (tl < v_rows ? tl : v_rows - 1)]);
   float m = -INFINITY, s = 0.f;
-  for (int c0 = lane; c0 < nch; c0 += 64 * kGroup) {
+  // one group: kGroup chunks per lane (c0, c0 + 64, ...), their maximum,
+  // then the sum rescaled to it
+  auto group = [&](float (&v)[kGroup][VEC]) {
+    float gm = m;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) gm = fmaxf(gm, v[g][e]);
+    // m == -inf only before a lane's first valid column: nothing to rescale then
+    float acc = m == -INFINITY ? 0.f : s * exp_shifted(m, gm);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += exp_shifted(v[g][e], gm);
+    m = gm;
+    s = acc;
+  };
+  // groups whose chunks lie wholly inside the row for every lane (the
+  // same for the whole wave): no clamping, no masking
+  const int full = v_rows / VEC / (64 * kGroup);
+  int c0 = lane;
+  for (int gi = 0; gi < full; ++gi, c0 += 64 * kGroup) {
+    float v[kGroup][VEC];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) load_whole_chunk<T>(row, c0 + g * 64, v[g]);
+    group(v);
+  }
+  for (; c0 < nch; c0 += 64 * kGroup) {
     float v[kGroup][VEC];
     // every load of the group first: a branch between two loads makes the
     // second wait for the first
@@ -103,19 +135,7 @@ __global__ void __launch_bounds__(256) ce_stats_kernel(const T* __restrict__ L, 
           if (c * VEC + e >= v_rows) v[g][e] = -INFINITY;
       }
     }
-    float gm = m;
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) gm = fmaxf(gm, v[g][e]);
-    // m == -inf only before a lane's first valid column: nothing to rescale then
-    float acc = m == -INFINITY ? 0.f : s * exp_shifted(m, gm);
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc += exp_shifted(v[g][e], gm);
-    m = gm;
-    s = acc;
+    group(v);
   }
   const float mw = wave_max(m);
   const float sw = wave_sum(m == -INFINITY ? 0.f : s * exp_shifted(m, mw));
@@ -166,13 +186,44 @@ __global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, in
   const int lane = threadIdx.x;
   const int nch = (v_rows + VEC - 1) / VEC;
   // one workgroup per row at a time: its 256 lanes stream the row contiguously
+  const int full = v_rows / VEC / (256 * kGroup);   // groups wholly inside the row
   for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
     const T* row = L + t * ldl;
     T* drow = dL + t * ldl;
     const int64_t tl64 = (int64_t)targets[t] - v_start;
     const int tl = (tl64 >= 0 && tl64 < v_rows) ? (int)tl64 : -VEC;   // owned column, or none
     const float l = lse[t], g = dloss[t];
-    for (int c0 = lane; c0 < nch; c0 += 256 * kGroup) {
+    // whole groups: exp only.  An owned target that falls here is rewritten
+    // afterwards by the lane that stores its chunk (chunk c belongs to lane
+    // c mod 256), which reads the target's logit before any of its stores
+    // (dL may be L; no other lane writes that chunk).
+    const bool fix = tl >= 0 && tl < full * 256 * kGroup * VEC && lane == (tl / VEC) % 256;
+    const float xt = Elem<T>::to_f32(row[tl >= 0 ? tl : 0]);
+    int c0 = lane;
+    for (int gi = 0; gi < full; ++gi, c0 += 256 * kGroup) {
+      float v[kGroup][VEC];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) load_whole_chunk<T>(row, c0 + k * 256, v[k]);
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        const int c = c0 + k * 256;
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = g * exp_shifted(v[k][e], l);
+        if constexpr (sizeof(T) == 2) {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+          u32x4_t w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{o[2 * i], o[2 * i + 1]}, b2));
+          *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(drow) + (int64_t)c * 8) = w;
+        } else {
+          store4<float>(reinterpret_cast<float*>(drow) + (int64_t)c * 4, o, VEC);
+        }
+      }
+    }
+    for (; c0 < nch; c0 += 256 * kGroup) {
       float v[kGroup][VEC];
 #pragma unroll
       for (int k = 0; k < kGroup; ++k) load_chunk<T>(row, c0 + k * 256, nch, v[k]);
@@ -204,6 +255,18 @@ __global__ void __launch_bounds__(256) ce_bwd_kernel(const T* L, int64_t ldl, in
           store4<float>(reinterpret_cast<float*>(drow) + (int64_t)c * 4, o,
                         v_rows - c * VEC < VEC ? v_rows - c * VEC : VEC);
         }
+      }
+    }
+    if (fix) {   // after this lane's own store of the chunk (same address, program order)
+      float o = g * exp_shifted(xt, l);
+      o -= g;
+      if constexpr (sizeof(T) == 2) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{o, 0.f}, b2));
+        reinterpret_cast<bf16_t*>(drow)[tl] = (bf16_t)(w & 0xffffu);
+      } else {
+        reinterpret_cast<float*>(drow)[tl] = o;
       }
     }
   }
