@@ -406,6 +406,34 @@ static int device_cus() {
   return n;
 }
 
+// Workgroups of a kernel that one CU holds at once (registers and LDS), as
+// the runtime reports it; 1 when it cannot tell.  Cached per kernel.
+template <class K>
+static int blocks_per_cu(K kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  return n;
+}
+
+// Work items one round of the flash forward runs at once: CUs times the
+// kernel's workgroups per CU, so that a wave of one item can run its
+// softmax while another's MFMAs run on the same SIMD.
+template <int D>
+static int fwd_slots() {
+  constexpr int QB = D >= 512 ? 1 : 2;
+  static const int per_cu = blocks_per_cu(flash::attn_fwd_flash_kernel<D, QB>, flash::Shape<D, QB>::THREADS);
+  return device_cus() * per_cu;
+}
+static int fwd_slots_d(int64_t d) {
+  if (d == 64) return fwd_slots<64>();
+  if (d == 128) return fwd_slots<128>();
+  if (d == 256) return fwd_slots<256>();
+  return fwd_slots<512>();
+}
+
 extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d) {
   (void)dt;
   (void)h;
@@ -413,9 +441,9 @@ extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int
   if (use_flash(d, sq)) {
     // the query has no causal argument: cover the larger of the two plans
     // (without the mask every block has all keys, so more chunks)
-    const int cus = device_cus();
-    return std::max(flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 1, cus), (int)d),
-                    flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 0, cus), (int)d));
+    const int slots = fwd_slots_d(d);
+    return std::max(flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 1, slots), (int)d),
+                    flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 0, slots), (int)d));
   }
   return attn_fwd_ws_layout(b, sq, hs).total;
 }
@@ -460,7 +488,7 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
     // QKV_i = X Wqkv_i                       (NN)
     TPS_TRY((gemm_bf16<true, false>((const bf16_t*)X, (const bf16_t*)Wqkv_i, shape(M, w3, h, h, w3),
                                     EpiStore<bf16_t>{qkv, w3, 0, 0}, st)));
-    const flash::Plan p = flash::make_plan(b, sq, hs, (int)d, causal ? 1 : 0, device_cus());
+    const flash::Plan p = flash::make_plan(b, sq, hs, (int)d, causal ? 1 : 0, fwd_slots_d(d));
     if (ws_bytes < flash::plan_workspace(p, (int)d))
       return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
     if (d == 64) TPS_TRY(flash_fwd_core<64>(qkv, o, lse_i, ws, p, st));
@@ -513,17 +541,23 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
 
 // The two work plans of a flash backward call (query blocks over keys for
 // the Delta and dQ phases, key blocks over queries for the dK/dV phase).
+// (one round of items per phase: CUs times the phase kernel's workgroups per
+// CU; the Delta and dQ phases share a plan sized for the dQ kernel)
 template <int D>
-static void flash_bwd_works(int64_t b, int64_t sq, int64_t hs, int causal, int cus, flash::BwdWork& wq,
-                            flash::BwdWork& wk) {
-  wq = flash::make_bwd_work(b, sq, hs, flash::BwdShape<D, false>::BB, causal, 0, cus);
-  wk = flash::make_bwd_work(b, sq, hs, flash::BwdShape<D, true>::BB, causal, 1, cus);
+static void flash_bwd_works(int64_t b, int64_t sq, int64_t hs, int causal, flash::BwdWork& wq, flash::BwdWork& wk) {
+  using SQ = flash::BwdShape<D, false>;
+  using SK = flash::BwdShape<D, true>;
+  static const int per_cu_q = blocks_per_cu(flash::attn_bwd_q_kernel<D, 1>, SQ::THREADS);
+  static const int per_cu_k = blocks_per_cu(flash::attn_bwd_kv_kernel<D>, SK::THREADS);
+  const int cus = device_cus();
+  wq = flash::make_bwd_work(b, sq, hs, SQ::BB, causal, 0, cus * per_cu_q);
+  wk = flash::make_bwd_work(b, sq, hs, SK::BB, causal, 1, cus * per_cu_k);
 }
-static void flash_bwd_works_d(int64_t d, int64_t b, int64_t sq, int64_t hs, int causal, int cus, flash::BwdWork& wq,
+static void flash_bwd_works_d(int64_t d, int64_t b, int64_t sq, int64_t hs, int causal, flash::BwdWork& wq,
                               flash::BwdWork& wk) {
-  if (d == 64) flash_bwd_works<64>(b, sq, hs, causal, cus, wq, wk);
-  else if (d == 128) flash_bwd_works<128>(b, sq, hs, causal, cus, wq, wk);
-  else flash_bwd_works<256>(b, sq, hs, causal, cus, wq, wk);
+  if (d == 64) flash_bwd_works<64>(b, sq, hs, causal, wq, wk);
+  else if (d == 128) flash_bwd_works<128>(b, sq, hs, causal, wq, wk);
+  else flash_bwd_works<256>(b, sq, hs, causal, wq, wk);
 }
 
 extern "C" size_t tp_attn_bwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d) {
@@ -532,11 +566,10 @@ extern "C" size_t tp_attn_bwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int
   if (b <= 0 || sq <= 0 || hs <= 0 || d <= 0) return 0;
   if (use_flash_bwd(d)) {
     // the query has no causal argument: cover both plans
-    const int cus = device_cus();
     size_t need = 0;
     for (int causal = 0; causal < 2; ++causal) {
       flash::BwdWork wq, wk;
-      flash_bwd_works_d(d, b, sq, hs, causal, cus, wq, wk);
+      flash_bwd_works_d(d, b, sq, hs, causal, wq, wk);
       need = std::max(need, attn_flash_bwd_ws_layout(b, sq, hs, d, wq, wk).total);
     }
     return need;
@@ -605,7 +638,7 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
     // the kernels' per-lane tile offsets (32 rows of QKV) are 32-bit
     TPS_REQ(3 * hs * d <= (1LL << 25), "3 hs d must be <= 2^25");
     flash::BwdWork wq, wk;
-    flash_bwd_works_d(d, b, sq, hs, causal ? 1 : 0, device_cus(), wq, wk);
+    flash_bwd_works_d(d, b, sq, hs, causal ? 1 : 0, wq, wk);
     const AttnFlashBwdWs L = attn_flash_bwd_ws_layout(b, sq, hs, d, wq, wk);
     if (ws_bytes < L.total) return set_error(TPS_EWORKSPACE, "tp_attn_bwd: workspace too small");
     hipStream_t st = static_cast<hipStream_t>(stream);
