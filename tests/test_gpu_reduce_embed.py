@@ -224,3 +224,27 @@ def test_embed_bwd_wide_shard_single_sort(tp):
         dE = _embed_bwd(tp, ids, dY, s, c, H)
         ref = O.vocab_embed_backward(ids, dY.f64, s, c)
         assert rel_err(to_f64(dE), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dt,H", [("bf16", 4096), ("f32", 1000)])
+def test_embed_bwd_paths_agree_bit_for_bit(tp, dt, H):
+    """Up to 16384 tokens the keys are sorted by per-bucket radix passes;
+    past that by a bitonic network.  Both give each row's tokens in
+    increasing order, so the same 16384 tokens with one more, out-of-range
+    token appended (which moves the call to the bitonic path) give the same
+    bits on top of the same existing dE."""
+    say(f"vocab_embed_bwd radix path vs bitonic path dt={dt} H={H}")
+    T, V = 16384, 50257
+    s, c = O.partition(V, 2, 0)
+    ids = synth.uniform_ids(99, 0, T, V)
+    ids[:300] = 17                       # a long segment
+    dY = synth.make(99, 1, (T + 1, H), 1.0, dt)
+    init = synth.make(99, 2, (c, H), 1.0, "f32")
+    ids2 = np.concatenate([ids, np.array([V + 5], dtype=np.int32)])
+    dY1 = synth.Tensor(np.ascontiguousarray(dY.store[:T]), dt)
+    a = _embed_bwd(tp, ids, dY1, s, c, H, init=init)
+    b = _embed_bwd(tp, ids2, dY, s, c, H, init=init)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_bits(a), raw_bits(b))
+    ref = init.f64 + O.vocab_embed_backward(ids, dY1.f64, s, c)
+    assert rel_err(to_f64(a), ref) <= 1e-5
