@@ -134,6 +134,18 @@ __host__ __device__ inline Item decode_item(const Plan& p, int item) {
   return t;
 }
 
+// 2^x by the hardware instruction (v_exp_f32, about 1 ulp; results below the
+// normal range flush to 0, which a softmax sum never feels, and 2^-inf = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 values to a bf16 pair by the hardware conversion (round to nearest
+// even, as pack_bf16x2), one instruction instead of the bit arithmetic.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
+}
+
 __device__ __forceinline__ uint64_t uniform_addr(const void* ptr) {
   const uint64_t b = (uint64_t)(uintptr_t)ptr;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
@@ -142,7 +154,7 @@ __device__ __forceinline__ uint64_t uniform_addr(const void* ptr) {
 }
 
 template <int D, int QB>
-__global__ void __launch_bounds__((Shape<D, QB>::THREADS), 1)
+__global__ void __launch_bounds__((Shape<D, QB>::THREADS), (D <= 128 ? 2 : 1))
 attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, float* __restrict__ lse,
                       float* __restrict__ part, Plan p, int total_items) {
   using S = Shape<D, QB>;
@@ -274,20 +286,34 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
       float t[QB][8];
       bool move = false;
       float mn[QB];
+      // the mask is tested only on a tile that reaches past the sequence or
+      // (causal) past the wave's first row (wave-uniform choice)
+      const bool whole = kb + kBK <= p.sq && (!p.causal || kb + kBK - 1 <= q0);
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
         const int row = q0 + 16 * b + r16;
         float mx = -INFINITY;
+        if (whole) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kb + 16 * h + 4 * g + e;
-            const bool masked = key >= p.sq || (p.causal && key > row);
-            const float v = masked ? -INFINITY : s[b][h][e] * p.scale_log2;
-            t[b][4 * h + e] = v;
-            mx = fmaxf(mx, v);
-          }
+            for (int e = 0; e < 4; ++e) {
+              const float v = s[b][h][e] * p.scale_log2;
+              t[b][4 * h + e] = v;
+              mx = fmaxf(mx, v);
+            }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = kb + 16 * h + 4 * g + e;
+              const bool masked = key >= p.sq || (p.causal && key > row);
+              const float v = masked ? -INFINITY : s[b][h][e] * p.scale_log2;
+              t[b][4 * h + e] = v;
+              mx = fmaxf(mx, v);
+            }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         mn[b] = fmaxf(m[b], mx);
@@ -313,11 +339,11 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2f(t[b][e] - sub);
+          pv[e] = fast_exp2(t[b][e] - sub);
           l[b] += pv[e];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[b][e] = pack_bf16x2(pv[2 * e], pv[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) pk[b][e] = cvt_bf16x2(pv[2 * e], pv[2 * e + 1]);
       }
       bf16x8_t pf[QB];
 #pragma unroll

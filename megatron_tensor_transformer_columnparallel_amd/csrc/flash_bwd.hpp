@@ -41,6 +41,8 @@
 // so both reads are free of bank conflicts.
 #pragma once
 
+#include <type_traits>
+
 #include "flash_attn.hpp"
 
 namespace tps {
@@ -66,6 +68,7 @@ struct BwdShape {
   static constexpr int CPR = D / 8;                       // 16-byte chunks per tile row
   static constexpr int TILE = kBT * D;                    // bf16 elements of one tile
   static constexpr int DPW = kBT * CPR / 64 / WAVES;      // 1 KB DMA instructions per wave per tile
+  static constexpr bool AGPR_ACC = DKV && D >= 128;
   static __host__ __device__ constexpr int swz(int r) {
     return CPR >= 16 ? (2 * (r & 7)) | ((r >> 3) & 1) : (2 * ((r >> 1) & 3)) | ((r >> 3) & 1);
   }
@@ -81,6 +84,7 @@ struct BwdPlan {
   int64_t ldo = 0;   // dO row stride (hs d)
   float scale = 0.f;        // 1 / sqrt(d)
   float scale_log2 = 0.f;   // log2(e) / sqrt(d)
+  float neg_sqrt_d = 0.f;   // -sqrt(d)
 };
 
 inline BwdPlan make_bwd_plan(int64_t b, int64_t sq, int64_t hs, int d, int causal) {
@@ -93,6 +97,7 @@ inline BwdPlan make_bwd_plan(int64_t b, int64_t sq, int64_t hs, int d, int causa
   p.ldo = hs * d;
   p.scale = 1.f / sqrtf((float)d);
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
+  p.neg_sqrt_d = -sqrtf((float)d);
   return p;
 }
 
@@ -101,6 +106,16 @@ inline BwdPlan make_bwd_plan(int64_t b, int64_t sq, int64_t hs, int d, int causa
 // of this wave fills slots (wave DPW + i) 64 .. +63; slot q is row q / CPR,
 // position q % CPR, which holds the row's logical chunk position ^ swz.
 // Rows past `rmax` re-read row rmax (their results are masked or dropped).
+// DMA of the fp32 values of queries r0 .. r0+31 (lanes 32..63 repeat them)
+// into 256 bytes of LDS at byte address m0: lane l's dword lands at m0 + 4 l.
+// Queries past `rmax` re-read rmax.
+__device__ __forceinline__ void bwd_dma_rowvals(const float* v, int r0, int rmax, uint32_t m0, int lane) {
+  const uint64_t sb = uniform_addr(v);
+  const uint32_t voff = (uint32_t)min(r0 + (lane & 31), rmax) * 4u;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sb), "s"(m0) : "memory", "m0");
+}
+
 template <class S>
 __device__ __forceinline__ void bwd_dma_tile(const bf16_t* head, int64_t ld, int r0, int rmax, uint32_t lds0,
                                              uint32_t off, int wave, int lane) {
@@ -142,8 +157,8 @@ __device__ __forceinline__ bf16x8_t bwd_tr_frag(const bf16_t* tile, int nb, int 
 }
 
 __device__ __forceinline__ bf16x8_t pack_frag(const float v[8]) {
-  return __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]),
+                                              cvt_bf16x2(v[4], v[5]), cvt_bf16x2(v[6], v[7])});
 }
 
 // ---------------------------------------------------------------- work items
@@ -245,7 +260,7 @@ inline int work_merges_per_z(const BwdWork& w) {
 // as an fp32 partial (part[item][row][D]) for the merge; the block's first
 // chunk also writes Delta for the dK/dV phase.
 template <int D, int PHASE>
-__global__ void __launch_bounds__((BwdShape<D, false>::THREADS), 1)
+__global__ void __launch_bounds__((BwdShape<D, false>::THREADS), (D <= 128 ? 2 : 1))
 attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
                   bf16_t* __restrict__ dqkv, float* __restrict__ delta, float* __restrict__ rd,
                   float* __restrict__ part, BwdPlan p, BwdWork wk) {
@@ -352,19 +367,27 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
         __builtin_amdgcn_sched_barrier(0);
         k0 = k0n; k1 = k1n; v0 = v0n; v1 = v1n;
       }
+      // P; the mask is tested only on a tile that reaches past the sequence
+      // or (causal) past the wave's first row (wave-uniform choice)
       float pr[QB][8];
+      auto probs = [&](auto mask) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        const int row = q0 + 16 * b + r16;
+        for (int b = 0; b < QB; ++b) {
+          const int row = q0 + 16 * b + r16;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kb + 16 * h + 4 * g + e;
-            const bool masked = key >= p.sq || (p.causal && key > row);
-            pr[b][4 * h + e] = masked ? 0.f : exp2f(s[b][h][e] * p.scale_log2 - lse2[b]);
-          }
-      }
+            for (int e = 0; e < 4; ++e) {
+              const int key = kb + 16 * h + 4 * g + e;
+              float x = s[b][h][e] * p.scale_log2 - lse2[b];
+              // a masked pair's exponent is -inf (2^-inf = 0): a select, not a branch
+              if constexpr (decltype(mask)::value) x = (key >= p.sq || (p.causal && key > row)) ? -INFINITY : x;
+              pr[b][4 * h + e] = fast_exp2(x);
+            }
+        }
+      };
+      if (kb + kBT <= p.sq && (!p.causal || kb + kBT - 1 <= q0)) probs(std::false_type{});
+      else probs(std::true_type{});
       if constexpr (PHASE == 0) {
 #pragma unroll
         for (int b = 0; b < QB; ++b)
@@ -441,7 +464,7 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
 // dV written as bf16 when the block is one chunk, else as one fp32 partial
 // (part[item][key][2 D]: dK then dV) for the merge.
 template <int D>
-__global__ void __launch_bounds__((BwdShape<D, true>::THREADS), 1)
+__global__ void __launch_bounds__((BwdShape<D, true>::THREADS), (D <= 64 ? 2 : 1))
 attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
                    const float* __restrict__ delta, bf16_t* __restrict__ dqkv, float* __restrict__ part, BwdPlan p,
                    BwdWork wk) {
@@ -449,6 +472,7 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
   constexpr int KB = S::RB;     // 16-key blocks per wave
   constexpr int WR = 16 * KB;   // keys per wave
   __shared__ __attribute__((aligned(16))) bf16_t lds[4 * S::TILE];   // Q0 Q1 dO0 dO1
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][64];        // per stage: lse, Delta of the tile's queries
 
   const int total = work_total(wk);
   const int item = total - 1 - (int)blockIdx.x;   // longest blocks first
@@ -469,11 +493,14 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
 
   const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)lds);
-  auto issue = [&](int jj) {   // query tile it0 + jj into stage jj & 1
+  const uint32_t rv0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&rowv[0][0][0]);
+  auto issue = [&](int jj) {   // query tile it0 + jj (and its lse, Delta) into stage jj & 1
     const int qb = (it.it0 + jj) * kBT;
     const uint32_t st = (uint32_t)(jj & 1);
     bwd_dma_tile<S>(Qh, p.ld, qb, p.sq - 1, lds0, st * S::TILE * 2, wave, lane);
     bwd_dma_tile<S>(dOh, p.ldo, qb, p.sq - 1, lds0, (2 + st) * S::TILE * 2, wave, lane);
+    if (wave < 2) bwd_dma_rowvals(wave == 0 ? lz : dz, qb, p.sq - 1, rv0 + (2 * st + wave) * 256, lane);
   };
   issue(0);
   if (niter > 1) issue(1);
@@ -507,19 +534,21 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
     const bool live = !p.causal || qb + kBT - 1 >= k0;
     if (live) {
       // lane holds key 16 b + r16 and the tile's queries 16 h + 4 g + e
-      float lq[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lq[4 * h + e] = lz[min(qb + 16 * h + 4 * g + e, p.sq - 1)] * 1.4426950408889634f;
+      const float* rv = &rowv[jj & 1][0][0];
       // S^T = K Q^T, then P^T (fp32, kept for dS) and its bf16 fragment.
-      // The next k-step's fragments are read while this one's MFMAs run.
+      // The accumulators start at -lse sqrt(d), so that scaling them by
+      // log2(e) / sqrt(d) gives the exponent of P directly.  The next
+      // k-step's fragments are read while this one's MFMAs run.
       float pr[KB][8];
       bf16x8_t pf[KB];
       {
         f32x4_t sc[KB][2];
 #pragma unroll
-        for (int b = 0; b < KB; ++b) sc[b][0] = sc[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(rv + 16 * h + 4 * g) * p.neg_sqrt_d;
+#pragma unroll
+          for (int b = 0; b < KB; ++b) sc[b][h] = l4;
+        }
         bf16x8_t f0 = bwd_row_frag<S>(Qt, 0, 0, r16, g), f1 = bwd_row_frag<S>(Qt, 0, 1, r16, g);
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) {
@@ -537,19 +566,27 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           f0 = n0;
           f1 = n1;
         }
+        // the mask is tested only on a tile that reaches past the sequence
+        // or (causal) before the wave's last key (wave-uniform choice)
+        auto probs = [&](auto mask) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          const int key = k0 + 16 * b + r16;
+          for (int b = 0; b < KB; ++b) {
+            const int key = k0 + 16 * b + r16;
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int q = qb + 16 * h + 4 * g + e;
-              const bool masked = q >= p.sq || (p.causal && q < key);
-              pr[b][4 * h + e] = masked ? 0.f : exp2f(sc[b][h][e] * p.scale_log2 - lq[4 * h + e]);
-            }
-          pf[b] = pack_frag(pr[b]);
-        }
+              for (int e = 0; e < 4; ++e) {
+                const int q = qb + 16 * h + 4 * g + e;
+                float x = sc[b][h][e] * p.scale_log2;
+                // a masked pair's exponent is -inf (2^-inf = 0): a select, not a branch
+                if constexpr (decltype(mask)::value) x = (q >= p.sq || (p.causal && q < key)) ? -INFINITY : x;
+                pr[b][4 * h + e] = fast_exp2(x);
+              }
+            pf[b] = pack_frag(pr[b]);
+          }
+        };
+        if (qb + kBT <= p.sq && (!p.causal || qb >= k0 + WR - 1)) probs(std::false_type{});
+        else probs(std::true_type{});
       }
       // dV += P^T dO: dO^T fragment of column block n at query rows 4 g.. and 16 + 4 g..
       {
@@ -564,17 +601,17 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           oc = on;
         }
       }
-      // dP^T = V dO^T, then dS^T = P^T (dP^T - Delta) / sqrt(d) as a bf16 fragment
+      // dP^T - Delta = V dO^T - Delta (accumulators start at -Delta), then
+      // dS^T = P^T (dP^T - Delta) / sqrt(d) as a bf16 fragment
       bf16x8_t dsf[KB];
       {
-        float dq[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dq[4 * h + e] = dz[min(qb + 16 * h + 4 * g + e, p.sq - 1)];
         f32x4_t dc[KB][2];
 #pragma unroll
-        for (int b = 0; b < KB; ++b) dc[b][0] = dc[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < 2; ++h) {
+          const f32x4_t d4 = -*reinterpret_cast<const f32x4_t*>(rv + 64 + 16 * h + 4 * g);
+#pragma unroll
+          for (int b = 0; b < KB; ++b) dc[b][h] = d4;
+        }
         bf16x8_t f0 = bwd_row_frag<S>(Ot, 0, 0, r16, g), f1 = bwd_row_frag<S>(Ot, 0, 1, r16, g);
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) {
@@ -599,7 +636,7 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              ds[4 * h + e] = pr[b][4 * h + e] * (dc[b][h][e] - dq[4 * h + e]) * p.scale;
+              ds[4 * h + e] = pr[b][4 * h + e] * dc[b][h][e] * p.scale;
           dsf[b] = pack_frag(ds);
         }
       }
@@ -616,6 +653,14 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           qc = qn;
         }
       }
+    }
+    if constexpr (S::AGPR_ACC) {
+      // the accumulators stay in the accumulation registers across
+      // iterations (the MFMAs read and write them there in place)
+#pragma unroll
+      for (int b = 0; b < KB; ++b)
+#pragma unroll
+        for (int n = 0; n < S::NB; ++n) asm volatile("" : "+a"(dk[b][n]), "+a"(dv[b][n]));
     }
     if (jj + 1 < niter) {
       wait_vmem();
