@@ -107,26 +107,64 @@ __host__ __device__ inline int block_chunks(const Plan& p, int i) {
   return (block_iters(p, i) + p.chunk - 1) / p.chunk;
 }
 
+// Search over blocks 0 .. nb-1 with per-block counts (a, b) = cnt(s): the
+// first block s at which the running sum of a exceeds r, and the sums of a
+// and of b over the blocks before it.  The wave's 64 lanes take 64 blocks
+// at a time and form inclusive prefix sums by shuffles, so a search costs
+// one count per lane and round instead of one per block.  Called by every
+// lane of the wave; all lanes get the same result.  If r is past the total,
+// the last block is returned (with its sums before it).
+struct Located {
+  int s, a, b;
+};
+template <class F>
+__device__ inline Located wave_locate(int nb, int r, F cnt) {
+  const int lane = threadIdx.x & 63;
+  int a0 = 0, b0 = 0, la = 0, lb = 0;
+  for (int s0 = 0; s0 < nb; s0 += 64) {
+    const int s = s0 + lane;
+    int ca = 0, cb = 0;
+    if (s < nb) {
+      const int2 c = cnt(s);
+      ca = c.x;
+      cb = c.y;
+    }
+    int ia = ca, ib = cb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int ta = __shfl_up(ia, off), tb = __shfl_up(ib, off);
+      if (lane >= off) {
+        ia += ta;
+        ib += tb;
+      }
+    }
+    const uint64_t hit = __ballot(a0 + ia > r);
+    if (hit) {
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      return Located{s0 + L, a0 + __shfl(ia - ca, L), b0 + __shfl(ib - cb, L)};
+    }
+    const int last = min(63, nb - 1 - s0);
+    la = __shfl(ca, last);
+    lb = __shfl(cb, last);
+    a0 += __shfl(ia, 63);
+    b0 += __shfl(ib, 63);
+  }
+  return Located{nb - 1, a0 - la, b0 - lb};
+}
+
 // item -> (z, query block i, chunk c of C, its iterations [it0, it1), first item of the block)
 struct Item {
   int z, i, c, C, it0, it1, first;
 };
-__host__ __device__ inline Item decode_item(const Plan& p, int item) {
+__device__ inline Item decode_item(const Plan& p, int item) {
   Item t;
   t.z = item / p.items_per_z;
-  int r = item - t.z * p.items_per_z;
-  int i = 0, base = 0;
-  for (;; ++i) {
-    const int C = block_chunks(p, i);
-    if (r < C || i == p.nqb - 1) {
-      t.i = i;
-      t.c = r;
-      t.C = C;
-      break;
-    }
-    r -= C;
-    base += C;
-  }
+  const int r = item - t.z * p.items_per_z;
+  const Located l = wave_locate(p.nqb, r, [&](int i) { return int2{block_chunks(p, i), 0}; });
+  const int base = __builtin_amdgcn_readfirstlane(l.a);
+  t.i = __builtin_amdgcn_readfirstlane(l.s);
+  t.c = r - base;
+  t.C = block_chunks(p, t.i);
   const int n = block_iters(p, t.i);
   t.it0 = (int)((int64_t)t.c * n / t.C);
   t.it1 = (int)((int64_t)(t.c + 1) * n / t.C);
@@ -433,16 +471,13 @@ __global__ void __launch_bounds__(kMergeThreads) attn_fwd_merge_kernel(const flo
   const int blk = blockIdx.x / GROUPS;
   const int rg = blockIdx.x - blk * GROUPS;
   const int z = blk / merges_per_z;
-  int k = blk - z * merges_per_z;   // k-th split block of this (batch, head)
-  int i = 0, base = 0;
-  for (; i < p.nqb; ++i) {
-    const int C = block_chunks(p, i);
-    if (C > 1) {
-      if (k == 0) break;
-      --k;
-    }
-    base += C;
-  }
+  const int k = blk - z * merges_per_z;   // k-th split block of this (batch, head)
+  const Located l = wave_locate(p.nqb, k, [&](int i) {
+    const int c = block_chunks(p, i);
+    return int2{c > 1 ? 1 : 0, c};
+  });
+  const int i = __builtin_amdgcn_readfirstlane(l.s);
+  const int base = __builtin_amdgcn_readfirstlane(l.b);
   const int C = block_chunks(p, i);
   const int first = z * p.items_per_z + base;
   const int zo = z / p.hs, zi = z - zo * p.hs;

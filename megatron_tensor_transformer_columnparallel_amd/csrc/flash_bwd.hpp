@@ -188,22 +188,15 @@ __host__ __device__ inline int work_tiles(const BwdWork& w, int i) {
 __host__ __device__ inline int work_chunks(const BwdWork& w, int i) { return (work_tiles(w, i) + w.chunk - 1) / w.chunk; }
 
 // item -> (z, block i, chunk c of C, absolute tiles [it0, it1), first item of the block)
-__host__ __device__ inline Item work_item(const BwdWork& w, int item) {
+__device__ inline Item work_item(const BwdWork& w, int item) {
   Item t;
   t.z = item / w.items_per_z;
-  int r = item - t.z * w.items_per_z;
-  int s = 0, base = 0;
-  for (;; ++s) {
-    const int C = work_chunks(w, work_block(w, s));
-    if (r < C || s == w.nb - 1) {
-      t.i = work_block(w, s);
-      t.c = r;
-      t.C = C;
-      break;
-    }
-    r -= C;
-    base += C;
-  }
+  const int r = item - t.z * w.items_per_z;
+  const Located l = wave_locate(w.nb, r, [&](int s) { return int2{work_chunks(w, work_block(w, s)), 0}; });
+  const int base = __builtin_amdgcn_readfirstlane(l.a);
+  t.i = work_block(w, __builtin_amdgcn_readfirstlane(l.s));
+  t.c = r - base;
+  t.C = work_chunks(w, t.i);
   const int n = work_tiles(w, t.i), f = work_first_tile(w, t.i);
   t.it0 = f + (int)((int64_t)t.c * n / t.C);
   t.it1 = f + (int)((int64_t)(t.c + 1) * n / t.C);
@@ -711,17 +704,13 @@ __global__ void __launch_bounds__(kMergeThreads) attn_bwd_merge_kernel(const flo
   const int blk = blockIdx.x / groups;
   const int rg = blockIdx.x - blk * groups;
   const int z = blk / merges_per_z;
-  int k = blk - z * merges_per_z;   // k-th split block of this (batch, head), in slot order
-  int s = 0, base = 0;
-  for (; s < wk.nb; ++s) {
-    const int C = work_chunks(wk, work_block(wk, s));
-    if (C > 1) {
-      if (k == 0) break;
-      --k;
-    }
-    base += C;
-  }
-  const int i = work_block(wk, s);
+  const int k = blk - z * merges_per_z;   // k-th split block of this (batch, head), in slot order
+  const Located l = wave_locate(wk.nb, k, [&](int s) {
+    const int c = work_chunks(wk, work_block(wk, s));
+    return int2{c > 1 ? 1 : 0, c};
+  });
+  const int i = work_block(wk, __builtin_amdgcn_readfirstlane(l.s));
+  const int base = __builtin_amdgcn_readfirstlane(l.b);
   const int C = work_chunks(wk, i);
   const int first = z * wk.items_per_z + base;
   const int zo = z / p.hs, zi = z - zo * p.hs;
