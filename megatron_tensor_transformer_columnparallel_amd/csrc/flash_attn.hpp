@@ -57,11 +57,14 @@ struct Shape {
   static constexpr int NB = D / 16;      // 16-column blocks of O
   static constexpr int CPR = D / 8;      // 16-byte chunks per K or V row
   // LDS layout of a K or V tile (kBK key rows of CPR 16-byte chunks).
-  // Rows of at most 32 chunks: XOR swizzle.  K: chunk c of key row r sits at
-  // c ^ (r & KSW), so the 16 lanes that read one chunk of 16 consecutive keys
-  // hit 16 distinct slots; V: at c ^ 2 (r & VSW) (chunk pairs stay pairs), so
+  // Rows of 16 or 32 chunks: XOR swizzle.  K: chunk c of key row r sits at
+  // c ^ (r & 15), so the 16 lanes that read one chunk of 16 consecutive keys
+  // hit 16 distinct slots; V: at c ^ 2 (r & 7) (chunk pairs stay pairs), so
   // the transposing read of 4 consecutive key rows x 32 bytes by a 16-lane
-  // group, and of two such groups, hits distinct slots.
+  // group, and of two such groups, hits distinct slots.  Rows of 8 chunks
+  // (head dim 64): both at c ^ (r & 7), which keeps the row read and the
+  // transposing read at full LDS rate (a pattern probe timed 2 (r & 3) for V
+  // 1.3x slower there).
   // Rows of 64 chunks (head dim 512): each row is padded to ROT_PITCH chunks
   // and rotated instead (chunk c of K row r at c + (r & 15), of V row r at
   // c + 2 (r & 7)): the same bank spread, but a lane's address for every
@@ -70,14 +73,15 @@ struct Shape {
   static constexpr bool ROT = CPR >= 64;
   static constexpr int PITCH = ROT ? (CPR + 16) * 8 : D;   // bf16 elements per LDS row
   static constexpr int TILE = kBK * PITCH;                // bf16 elements of one K or V tile
-  static constexpr int KSW = (CPR >= 16 ? 16 : CPR) - 1;
-  static constexpr int VSW = (CPR >= 16 ? 8 : CPR / 2) - 1;
+  // slot of logical chunk c of K (V) row r (XOR layouts)
+  static __host__ __device__ constexpr int kswz(int r) { return CPR >= 16 ? (r & 15) : (r & 7); }
+  static __host__ __device__ constexpr int vswz(int r) { return CPR >= 16 ? 2 * (r & 7) : (r & 7); }
   // element offset of logical chunk c of K (V) row r
   static __device__ __forceinline__ int koff(int r, int c) {
-    return r * PITCH + (ROT ? c + (r & 15) : c ^ (r & KSW)) * 8;
+    return r * PITCH + (ROT ? c + (r & 15) : c ^ kswz(r)) * 8;
   }
   static __device__ __forceinline__ int voff(int r, int c) {
-    return r * PITCH + (ROT ? c + 2 * (r & 7) : c ^ (2 * (r & VSW))) * 8;
+    return r * PITCH + (ROT ? c + 2 * (r & 7) : c ^ vswz(r)) * 8;
   }
   static constexpr int DPW = kBK * CPR / 64 / WAVES;   // 1 KB DMA instructions per wave per tile
   static_assert(D % 64 == 0 && D >= 64 && D <= 512, "head dim");
@@ -239,7 +243,7 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
       } else {
         const int q = ins * 64 + lane;
         const int r = q / S::CPR, ph = q % S::CPR;
-        const int c = ph ^ (isV ? 2 * (r & S::VSW) : (r & S::KSW));
+        const int c = ph ^ (isV ? S::vswz(r) : S::kswz(r));
         sb = uniform_addr(head + (int64_t)kb * p.ld);
         voff = (uint32_t)((int64_t)min(r, rmax) * p.ld * 2 + c * 16);
         m0 = lds0 + off + (uint32_t)(ins * 64 * 16);
