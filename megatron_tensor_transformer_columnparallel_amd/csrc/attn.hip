@@ -418,14 +418,17 @@ static int blocks_per_cu(K kernel, int threads) {
   return n;
 }
 
-// Work items one round of the flash forward runs at once: CUs times the
-// kernel's workgroups per CU, so that a wave of one item can run its
-// softmax while another's MFMAs run on the same SIMD.
+// Work items the flash forward plans for: CUs times the kernel's
+// workgroups per CU, so that a wave of one item can run its softmax while
+// another's MFMAs run on the same SIMD; at most two per CU from head dim
+// 128 on, where the partials of the extra split blocks cost the merge more
+// than the third workgroup gains (measured at s = 2048 with 8 heads of 128:
+// 39.7 us with two, 44.1 us with three).
 template <int D>
 static int fwd_slots() {
   constexpr int QB = D >= 512 ? 1 : 2;
   static const int per_cu = blocks_per_cu(flash::attn_fwd_flash_kernel<D, QB>, flash::Shape<D, QB>::THREADS);
-  return device_cus() * per_cu;
+  return device_cus() * (D >= 128 ? std::min(per_cu, 2) : per_cu);
 }
 static int fwd_slots_d(int64_t d) {
   if (d == 64) return fwd_slots<64>();

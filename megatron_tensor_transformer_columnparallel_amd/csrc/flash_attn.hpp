@@ -180,6 +180,26 @@ __device__ inline Item decode_item(const Plan& p, int item) {
 // normal range flush to 0, which a softmax sum never feels, and 2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions of a value over lanes i and i ^ 16 (i ^ 32) by the lane-swap
+// instructions: with both operands holding v, the swap leaves lane i with
+// v_i in one and v_(i^16) (v_(i^32)) in the other.
+__device__ __forceinline__ float lane_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Two fp32 values to a bf16 pair by the hardware conversion (round to nearest
 // even, as pack_bf16x2), one instruction instead of the bit arithmetic.
 __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
@@ -324,42 +344,34 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
         kc0 = kn0;
         kc1 = kn1;
       }
-      // online softmax (log2 domain)
-      float t[QB][8];
-      bool move = false;
-      float mn[QB];
-      // the mask is tested only on a tile that reaches past the sequence or
-      // (causal) past the wave's first row (wave-uniform choice)
-      const bool whole = kb + kBK <= p.sq && (!p.causal || kb + kBK - 1 <= q0);
+      // online softmax (log2 domain).  The mask is applied only on a tile
+      // that reaches past the sequence or (causal) past the wave's first row
+      // (wave-uniform choice), by setting the raw score to -inf in place;
+      // the running max m is kept in log2 units (raw max x scale).
+      if (!(kb + kBK <= p.sq && (!p.causal || kb + kBK - 1 <= q0))) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        const int row = q0 + 16 * b + r16;
-        float mx = -INFINITY;
-        if (whole) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float v = s[b][h][e] * p.scale_log2;
-              t[b][4 * h + e] = v;
-              mx = fmaxf(mx, v);
-            }
-        } else {
+        for (int b = 0; b < QB; ++b) {
+          const int row = q0 + 16 * b + r16;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int key = kb + 16 * h + 4 * g + e;
-              const bool masked = key >= p.sq || (p.causal && key > row);
-              const float v = masked ? -INFINITY : s[b][h][e] * p.scale_log2;
-              t[b][4 * h + e] = v;
-              mx = fmaxf(mx, v);
+              if (key >= p.sq || (p.causal && key > row)) s[b][h][e] = -INFINITY;
             }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mn[b] = fmaxf(m[b], mx);
-        move |= mn[b] > m[b] + kLazy || (m[b] == -INFINITY && mn[b] > -INFINITY);
+      }
+      bool move = false;
+      float mn[QB];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        float mx = fmaxf(fmaxf(fmaxf(s[b][0][0], s[b][0][1]), fmaxf(s[b][0][2], s[b][0][3])),
+                         fmaxf(fmaxf(s[b][1][0], s[b][1][1]), fmaxf(s[b][1][2], s[b][1][3])));
+        mx = lane_max16(mx);
+        mx = lane_max32(mx);
+        mn[b] = fmaxf(m[b], mx * p.scale_log2);
+        // -inf + 8 = -inf: the first finite max moves it too
+        move |= mn[b] > m[b] + kLazy;
       }
       if (__ballot(move)) {
         // move every row's max to its block max (alpha = 1 where unchanged)
@@ -367,7 +379,7 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
         for (int b = 0; b < QB; ++b) {
           // m = -inf and a finite new max: 0 (nothing accumulated yet);
           // a row still without any score: unchanged
-          const float alpha = mn[b] == -INFINITY ? 1.f : exp2f(m[b] - mn[b]);
+          const float alpha = mn[b] == -INFINITY ? 1.f : fast_exp2(m[b] - mn[b]);
           l[b] *= alpha;
 #pragma unroll
           for (int n = 0; n < S::NB; ++n) acc[b][n] *= alpha;
@@ -377,11 +389,13 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
       uint32_t pk[QB][4];
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
+        // a row without any score so far keeps m = -inf: its masked scores
+        // give 2^(-inf - 0) = 0
         const float sub = m[b] == -INFINITY ? 0.f : m[b];
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(t[b][e] - sub);
+          pv[e] = fast_exp2(fmaf(s[b][e >> 2][e & 3], p.scale_log2, -sub));
           l[b] += pv[e];
         }
 #pragma unroll
@@ -423,10 +437,7 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
 
   // row sums over the four lanes of each row
 #pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    l[b] += __shfl_xor(l[b], 16);
-    l[b] += __shfl_xor(l[b], 32);
-  }
+  for (int b = 0; b < QB; ++b) l[b] = lane_sum32(lane_sum16(l[b]));
   if (it.C == 1) {
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
