@@ -7,7 +7,9 @@
 //   P_ij  = exp(S_ij - lse_i)                     recomputed from the saved lse
 //   dP_ij = dO_i . V_j
 //   dS_ij = P_ij (dP_ij - Delta_i) / sqrt(d)      Delta_i = sum_j P_ij dP_ij / sum_j P_ij
-// and dQ = dS K, dK = dS^T Q, dV = P^T dO.  Delta is taken from the same
+// and dQ = dS K, dK = dS^T Q, dV = P^T dO.  The kernels round P (dP - Delta)
+// to bf16 for the products and apply the 1 / sqrt(d) to dQ and dK once, in
+// fp32, where they are written.  Delta is taken from the same
 // fp32 P and dP that form dS, so every row of dS sums to zero: a rounding of
 // O or dO cannot leak into dQ through the keys' common component.
 //
@@ -254,7 +256,7 @@ inline int work_merges_per_z(const BwdWork& w) {
 // (in chunk order, so every chunk of a block gets the same bits), then dQ
 // over the item's keys: written as bf16 when the block is one chunk, else
 // as an fp32 partial (part[item][row][D]) for the merge; the block's first
-// chunk also writes Delta for the dK/dV phase.
+// chunk also writes -Delta (negated) for the dK/dV phase.
 template <int D, int PHASE>
 __global__ void __launch_bounds__((BwdShape<D, false>::THREADS), (D <= 128 ? 2 : 1))
 attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO, const float* __restrict__ lse,
@@ -402,7 +404,7 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ds[4 * h + e] = pr[b][4 * h + e] * (dp[b][h][e] - dl[b]) * p.scale;
+            for (int e = 0; e < 4; ++e) ds[4 * h + e] = pr[b][4 * h + e] * (dp[b][h][e] - dl[b]);
           dsf[b] = pack_frag(ds);
         }
         // dQ += dS K: K^T fragment of column block n at key rows 4 g.. and 16 + 4 g..
@@ -441,16 +443,16 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
           bf16_t* dst = dqkv + ((int64_t)zo * p.sq + row) * p.ld + (int64_t)zi * D + 4 * g;
 #pragma unroll
           for (int n = 0; n < S::NB; ++n) {
-            const f32x4_t v = acc[b][n];
+            const f32x4_t v = acc[b][n] * p.scale;
             *reinterpret_cast<u32x2_t*>(dst + 16 * n) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
         }
       } else {
         float* po = part + ((int64_t)item * S::BB + rl) * D + 4 * g;
 #pragma unroll
-        for (int n = 0; n < S::NB; ++n) *reinterpret_cast<f32x4_t*>(po + 16 * n) = acc[b][n];
+        for (int n = 0; n < S::NB; ++n) *reinterpret_cast<f32x4_t*>(po + 16 * n) = acc[b][n] * p.scale;
       }
-      if (it.c == 0 && g == 0 && row < p.sq) delta[(int64_t)z * p.sq + row] = dl[b];
+      if (it.c == 0 && g == 0 && row < p.sq) delta[(int64_t)z * p.sq + row] = -dl[b];   // stored negated
     }
   }
 }
@@ -539,12 +541,9 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
       bf16x8_t pf[KB];
       {
         f32x4_t sc[KB][2];
+        f32x4_t l4[2];   // the first k-step's MFMAs start from it
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(rv + 16 * h + 4 * g) * p.neg_sqrt_d;
-#pragma unroll
-          for (int b = 0; b < KB; ++b) sc[b][h] = l4;
-        }
+        for (int h = 0; h < 2; ++h) l4[h] = *reinterpret_cast<const f32x4_t*>(rv + 16 * h + 4 * g) * p.neg_sqrt_d;
         bf16x8_t f0 = bwd_row_frag<S>(Qt, 0, 0, r16, g), f1 = bwd_row_frag<S>(Qt, 0, 1, r16, g);
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) {
@@ -555,8 +554,8 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           }
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
-            sc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, kf[b][ks], sc[b][0], 0, 0, 0);
-            sc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, kf[b][ks], sc[b][1], 0, 0, 0);
+            sc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, kf[b][ks], ks == 0 ? l4[0] : sc[b][0], 0, 0, 0);
+            sc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, kf[b][ks], ks == 0 ? l4[1] : sc[b][1], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
           f0 = n0;
@@ -598,16 +597,13 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
         }
       }
       // dP^T - Delta = V dO^T - Delta (accumulators start at -Delta), then
-      // dS^T = P^T (dP^T - Delta) / sqrt(d) as a bf16 fragment
+      // P^T (dP^T - Delta) as a bf16 fragment (dK takes the 1 / sqrt(d) at the end)
       bf16x8_t dsf[KB];
       {
         f32x4_t dc[KB][2];
+        f32x4_t d4[2];   // -Delta of the tile's queries (stored negated)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x4_t d4 = -*reinterpret_cast<const f32x4_t*>(rv + 64 + 16 * h + 4 * g);
-#pragma unroll
-          for (int b = 0; b < KB; ++b) dc[b][h] = d4;
-        }
+        for (int h = 0; h < 2; ++h) d4[h] = *reinterpret_cast<const f32x4_t*>(rv + 64 + 16 * h + 4 * g);
         bf16x8_t f0 = bwd_row_frag<S>(Ot, 0, 0, r16, g), f1 = bwd_row_frag<S>(Ot, 0, 1, r16, g);
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) {
@@ -618,8 +614,8 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           }
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
-            dc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, vf[b][ks], dc[b][0], 0, 0, 0);
-            dc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, vf[b][ks], dc[b][1], 0, 0, 0);
+            dc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, vf[b][ks], ks == 0 ? d4[0] : dc[b][0], 0, 0, 0);
+            dc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, vf[b][ks], ks == 0 ? d4[1] : dc[b][1], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
           f0 = n0;
@@ -632,7 +628,7 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              ds[4 * h + e] = pr[b][4 * h + e] * dc[b][h][e] * p.scale;
+              ds[4 * h + e] = pr[b][4 * h + e] * dc[b][h][e];
           dsf[b] = pack_frag(ds);
         }
       }
@@ -675,7 +671,7 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
         bf16_t* dvd = dkd + (int64_t)p.hs * D;
 #pragma unroll
         for (int n = 0; n < S::NB; ++n) {
-          const f32x4_t a = dk[b][n], c = dv[b][n];
+          const f32x4_t a = dk[b][n] * p.scale, c = dv[b][n];
           *reinterpret_cast<u32x2_t*>(dkd + 16 * n) = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
           *reinterpret_cast<u32x2_t*>(dvd + 16 * n) = u32x2_t{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
         }
@@ -684,7 +680,7 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
       float* po = part + ((int64_t)item * S::BB + rl) * (2 * D) + 4 * g;
 #pragma unroll
       for (int n = 0; n < S::NB; ++n) {
-        *reinterpret_cast<f32x4_t*>(po + 16 * n) = dk[b][n];
+        *reinterpret_cast<f32x4_t*>(po + 16 * n) = dk[b][n] * p.scale;
         *reinterpret_cast<f32x4_t*>(po + D + 16 * n) = dv[b][n];
       }
     }
