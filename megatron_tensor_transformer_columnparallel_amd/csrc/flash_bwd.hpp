@@ -336,35 +336,34 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
     const bf16_t* Vt = lds + (2 + (jj & 1)) * S::TILE;
     const bool live = !p.causal || kb <= q0 + WR - 1;
     if (live) {
-      // S = Q K^T and dP = dO V^T: lane holds row 16 b + r16, keys 16 h + 4 g + e.
-      // The next k-step's four fragments are read while this one's MFMAs
-      // run; the scheduling barrier keeps the compiler from hoisting every
-      // read of the loop (4 KS more registers).
+      // S = Q K^T, then dP = dO V^T: lane holds row 16 b + r16, keys
+      // 16 h + 4 g + e.  The S chain goes first, so the P arithmetic runs
+      // while the dP MFMAs execute.  The next k-step's fragments are read
+      // while this one's MFMAs run; the scheduling barriers keep the compiler
+      // from hoisting every read of the loop.
       f32x4_t s[QB][2], dp[QB][2];
+      auto chain = [&](const bf16_t* tile, const bf16x8_t (&x)[QB][S::KS], f32x4_t (&c)[QB][2]) {
+        bf16x8_t f0 = bwd_row_frag<S>(tile, 0, 0, r16, g), f1 = bwd_row_frag<S>(tile, 0, 1, r16, g);
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
-        s[b][0] = s[b][1] = dp[b][0] = dp[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      bf16x8_t k0 = bwd_row_frag<S>(Kt, 0, 0, r16, g), k1 = bwd_row_frag<S>(Kt, 0, 1, r16, g);
-      bf16x8_t v0 = bwd_row_frag<S>(Vt, 0, 0, r16, g), v1 = bwd_row_frag<S>(Vt, 0, 1, r16, g);
+        for (int ks = 0; ks < S::KS; ++ks) {
+          bf16x8_t n0 = f0, n1 = f1;
+          if (ks + 1 < S::KS) {
+            n0 = bwd_row_frag<S>(tile, ks + 1, 0, r16, g);
+            n1 = bwd_row_frag<S>(tile, ks + 1, 1, r16, g);
+          }
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        bf16x8_t k0n = k0, k1n = k1, v0n = v0, v1n = v1;
-        if (ks + 1 < S::KS) {
-          k0n = bwd_row_frag<S>(Kt, ks + 1, 0, r16, g);
-          k1n = bwd_row_frag<S>(Kt, ks + 1, 1, r16, g);
-          v0n = bwd_row_frag<S>(Vt, ks + 1, 0, r16, g);
-          v1n = bwd_row_frag<S>(Vt, ks + 1, 1, r16, g);
+          for (int b = 0; b < QB; ++b) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            c[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, x[b][ks], ks == 0 ? z : c[b][0], 0, 0, 0);
+            c[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, x[b][ks], ks == 0 ? z : c[b][1], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          f0 = n0;
+          f1 = n1;
         }
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-          s[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[b][ks], s[b][0], 0, 0, 0);
-          s[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[b][ks], s[b][1], 0, 0, 0);
-          dp[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, of[b][ks], dp[b][0], 0, 0, 0);
-          dp[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, of[b][ks], dp[b][1], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        k0 = k0n; k1 = k1n; v0 = v0n; v1 = v1n;
-      }
+      };
+      chain(Kt, qf, s);
+      chain(Vt, of, dp);
       // P; the mask is tested only on a tile that reaches past the sequence
       // or (causal) past the wave's first row (wave-uniform choice)
       float pr[QB][8];
@@ -533,14 +532,14 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
     if (live) {
       // lane holds key 16 b + r16 and the tile's queries 16 h + 4 g + e
       const float* rv = &rowv[jj & 1][0][0];
-      // S^T = K Q^T, then P^T (fp32, kept for dS) and its bf16 fragment.
-      // The accumulators start at -lse sqrt(d), so that scaling them by
-      // log2(e) / sqrt(d) gives the exponent of P directly.  The next
-      // k-step's fragments are read while this one's MFMAs run.
-      float pr[KB][8];
-      bf16x8_t pf[KB];
+      // S^T = K Q^T and dP^T - Delta = V dO^T - Delta back to back, so that
+      // the P arithmetic runs while the dP^T MFMAs execute and the dS
+      // arithmetic while the dV MFMAs do.  The S^T accumulators start at
+      // -lse sqrt(d), so that scaling them by log2(e) / sqrt(d) gives the
+      // exponent of P directly; the dP^T ones at -Delta.  The next k-step's
+      // fragments are read while this one's MFMAs run.
+      f32x4_t sc[KB][2], dc[KB][2];
       {
-        f32x4_t sc[KB][2];
         f32x4_t l4[2];   // the first k-step's MFMAs start from it
 #pragma unroll
         for (int h = 0; h < 2; ++h) l4[h] = *reinterpret_cast<const f32x4_t*>(rv + 16 * h + 4 * g) * p.neg_sqrt_d;
@@ -561,8 +560,35 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           f0 = n0;
           f1 = n1;
         }
-        // the mask is tested only on a tile that reaches past the sequence
-        // or (causal) before the wave's last key (wave-uniform choice)
+      }
+      {
+        f32x4_t d4[2];   // -Delta of the tile's queries (stored negated)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) d4[h] = *reinterpret_cast<const f32x4_t*>(rv + 64 + 16 * h + 4 * g);
+        bf16x8_t f0 = bwd_row_frag<S>(Ot, 0, 0, r16, g), f1 = bwd_row_frag<S>(Ot, 0, 1, r16, g);
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks) {
+          bf16x8_t n0 = f0, n1 = f1;
+          if (ks + 1 < S::KS) {
+            n0 = bwd_row_frag<S>(Ot, ks + 1, 0, r16, g);
+            n1 = bwd_row_frag<S>(Ot, ks + 1, 1, r16, g);
+          }
+#pragma unroll
+          for (int b = 0; b < KB; ++b) {
+            dc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, vf[b][ks], ks == 0 ? d4[0] : dc[b][0], 0, 0, 0);
+            dc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, vf[b][ks], ks == 0 ? d4[1] : dc[b][1], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          f0 = n0;
+          f1 = n1;
+        }
+      }
+      // P^T (fp32, kept for dS) and its bf16 fragment.  The mask is tested
+      // only on a tile that reaches past the sequence or (causal) before the
+      // wave's last key (wave-uniform choice).
+      float pr[KB][8];
+      bf16x8_t pf[KB];
+      {
         auto probs = [&](auto mask) {
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
@@ -596,41 +622,16 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
           oc = on;
         }
       }
-      // dP^T - Delta = V dO^T - Delta (accumulators start at -Delta), then
       // P^T (dP^T - Delta) as a bf16 fragment (dK takes the 1 / sqrt(d) at the end)
       bf16x8_t dsf[KB];
-      {
-        f32x4_t dc[KB][2];
-        f32x4_t d4[2];   // -Delta of the tile's queries (stored negated)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) d4[h] = *reinterpret_cast<const f32x4_t*>(rv + 64 + 16 * h + 4 * g);
-        bf16x8_t f0 = bwd_row_frag<S>(Ot, 0, 0, r16, g), f1 = bwd_row_frag<S>(Ot, 0, 1, r16, g);
+      for (int b = 0; b < KB; ++b) {
+        float ds[8];
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) {
-          bf16x8_t n0 = f0, n1 = f1;
-          if (ks + 1 < S::KS) {
-            n0 = bwd_row_frag<S>(Ot, ks + 1, 0, r16, g);
-            n1 = bwd_row_frag<S>(Ot, ks + 1, 1, r16, g);
-          }
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int b = 0; b < KB; ++b) {
-            dc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, vf[b][ks], ks == 0 ? d4[0] : dc[b][0], 0, 0, 0);
-            dc[b][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, vf[b][ks], ks == 0 ? d4[1] : dc[b][1], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          f0 = n0;
-          f1 = n1;
-        }
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          float ds[8];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              ds[4 * h + e] = pr[b][4 * h + e] * dc[b][h][e];
-          dsf[b] = pack_frag(ds);
-        }
+          for (int e = 0; e < 4; ++e) ds[4 * h + e] = pr[b][4 * h + e] * dc[b][h][e];
+        dsf[b] = pack_frag(ds);
       }
       // dK += dS^T Q: Q^T fragment of column block n at query rows 4 g.. and 16 + 4 g..
       {
