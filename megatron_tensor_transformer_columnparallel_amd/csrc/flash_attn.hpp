@@ -180,6 +180,20 @@ __device__ inline Item decode_item(const Plan& p, int item) {
 // normal range flush to 0, which a softmax sum never feels, and 2^-inf = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait for every vector-memory operation of this wave (vmcnt(0); expcnt and
+// lgkmcnt left at their maxima), as the compiler's own instruction: its
+// wait-count pass then knows that the loads issued before this point are
+// complete.  The inline-assembly wait does not tell it that, so before a
+// loop it would place waits for those loads inside the loop body, where they
+// also wait for the tile DMA in flight (which the compiler does not count)
+// on every iteration.
+__device__ __forceinline__ void wait_vmem_known() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Makes the compiler complete a loaded value here (it places its own wait
+// before this point), so that the load is neither moved into nor waited
+// for inside a loop that follows.
+template <class T>
+__device__ __forceinline__ void loaded_here(const T& x) { asm volatile("" :: "v"(x)); }
+
 // Reductions of a value over lanes i and i ^ 16 (i ^ 32) by the lane-swap
 // instructions: with both operands holding v, the swap leaves lane i with
 // v_i in one and v_(i^16) (v_(i^32)) in the other.
@@ -293,6 +307,10 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) qf[b][ks] = *reinterpret_cast<const bf16x8_t*>(src + 32 * ks);
   }
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) loaded_here(qf[b][ks]);
   f32x4_t acc[QB][S::NB];
 #pragma unroll
   for (int b = 0; b < QB; ++b)
@@ -305,7 +323,7 @@ attn_fwd_flash_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, fl
     l[b] = 0.f;
   }
 
-  wait_vmem();
+  wait_vmem_known();
   __syncthreads();
 
   for (int jj = 0; jj < niter; ++jj) {

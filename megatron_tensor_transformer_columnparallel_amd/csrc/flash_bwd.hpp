@@ -318,6 +318,13 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
       dl[b] = den > 0.f ? num / den : 0.f;
     }
   }
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      loaded_here(qf[b][ks]);
+      loaded_here(of[b][ks]);
+    }
   f32x4_t acc[QB][S::NB];
 #pragma unroll
   for (int b = 0; b < QB; ++b)
@@ -327,7 +334,7 @@ attn_bwd_q_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO,
 #pragma unroll
   for (int b = 0; b < QB; ++b) num[b] = den[b] = 0.f;
 
-  wait_vmem();
+  wait_vmem_known();
   __syncthreads();
 
   for (int jj = 0; jj < niter; ++jj) {
@@ -514,13 +521,20 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
       vf[b][ks] = *reinterpret_cast<const bf16x8_t*>(vs_ + 32 * ks);
     }
   }
+#pragma unroll
+  for (int b = 0; b < KB; ++b)
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      loaded_here(kf[b][ks]);
+      loaded_here(vf[b][ks]);
+    }
   f32x4_t dk[KB][S::NB], dv[KB][S::NB];
 #pragma unroll
   for (int b = 0; b < KB; ++b)
 #pragma unroll
     for (int n = 0; n < S::NB; ++n) dk[b][n] = dv[b][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  wait_vmem();
+  wait_vmem_known();
   __syncthreads();
 
   for (int jj = 0; jj < niter; ++jj) {
