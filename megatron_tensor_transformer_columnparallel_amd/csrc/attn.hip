@@ -22,6 +22,7 @@
 
 #include "flash_attn.hpp"
 #include "flash_bwd.hpp"
+#include "flash_fwd_pp.hpp"
 #include "gemm.hpp"
 
 namespace tps {
@@ -418,23 +419,36 @@ static int blocks_per_cu(K kernel, int threads) {
   return n;
 }
 
-// Work items the flash forward plans for: CUs times the kernel's
-// workgroups per CU, so that a wave of one item can run its softmax while
-// another's MFMAs run on the same SIMD; at most two per CU from head dim
-// 128 on, where the partials of the extra split blocks cost the merge more
-// than the third workgroup gains (measured at s = 2048 with 8 heads of 128:
-// 39.7 us with two, 44.1 us with three).
+// Work items the flash forward plans for.  Head dim 128 runs the two-group
+// kernel (256-row items, eight waves): CUs times its workgroups per CU (one).
+// The other head dims run the one-group kernel (128-row items): CUs times
+// its workgroups per CU, so that a wave of one item can run its softmax
+// while another's MFMAs run on the same SIMD; at most two per CU from head
+// dim 256 on, where the partials of the extra split blocks cost the merge
+// more than a third workgroup gains.  At head dim 64 the two-group kernel
+// is slower (63.6 against 45.2 us for 2 x 16 heads at s = 2048): its
+// products are half of head dim 128's while its softmax is the same, and it
+// holds one workgroup per CU where the one-group kernel holds three or four.
+static bool fwd_two_group(int64_t d) { return d == 128; }
 template <int D>
 static int fwd_slots() {
-  constexpr int QB = D >= 512 ? 1 : 2;
-  static const int per_cu = blocks_per_cu(flash::attn_fwd_flash_kernel<D, QB>, flash::Shape<D, QB>::THREADS);
-  return device_cus() * (D >= 128 ? std::min(per_cu, 2) : per_cu);
+  if constexpr (D == 128) {
+    static const int per_cu = blocks_per_cu(flash::attn_fwd_pp_kernel<D>, flash::PPShape<D>::THREADS);
+    return device_cus() * per_cu;
+  } else {
+    constexpr int QB = D >= 512 ? 1 : 2;
+    static const int per_cu = blocks_per_cu(flash::attn_fwd_flash_kernel<D, QB>, flash::Shape<D, QB>::THREADS);
+    return device_cus() * (D >= 256 ? std::min(per_cu, 2) : per_cu);
+  }
 }
 static int fwd_slots_d(int64_t d) {
   if (d == 64) return fwd_slots<64>();
   if (d == 128) return fwd_slots<128>();
   if (d == 256) return fwd_slots<256>();
   return fwd_slots<512>();
+}
+static flash::Plan fwd_plan(int64_t b, int64_t sq, int64_t hs, int64_t d, int causal) {
+  return flash::make_plan(b, sq, hs, (int)d, causal, fwd_slots_d(d), fwd_two_group(d) ? flash::kPPRows : flash::kBQ);
 }
 
 extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int64_t h, int64_t hs, int64_t d) {
@@ -444,9 +458,8 @@ extern "C" size_t tp_attn_fwd_workspace(tps_dtype dt, int64_t b, int64_t sq, int
   if (use_flash(d, sq)) {
     // the query has no causal argument: cover the larger of the two plans
     // (without the mask every block has all keys, so more chunks)
-    const int slots = fwd_slots_d(d);
-    return std::max(flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 1, slots), (int)d),
-                    flash::plan_workspace(flash::make_plan(b, sq, hs, (int)d, 0, slots), (int)d));
+    return std::max(flash::plan_workspace(fwd_plan(b, sq, hs, d, 1), (int)d),
+                    flash::plan_workspace(fwd_plan(b, sq, hs, d, 0), (int)d));
   }
   return attn_fwd_ws_layout(b, sq, hs).total;
 }
@@ -461,7 +474,12 @@ static tps_status flash_fwd_core(const bf16_t* qkv, bf16_t* o, float* lse, void*
                                  hipStream_t st) {
   const int total = p.items_per_z * p.nz;
   float* part = static_cast<float*>(ws);
-  {
+  if constexpr (D == 128) {
+    TraceScope trace_(st, "attn_fwd_pp_kernel");
+    hipLaunchKernelGGL((flash::attn_fwd_pp_kernel<D>), dim3((unsigned)total), dim3(flash::PPShape<D>::THREADS), 0,
+                       st, qkv, o, lse, part, p, total);
+    TPS_TRY(check_launch("attn_fwd_pp_kernel"));
+  } else {
     TraceScope trace_(st, "attn_fwd_flash_kernel");
     constexpr int QB = D >= 512 ? 1 : 2;
     hipLaunchKernelGGL((flash::attn_fwd_flash_kernel<D, QB>), dim3((unsigned)total),
@@ -471,7 +489,7 @@ static tps_status flash_fwd_core(const bf16_t* qkv, bf16_t* o, float* lse, void*
   const int mz = flash::plan_merges_per_z(p);
   if (mz == 0) return TPS_OK;
   TraceScope trace_(st, "attn_fwd_merge_kernel");
-  hipLaunchKernelGGL((flash::attn_fwd_merge_kernel<D>), dim3((unsigned)(mz * p.nz * flash::merge_groups<D>())),
+  hipLaunchKernelGGL((flash::attn_fwd_merge_kernel<D>), dim3((unsigned)(mz * p.nz * flash::merge_groups<D>(p.bq))),
                      dim3(flash::kMergeThreads), 0, st, part, o, lse, p, total, mz);
   return check_launch("attn_fwd_merge_kernel");
 }
@@ -491,7 +509,7 @@ extern "C" tps_status tp_attn_fwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
     // QKV_i = X Wqkv_i                       (NN)
     TPS_TRY((gemm_bf16<true, false>((const bf16_t*)X, (const bf16_t*)Wqkv_i, shape(M, w3, h, h, w3),
                                     EpiStore<bf16_t>{qkv, w3, 0, 0}, st)));
-    const flash::Plan p = flash::make_plan(b, sq, hs, (int)d, causal ? 1 : 0, fwd_slots_d(d));
+    const flash::Plan p = fwd_plan(b, sq, hs, d, causal ? 1 : 0);
     if (ws_bytes < flash::plan_workspace(p, (int)d))
       return set_error(TPS_EWORKSPACE, "tp_attn_fwd: workspace too small");
     if (d == 64) TPS_TRY(flash_fwd_core<64>(qkv, o, lse_i, ws, p, st));

@@ -1,5 +1,6 @@
 // Flash-style attention forward for one tensor-parallel shard (head dims
-// 64, 128, 256, 512).
+// 64, 256, 512; head dim 128 runs the two-group kernel of flash_fwd_pp.hpp,
+// which shares this file's plan, layouts and merge).
 //
 // Per (batch, head) the queries are cut into blocks of 128 rows; a work item
 // is one query block and a contiguous range of its keys (all of them when the
@@ -93,6 +94,7 @@ struct Shape {
 struct Plan {
   int sq = 0;           // sequence length
   int hs = 0;           // heads of this shard
+  int bq = kBQ;         // query rows per block (128, or 256 for the two-group kernel)
   int nqb = 0;          // query blocks per (batch, head)
   int causal = 0;
   int chunk = 1;        // most iterations (of kBK keys) in one work item
@@ -104,7 +106,7 @@ struct Plan {
 };
 
 __host__ __device__ inline int block_iters(const Plan& p, int i) {
-  const int kend = p.causal ? min(p.sq, (i + 1) * kBQ) : p.sq;
+  const int kend = p.causal ? min(p.sq, (i + 1) * p.bq) : p.sq;
   return (kend + kBK - 1) / kBK;
 }
 __host__ __device__ inline int block_chunks(const Plan& p, int i) {
@@ -500,7 +502,7 @@ __global__ void __launch_bounds__(kMergeThreads) attn_fwd_merge_kernel(const flo
                                                                        Plan p, int total_items, int merges_per_z) {
   constexpr int CH = D / 4;                      // float4 chunks per row
   constexpr int ROWS = kMergeThreads / CH >= 1 ? kMergeThreads / CH : 1;   // rows per workgroup
-  constexpr int GROUPS = kBQ / ROWS;             // workgroups per split block
+  const int GROUPS = p.bq / ROWS;                // workgroups per split block
   const int blk = blockIdx.x / GROUPS;
   const int rg = blockIdx.x - blk * GROUPS;
   const int z = blk / merges_per_z;
@@ -514,20 +516,43 @@ __global__ void __launch_bounds__(kMergeThreads) attn_fwd_merge_kernel(const flo
   const int C = block_chunks(p, i);
   const int first = z * p.items_per_z + base;
   const int zo = z / p.hs, zi = z - zo * p.hs;
-  const float* pml = part + (int64_t)total_items * kBQ * D;
+  const int bq = p.bq;
+  const float* pml = part + (int64_t)total_items * bq * D;
   for (int e = threadIdx.x; e < ROWS * CH; e += kMergeThreads) {
     const int rl = rg * ROWS + e / CH, ch = e % CH;
-    const int row = i * kBQ + rl;
+    const int row = i * bq + rl;
     if (row >= p.sq) continue;
+    // the chunks' loads are issued four at a time (eight for the maxima)
+    // and their terms added in chunk order
+    const float* ml = pml + ((int64_t)first * bq + rl) * 2;   // (m, l) of chunk c at ml + c * 2 bq
+    const float* src = part + ((int64_t)first * bq + rl) * D + 4 * ch;
+    const int64_t cs = (int64_t)bq * D;   // floats between consecutive chunks' partials
     float M = -INFINITY;
-    for (int c = 0; c < C; ++c) M = fmaxf(M, pml[((int64_t)(first + c) * kBQ + rl) * 2]);
+    for (int c0 = 0; c0 < C; c0 += 8) {
+      float mc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mc[j] = c0 + j < C ? ml[(int64_t)(c0 + j) * 2 * bq] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, mc[j]);
+    }
     float L = 0.f;
     f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < C; ++c) {
-      const float mc = pml[((int64_t)(first + c) * kBQ + rl) * 2];
-      const float w = mc == -INFINITY ? 0.f : exp2f(mc - M);
-      L += w * pml[((int64_t)(first + c) * kBQ + rl) * 2 + 1];
-      o += w * *reinterpret_cast<const f32x4_t*>(part + ((int64_t)(first + c) * kBQ + rl) * D + 4 * ch);
+    for (int c0 = 0; c0 < C; c0 += 4) {
+      float2 mlc[4];
+      f32x4_t oc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = min(c0 + j, C - 1);
+        mlc[j] = *reinterpret_cast<const float2*>(ml + (int64_t)c * 2 * bq);
+        oc[j] = *reinterpret_cast<const f32x4_t*>(src + c * cs);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c0 + j >= C) break;
+        const float w = mlc[j].x == -INFINITY ? 0.f : exp2f(mlc[j].x - M);
+        L += w * mlc[j].y;
+        o += w * oc[j];
+      }
     }
     const float inv = 1.f / L;
     bf16_t* dst = O + ((int64_t)zo * p.sq + row) * p.ldo + (int64_t)zi * D + 4 * ch;
@@ -536,18 +561,20 @@ __global__ void __launch_bounds__(kMergeThreads) attn_fwd_merge_kernel(const flo
   }
 }
 
+// merge workgroups per split block of bq rows
 template <int D>
-constexpr int merge_groups() {
-  return kBQ / (kMergeThreads / (D / 4) >= 1 ? kMergeThreads / (D / 4) : 1);
+constexpr int merge_groups(int bq) {
+  return bq / (kMergeThreads / (D / 4) >= 1 ? kMergeThreads / (D / 4) : 1);
 }
 
 // Host: the plan for a call.  The chunk length minimises (rounds of
 // `cus` items) x (iterations per item), preferring longer chunks on ties.
-inline Plan make_plan(int64_t b, int64_t sq, int64_t hs, int d, int causal, int cus) {
+inline Plan make_plan(int64_t b, int64_t sq, int64_t hs, int d, int causal, int cus, int bq = kBQ) {
   Plan p;
   p.sq = (int)sq;
   p.hs = (int)hs;
-  p.nqb = (int)((sq + kBQ - 1) / kBQ);
+  p.bq = bq;
+  p.nqb = (int)((sq + bq - 1) / bq);
   p.causal = causal;
   p.nz = (int)(b * hs);
   p.ld = 3 * hs * d;
@@ -588,7 +615,7 @@ inline int plan_merges_per_z(const Plan& p) {
 
 inline size_t plan_workspace(const Plan& p, int d) {
   const int64_t items = (int64_t)p.items_per_z * p.nz;
-  return (size_t)items * kBQ * (d + 2) * sizeof(float);
+  return (size_t)items * p.bq * (d + 2) * sizeof(float);
 }
 
 }  // namespace flash

@@ -44,6 +44,11 @@ def _weights(inp, hs, d):
     (205, 2, 333, 128, 1, 512, False),    # the same path, non-causal, batch 2
     (207, 1, 4200, 128, 1, 512, False),   # head dim 512 past 4096 positions: flash (16-row waves, rotated LDS rows)
     (208, 1, 4100, 128, 1, 512, True),    # the same, causal, ragged last block
+    (209, 1, 1100, 256, 2, 128, False),   # two-group kernel (256-row items): non-causal, split, ragged
+    (210, 1, 300, 128, 2, 64, False),     # head dim 64 non-causal: one full and one short 256-row span
+    (211, 3, 77, 128, 2, 128, True),      # shorter than one block, ragged last tile, batch 3
+    (212, 1, 2600, 128, 1, 128, True),    # causal, many split blocks, ragged
+    (213, 2, 513, 128, 1, 64, True),      # one row past two blocks, batch 2
 ])
 def test_flash_forward_matches_oracle(tp, w, b, sq, h, hs, d, causal):
     say(f"flash forward b={b} sq={sq} h={h} hs={hs} d={d} causal={causal}")
@@ -64,20 +69,23 @@ def test_flash_forward_matches_oracle(tp, w, b, sq, h, hs, d, causal):
     assert el <= 1e-2 * max(1.0, np.max(np.abs(lse_r)))
 
 
-def test_flash_forward_long_sequence_sampled_rows(tp):
-    """sq = 8192 with two heads of 512: the workspace stays O(s d) and
-    sampled rows (block, chunk and sequence ends) match the oracle's
-    definition computed row by row from the same bf16 QKV."""
-    b, sq, h, hs, d = 1, 8192, 512, 2, 512
+@pytest.mark.parametrize("d", [512, 128])
+def test_flash_forward_long_sequence_sampled_rows(tp, d):
+    """sq = 8192 with two heads of 512 (one-group kernel) or of 128 (the
+    two-group kernel, at the benchmark's attention shape): the workspace
+    stays O(s d) and sampled rows (block, chunk and sequence ends) match the
+    oracle's definition computed row by row from the same bf16 QKV."""
+    b, sq, h, hs = 1, 8192, 512, 2
     ws = tp.tp_attn_fwd_workspace(torch.bfloat16, b, sq, h, hs, d)
     scores_bytes = b * hs * sq * sq * (4 + 2)    # fp32 scores + bf16 probabilities per head
-    # 128-row items of fp32 partial outputs: about one per CU, at least one per query block
-    bound = 2 * max(256, b * hs * sq // 128) * 128 * (d + 2) * 4
+    # fp32 partial outputs of items of at most 256 rows: about one round of
+    # items (at most 256 x 256 rows), at least one item per query block
+    bound = 2 * max(256 * 256, b * hs * sq) * (d + 2) * 4
     print(f"  workspace {ws / 2**20:.1f} MiB (bound {bound / 2**20:.1f}; stored scores would be "
           f"{scores_bytes / 2**20:.0f} MiB)", flush=True)
     assert ws <= bound and ws < scores_bytes // 10
     say(f"flash forward long sequence b={b} sq={sq} h={h} hs={hs} d={d}")
-    inp = synth.attn_inputs(206, b * sq, h, hs, d, "bf16")
+    inp = synth.attn_inputs(206 if d == 512 else 214, b * sq, h, hs, d, "bf16")
     Wqkv, Wo = _weights(inp, hs, d)
     M = b * sq
     QKV, Ob = empty((M, 3 * hs * d), torch.bfloat16), empty((M, hs * d), torch.bfloat16)
