@@ -522,20 +522,13 @@ __global__ void __launch_bounds__(kMergeThreads) attn_fwd_merge_kernel(const flo
     const int rl = rg * ROWS + e / CH, ch = e % CH;
     const int row = i * bq + rl;
     if (row >= p.sq) continue;
-    // the chunks' loads are issued four at a time (eight for the maxima)
-    // and their terms added in chunk order
+    // one pass over the chunks, four at a time: the four chunks' (m, l) and
+    // partial O are loaded together, then added in chunk order to a running
+    // sum kept relative to the running max (rescaled when a batch raises it)
     const float* ml = pml + ((int64_t)first * bq + rl) * 2;   // (m, l) of chunk c at ml + c * 2 bq
     const float* src = part + ((int64_t)first * bq + rl) * D + 4 * ch;
     const int64_t cs = (int64_t)bq * D;   // floats between consecutive chunks' partials
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < C; c0 += 8) {
-      float mc[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mc[j] = c0 + j < C ? ml[(int64_t)(c0 + j) * 2 * bq] : -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) M = fmaxf(M, mc[j]);
-    }
-    float L = 0.f;
+    float M = -INFINITY, L = 0.f;
     f32x4_t o = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < C; c0 += 4) {
       float2 mlc[4];
@@ -545,6 +538,16 @@ __global__ void __launch_bounds__(kMergeThreads) attn_fwd_merge_kernel(const flo
         const int c = min(c0 + j, C - 1);
         mlc[j] = *reinterpret_cast<const float2*>(ml + (int64_t)c * 2 * bq);
         oc[j] = *reinterpret_cast<const f32x4_t*>(src + c * cs);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + j < C) Mb = fmaxf(Mb, mlc[j].x);
+      if (Mb > M) {   // -inf > -inf is false: nothing accumulated while every max is -inf
+        const float r = M == -INFINITY ? 0.f : exp2f(M - Mb);
+        L *= r;
+        o *= r;
+        M = Mb;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
