@@ -419,20 +419,16 @@ static int blocks_per_cu(K kernel, int threads) {
   return n;
 }
 
-// Work items the flash forward plans for.  Head dim 128 runs the two-group
-// kernel (256-row items, eight waves): CUs times its workgroups per CU (one).
-// The other head dims run the one-group kernel (128-row items): CUs times
-// its workgroups per CU, so that a wave of one item can run its softmax
-// while another's MFMAs run on the same SIMD; at most two per CU from head
-// dim 256 on, where the partials of the extra split blocks cost the merge
-// more than a third workgroup gains.  At head dim 64 the two-group kernel
-// is slower (63.6 against 45.2 us for 2 x 16 heads at s = 2048): its
-// products are half of head dim 128's while its softmax is the same, and it
-// holds one workgroup per CU where the one-group kernel holds three or four.
-static bool fwd_two_group(int64_t d) { return d == 128; }
+// Work items the flash forward plans for.  Head dims 64 and 128 run the
+// two-group kernel (256-row items, eight waves): CUs times its workgroups
+// per CU (two at head dim 64, whose waves fit 128 registers; one at 128).
+// Head dims 256 and 512 run the one-group kernel (128-row items): CUs times
+// its workgroups per CU, at most two, where the partials of the extra split
+// blocks cost the merge more than a third workgroup gains.
+static bool fwd_two_group(int64_t d) { return d == 64 || d == 128; }
 template <int D>
 static int fwd_slots() {
-  if constexpr (D == 128) {
+  if constexpr (D <= 128) {
     static const int per_cu = blocks_per_cu(flash::attn_fwd_pp_kernel<D>, flash::PPShape<D>::THREADS);
     return device_cus() * per_cu;
   } else {
@@ -474,7 +470,7 @@ static tps_status flash_fwd_core(const bf16_t* qkv, bf16_t* o, float* lse, void*
                                  hipStream_t st) {
   const int total = p.items_per_z * p.nz;
   float* part = static_cast<float*>(ws);
-  if constexpr (D == 128) {
+  if constexpr (D <= 128) {
     TraceScope trace_(st, "attn_fwd_pp_kernel");
     hipLaunchKernelGGL((flash::attn_fwd_pp_kernel<D>), dim3((unsigned)total), dim3(flash::PPShape<D>::THREADS), 0,
                        st, qkv, o, lse, part, p, total);

@@ -1,6 +1,6 @@
 // Flash-style attention forward for one tensor-parallel shard (head dims
-// 64, 256, 512; head dim 128 runs the two-group kernel of flash_fwd_pp.hpp,
-// which shares this file's plan, layouts and merge).
+// 256 and 512; head dims 64 and 128 run the two-group kernel of
+// flash_fwd_pp.hpp, which shares this file's plan, layouts and merge).
 //
 // Per (batch, head) the queries are cut into blocks of 128 rows; a work item
 // is one query block and a contiguous range of its keys (all of them when the

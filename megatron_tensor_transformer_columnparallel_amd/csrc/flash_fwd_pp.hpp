@@ -1,4 +1,4 @@
-// Two-group flash attention forward (head dim 128).
+// Two-group flash attention forward (head dims 64 and 128).
 //
 // The same method as attn_fwd_flash_kernel (S = Q K^T, online softmax in
 // the log2 domain, O += P V with P taken straight from the S accumulators;
@@ -78,8 +78,10 @@ __device__ __forceinline__ float lane_vmax32(float v) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Head dim 64: two workgroups per CU (four waves per SIMD, 120 registers,
+// fragments one step ahead); head dim 128: one (190 registers).
 template <int D>
-__global__ void __launch_bounds__(PPShape<D>::THREADS)
+__global__ void __launch_bounds__(PPShape<D>::THREADS, (D <= 64 ? 2 : 1))
 attn_fwd_pp_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, float* __restrict__ lse,
                    float* __restrict__ part, Plan p, int total_items) {
   using S = PPShape<D>;
@@ -204,12 +206,12 @@ attn_fwd_pp_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, float
     // step x: the two P V MFMAs of column block x (if any) and the two S
     // MFMAs of k-step x / 2, key half x % 2, so that consecutive MFMAs on one
     // S accumulator are eight apart; the fragments of step x + 2 are read
-    // during step x.  The row sums of P go first (their operands are in
+    // during step x (x + 1 at head dim 64).  The row sums of P go first (their operands are in
     // registers).
 #pragma unroll
     for (int b = 0; b < 2; ++b) lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[b], lacc[b], 0, 0, 0);
     constexpr int NX = 2 * S::KS > S::NB ? 2 * S::KS : S::NB;
-    constexpr int PF = 2;
+    constexpr int PF = D <= 64 ? 1 : 2;
     bf16x8_t vq[NX + PF], kq[NX + PF];
 #pragma unroll
     for (int x = 0; x < PF; ++x) {
