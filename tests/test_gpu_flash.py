@@ -49,6 +49,8 @@ def _weights(inp, hs, d):
     (211, 3, 77, 128, 2, 128, True),      # shorter than one block, ragged last tile, batch 3
     (212, 1, 2600, 128, 1, 128, True),    # causal, many split blocks, ragged
     (213, 2, 513, 128, 1, 64, True),      # one row past two blocks, batch 2
+    (215, 8, 1024, 128, 16, 128, False),  # 512 whole 256-row blocks: more items than one round
+    (216, 16, 1024, 128, 16, 64, True),   # the same at head dim 64 (two workgroups per CU), causal
 ])
 def test_flash_forward_matches_oracle(tp, w, b, sq, h, hs, d, causal):
     say(f"flash forward b={b} sq={sq} h={h} hs={hs} d={d} causal={causal}")
