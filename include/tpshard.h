@@ -128,9 +128,9 @@ tps_status tp_mlp_bwd(tps_dtype dt, int64_t M, int64_t h, int64_t f_i,
  *   Z_i    [b*sq x h]     output: this shard's partial
  *   ws     caller scratch of at least tp_attn_fwd_workspace(...) bytes
  *          (16-byte aligned), free again when the stream has passed the
- *          call.  Head dims 64, 128, 256 (and 512 past 4096 positions) take
- *          the flash kernel: fp32 partial outputs of split query blocks,
- *          about one 128 x d block per compute unit (O(sq d), covering the
+ *          call.  Head dims 64, 128, 256 and 512 take the flash kernels:
+ *          fp32 partial outputs of split query blocks, about one block of
+ *          128 or 256 rows x d per compute unit (O(sq d), covering the
  *          causal and the non-causal plan).  Other head dims keep the scores
  *          and probabilities of every (batch, head), b*hs*sq*round_up(sq, 8)*6
  *          bytes.

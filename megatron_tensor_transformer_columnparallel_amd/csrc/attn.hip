@@ -376,19 +376,18 @@ static tps_status attn_checks(const char* fn, tps_dtype dt, int64_t b, int64_t s
 
 using namespace tps;
 
-// Which forward core a call takes.  The flash kernel is compiled for head
-// dims 64..512.  Up to 256 each wave keeps 32 query rows (Q fragments and
-// the fp32 output accumulator fit one wave's registers), and every K or V
-// fragment read from LDS feeds two MFMAs.  At 512 a wave can keep only 16
-// rows, so each fragment feeds one MFMA and the kernel is bound by LDS
-// bandwidth: at sq = 2048 with 4 heads it took 55 us plus 26 us to merge the
-// key chunks, against 61 us for the score GEMM, row softmax and PV GEMM.  So
-// head dim 512 takes the flash kernel only past sq = 4096, where the stored
-// scores and probabilities (6 bytes per query-key pair and head) would need
-// gigabytes.
+// Which forward core a call takes: the flash kernels for head dims 64, 128,
+// 256 and 512 at every sequence length; other head dims (multiples of 8)
+// take the score GEMM, row softmax and PV GEMM.  Up to 256 each wave keeps
+// 32 query rows (Q fragments and the fp32 output accumulator fit one wave's
+// registers), and every K or V fragment read from LDS feeds two MFMAs.  At
+// 512 a wave can keep only 16 rows, so each fragment feeds one MFMA and the
+// kernel is bound by LDS bandwidth; with the merge's single pass it still
+// beats the score path at sq = 2048 with 4 heads (48.2 + 16.1 us against
+// 68.0 us) and keeps the workspace O(sq d).
 static bool use_flash(int64_t d, int64_t sq) {
-  if (d == 64 || d == 128 || d == 256) return true;
-  return d == 512 && sq > 4096;
+  (void)sq;
+  return d == 64 || d == 128 || d == 256 || d == 512;
 }
 
 // Which backward core: the flash kernels are compiled for head dims 64..256

@@ -160,23 +160,24 @@ def test_workspace_queries_and_too_small_workspace(tp):
     for causal in (0, 1):
         st = lib.tp_attn_bwd(1, 1, 300, 4096, 2, 64, causal, *([ALIGNED] * 11), small, None)
         assert st == tp.binding.TPS_EWORKSPACE
-    # forward through the flash kernel (head dims up to 256, and 512 past 4096
-    # positions): fp32 partial outputs of the key chunks, about one 128-row
-    # item per compute unit whatever the sequence length (no per-(query, key)
+    # forward through the flash kernels (head dims 64, 128, 256, 512): fp32
+    # partial outputs of the key chunks, about one item of at most 256 rows
+    # per compute unit whatever the sequence length (no per-(query, key)
     # storage)
-    def bound(b, sq, hs, d):   # 128-row items: about one per CU, at least one per query block
-        return 2 * max(256, b * hs * -(-sq // 128)) * 128 * (d + 2) * 4
+    def bound(b, sq, hs, d):   # about one round of items, at least one per 128-row query block
+        return 2 * max(256 * 256, b * hs * -(-sq // 128) * 128) * (d + 2) * 4
     wf = lib.tp_attn_fwd_workspace(1, 1, 8192, 4096, 4, 512)
     assert 0 < wf <= bound(1, 8192, 4, 512)
     assert lib.tp_attn_fwd_workspace(1, 1, 32768, 4096, 4, 512) <= bound(1, 32768, 4, 512) < 4 * 32768 ** 2
     assert 0 < lib.tp_attn_fwd_workspace(1, 1, 2048, 1024, 4, 256) <= bound(1, 2048, 4, 256)
     st = lib.tp_attn_fwd(1, 1, 8192, 4096, 4, 512, 1, *([ALIGNED] * 8), wf - 1, None)
     assert st == tp.binding.TPS_EWORKSPACE
-    # other calls: fp32 log2-domain scores + bf16 probabilities per (batch, head)
-    wo = lib.tp_attn_fwd_workspace(1, 1, 2048, 4096, 4, 512)
+    assert 0 < lib.tp_attn_fwd_workspace(1, 1, 2048, 4096, 4, 512) <= bound(1, 2048, 4, 512)
+    # other head dims: fp32 log2-domain scores + bf16 probabilities per (batch, head)
+    wo = lib.tp_attn_fwd_workspace(1, 1, 2048, 4096, 4, 96)
     assert wo >= 4 * 2048 * 2048 * (4 + 2)
     assert lib.tp_attn_fwd_workspace(1, 1, 300, 480, 5, 96) >= 5 * 300 * 304 * (4 + 2)
-    st = lib.tp_attn_fwd(1, 1, 2048, 4096, 4, 512, 1, *([ALIGNED] * 8), wo - 1, None)
+    st = lib.tp_attn_fwd(1, 1, 2048, 4096, 4, 96, 1, *([ALIGNED] * 8), wo - 1, None)
     assert st == tp.binding.TPS_EWORKSPACE
 
 

@@ -1,10 +1,9 @@
 """GPU parity of the flash-style attention kernels.
 
 Forward: O and the log-sum-exp against the fp64 oracle, at sizes where the
-work is split into key chunks (the merge path), for head dims 64, 128 and
-256 and for head dim 512 past 4096 positions (shorter sequences at 512 take
-the score / softmax / PV path, also checked here), and at a sequence of
-8192 whose score matrix is never stored (sampled rows, checked one by one).
+work is split into key chunks (the merge path), for head dims 64, 128, 256
+and 512, and at a sequence of 8192 whose score matrix is never stored
+(sampled rows, checked one by one).
 
 Backward (head dims 64, 128, 256): dX, dW_QKV (its Q, K and V column blocks
 separately) and dW_O against the oracle at sizes spanning several 128-row
@@ -40,9 +39,9 @@ def _weights(inp, hs, d):
     (201, 1, 1100, 256, 2, 64, True),     # ragged rows and keys, many 64-key chunks
     (202, 2, 700, 256, 3, 128, True),     # batch 2, 3 heads
     (203, 1, 1100, 256, 2, 256, False),   # non-causal: every block split
-    (204, 1, 1100, 256, 2, 512, True),    # head dim 512, short: score / softmax / PV path
-    (205, 2, 333, 128, 1, 512, False),    # the same path, non-causal, batch 2
-    (207, 1, 4200, 128, 1, 512, False),   # head dim 512 past 4096 positions: flash (16-row waves, rotated LDS rows)
+    (204, 1, 1100, 256, 2, 512, True),    # head dim 512 (16-row waves, rotated LDS rows), short
+    (205, 2, 333, 128, 1, 512, False),    # the same, non-causal, batch 2
+    (207, 1, 4200, 128, 1, 512, False),   # head dim 512 past 4096 positions
     (208, 1, 4100, 128, 1, 512, True),    # the same, causal, ragged last block
     (209, 1, 1100, 256, 2, 128, False),   # two-group kernel (256-row items): non-causal, split, ragged
     (210, 1, 300, 128, 2, 64, False),     # head dim 64 non-causal: one full and one short 256-row span

@@ -34,15 +34,14 @@ def build_model(w, shape, ln_random):
 # The storage points of the library's stacked model, for the oracle's bf16
 # storage mode: every product reads bf16 operands and stores bf16 results;
 # the softmax backward recomputes P from the log-sum-exp and takes its row
-# term from the P that forms dS.  At head dims 64-256 the attention runs in
-# the flash kernels: the forward normalises O once at the end of its pass
-# over the keys (it rounds the unnormalised probabilities), and the backward
-# forms dS from the fp32 P.  At head dim 512 (up to 4096 positions) the
-# forward rounds the normalised probabilities and dS is formed from the
-# stored bf16 P.
+# term from the P that forms dS.  The forward runs in the flash kernels at
+# head dims 64-512: it normalises O once at the end of its pass over the
+# keys (it rounds the unnormalised probabilities).  The backward forms dS
+# from the fp32 P at head dims 64-256 (flash) and from the stored bf16 P at
+# 512.
 def storage_model(d, s):
     from oracle import bf16_storage as B
-    fwd_flash = d in (64, 128, 256) or (d == 512 and s > 4096)
+    fwd_flash = d in (64, 128, 256, 512)
     bwd_flash = d in (64, 128, 256)
     points = [p for p in B.POINTS if not (bwd_flash and p == "p_ds")]
     return B.Rounding(points, delta="p", p_fwd_form="unnormalised" if fwd_flash else "normalised")
