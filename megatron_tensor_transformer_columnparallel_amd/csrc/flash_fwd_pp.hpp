@@ -30,6 +30,8 @@
 // 128-row kernel with 256-row blocks (Plan::bq = 256).
 #pragma once
 
+#include <type_traits>
+
 #include "flash_attn.hpp"
 
 namespace tps {
@@ -177,12 +179,13 @@ attn_fwd_pp_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, float
   // keys of tile t all after the wave's last row: nothing to add
   auto live = [&](int t) { return !p.causal || kb0 + t * kBK <= q0 + 31; };
 
-  // products of round j: O += P(j-1) V(j-1), then S(j) = Q K(j)^T.  Both
-  // run in every round (straight-line code keeps the accumulators in place):
-  // P is zero before the first tile and for a tile whose keys all follow the
-  // wave's rows, and the scores of round n are never used (the stage then
-  // holds clamped tiles of the item).
-  auto products = [&](int stage) {
+  // products of round j: O += P(j-1) V(j-1) (from round 1 on), then
+  // S(j) = Q K(j)^T (up to round n - 1).  The first and last rounds are
+  // peeled, so each instance is straight-line code that keeps the
+  // accumulators in place; P is zero for a tile whose keys all follow the
+  // wave's rows.
+  auto products = [&](int stage, auto do_pv, auto do_s) {
+    constexpr bool PV = decltype(do_pv)::value, SC = decltype(do_s)::value;
     // the product phase issues at raised priority, so that on its SIMD the
     // other group's softmax fills the issue slots the MFMAs leave free
     __builtin_amdgcn_s_setprio(1);
@@ -201,36 +204,37 @@ attn_fwd_pp_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, float
     auto kread = [&](int x) {
       return *reinterpret_cast<const bf16x8_t*>(Kt + L::koff(16 * (x & 1) + r16, 4 * (x >> 1) + g));
     };
-#pragma unroll
-    for (int b = 0; b < 2; ++b) s[b][0] = s[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // step x: the two P V MFMAs of column block x (if any) and the two S
     // MFMAs of k-step x / 2, key half x % 2, so that consecutive MFMAs on one
     // S accumulator are eight apart; the fragments of step x + 2 are read
     // during step x (x + 1 at head dim 64).  The row sums of P go first (their operands are in
     // registers).
+    if constexpr (PV) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[b], lacc[b], 0, 0, 0);
+      for (int b = 0; b < 2; ++b) lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[b], lacc[b], 0, 0, 0);
+    }
     constexpr int NX = 2 * S::KS > S::NB ? 2 * S::KS : S::NB;
     constexpr int PF = D <= 64 ? 1 : 2;
     bf16x8_t vq[NX + PF], kq[NX + PF];
 #pragma unroll
     for (int x = 0; x < PF; ++x) {
-      if (x < S::NB) vq[x] = vread(x);
-      if (x < 2 * S::KS) kq[x] = kread(x);
+      if (PV && x < S::NB) vq[x] = vread(x);
+      if (SC && x < 2 * S::KS) kq[x] = kread(x);
     }
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-      if (x + PF < S::NB) vq[x + PF] = vread(x + PF);
-      if (x + PF < 2 * S::KS) kq[x + PF] = kread(x + PF);
-      if (x < S::NB) {
+      if (PV && x + PF < S::NB) vq[x + PF] = vread(x + PF);
+      if (SC && x + PF < 2 * S::KS) kq[x + PF] = kread(x + PF);
+      if (PV && x < S::NB) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           acc[b][x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vq[x], pf[b], acc[b][x], 0, 0, 0);
       }
-      if (x < 2 * S::KS) {
+      if (SC && x < 2 * S::KS) {
+        const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};   // the first k-step starts the chains
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          s[b][x & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[x], qf[b][x >> 1], s[b][x & 1], 0, 0, 0);
+          s[b][x & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kq[x], qf[b][x >> 1], x < 2 ? zero : s[b][x & 1], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -304,26 +308,49 @@ attn_fwd_pp_kernel(const bf16_t* __restrict__ qkv, bf16_t* __restrict__ O, float
     else wait_vmem();
     pp_barrier();
   };
+  const std::true_type yes{};
+  const std::false_type no{};
+  auto advance = [&]() {
+    stage = stage == kPPStages - 1 ? 0 : stage + 1;
+    stage2 = stage2 == kPPStages - 1 ? 0 : stage2 + 1;
+  };
+  // rounds 0 (S only), 1 .. n - 1, n (P V only); n >= 1
   if (grp == 0) {
-    for (int j = 0; j <= n; ++j) {
+    if (2 <= n) issue(2, stage2);
+    products(stage, no, yes);
+    pp_barrier();
+    softmax(0);
+    round_end(0);
+    advance();
+    for (int j = 1; j < n; ++j) {
       if (j + 2 <= n) issue(j + 2, stage2);
-      products(stage);
+      products(stage, yes, yes);
       pp_barrier();
       softmax(j);
       round_end(j);
-      stage = stage == kPPStages - 1 ? 0 : stage + 1;
-      stage2 = stage2 == kPPStages - 1 ? 0 : stage2 + 1;
+      advance();
     }
+    products(stage, yes, no);
+    pp_barrier();
+    round_end(n);
   } else {
-    for (int j = 0; j <= n; ++j) {
+    if (2 <= n) issue(2, stage2);
+    pp_barrier();
+    products(stage, no, yes);
+    round_end(0);
+    advance();
+    for (int j = 1; j < n; ++j) {
       if (j + 2 <= n) issue(j + 2, stage2);
       softmax(j - 1);
       pp_barrier();
-      products(stage);
+      products(stage, yes, yes);
       round_end(j);
-      stage = stage == kPPStages - 1 ? 0 : stage + 1;
-      stage2 = stage2 == kPPStages - 1 ? 0 : stage2 + 1;
+      advance();
     }
+    softmax(n - 1);
+    pp_barrier();
+    products(stage, yes, no);
+    round_end(n);
   }
 
   // row sums (every lane of a query holds its row's sum)
