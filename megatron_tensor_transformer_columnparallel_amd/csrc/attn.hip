@@ -707,6 +707,7 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   s.sa_o = sq * w3; s.sa_i = d; s.sb_o = sq * w3; s.sb_i = d;
   s.skip_upper = causal ? 1 : 0;
   s.skip_pad = kProbPad;   // P: zeros up to the causal pad, nothing beyond
+  s.live_tiles = 1;        // tile shape by the live tiles: every CU shares the exp epilogue
   // P = exp(Q K^T * scale - lse)           (NT)  [sq x sq] per head
   TPS_TRY((gemm_bf16<true, true>(qkv, qkv + w, s,
                                  EpiAttnProb<bf16_t>{P, lse_i, ldp, sp, (int)sq, (int)hs, causal ? 1 : 0,
@@ -716,6 +717,7 @@ extern "C" tps_status tp_attn_bwd(tps_dtype dt, int64_t b, int64_t sq, int64_t h
   GemmShape s2 = s;
   s2.lda = w; s2.sa_o = sq * w; s2.sa_i = d;
   s2.skip_pad = 1;   // dP is read only up to the diagonal
+  s2.live_tiles = 0;
   TPS_TRY((gemm_bf16<true, true>(dO, qkv + 2 * w, s2, EpiStore<float>{dP, ldp, hs * sp, sp}, st)));
   // dS = P * (dP - delta) * scale with delta from the same P and dP
   TPS_TRY(([&]() {

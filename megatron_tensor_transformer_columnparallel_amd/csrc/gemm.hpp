@@ -38,6 +38,10 @@ struct GemmShape {
   // at all (no epilogue): an output that only has to be written up to that
   // limit (1: the diagonal; 256: a zero pad to the next multiple of 256).
   int skip_pad = 0;
+  // live_tiles: with skip_upper and skip_pad > 0, the tile shape is chosen by
+  // the tiles that compute rather than by the whole grid (for an epilogue
+  // heavy enough that every CU should share it; see gemm_bf16).
+  int live_tiles = 0;
   int group_m = 8;  // tile rows per group in the tile order (8 measured best for M = 2048)
   // groups = 2: a second problem (GemmAlt) with this same shape, layout,
   // batch and K ranges runs in the same launch.
@@ -810,6 +814,11 @@ inline GemmAlt<Epi> no_alt(const Epi& e) {
 //     fewer than half of the CUs (64..127 tiles): twice the tiles (the
 //     tied-logits leftover 2048x553x4096 NT: 28.9 -> 22.0 us);
 //   64x64 for problems too small for 64 tiles of 128x128.
+// Causal problems with live_tiles count only the tiles that compute: the
+// attention probabilities P = exp(S - lse) at 4 heads x 2048 (head dim 512)
+// have 144 live tiles of 256x256 (112 CUs idle through the exp epilogue) and
+// 544 of 128x128, which take 32.0 us against 37.8; a plain fp32 store of the
+// same shape (dP) is faster on the 256x256 grid (29.5 against 34.4 us).
 // Longest-first (lpt) launches always take 128x128 with three stages: one
 // workgroup per CU, so the CUs that finish short tiles pick up the next
 // ones (dV and dK together: 57.6 -> 39.2 us against two launches).
@@ -817,10 +826,24 @@ inline GemmAlt<Epi> no_alt(const Epi& e) {
 // 256x256 grid does not fill whole rounds but a 256x192 grid with no edge
 // tiles does (2048x6144x4096 NN: 118 -> 107 us; 4096x6144x2048 TN: 120 us at
 // 128x128 -> 116 us).
+// Tiles of BM x BN that the dispatch counts: the whole grid, or with
+// live_tiles (and skip_upper, skip_pad > 0) only the tiles before the causal
+// limit rounded up to skip_pad; the others leave at once and occupy no CU.
+inline int64_t tile_count(const GemmShape& s, int64_t BM, int64_t BN) {
+  const int64_t tm = ceil_div(s.M, BM), tn = ceil_div(s.N, BN);
+  if (!(s.live_tiles && s.skip_upper && s.skip_pad > 0)) return tm * tn * (int64_t)s.batch * s.groups;
+  int64_t n = 0;
+  for (int64_t i = 0; i < tm; ++i) {
+    const int64_t mend = std::min<int64_t>((i + 1) * BM, s.M);
+    n += std::min<int64_t>(tn, ceil_div(ceil_div(mend, s.skip_pad) * s.skip_pad, BN));
+  }
+  return n * s.batch * s.groups;
+}
+
 template <bool AK, bool BKC, class Epi>
 inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s, const Epi& epi,
                             const GemmAlt<Epi>& alt, hipStream_t st) {
-  const int64_t t256 = ceil_div(s.M, 256) * ceil_div(s.N, 256) * (int64_t)s.batch * s.groups;
+  const int64_t t256 = tile_count(s, 256, 256);
   // Tail split: a single problem whose 256x256 grid ends in a round at most
   // a quarter full runs as whole rounds of 256x256 tiles plus the leftover
   // columns (or rows) as a second launch with smaller tiles.  Each output
@@ -848,8 +871,8 @@ inline tps_status gemm_bf16(const bf16_t* A, const bf16_t* B, const GemmShape& s
       return gemm_bf16<AK, BKC>(A + (AK ? (int64_t)mm * s.lda : (int64_t)mm), B, b, epi, alt, st);
     }
   }
-  const int64_t t128x256 = ceil_div(s.M, 128) * ceil_div(s.N, 256) * (int64_t)s.batch * s.groups;
-  const int64_t t128 = ceil_div(s.M, 128) * ceil_div(s.N, 128) * (int64_t)s.batch * s.groups;
+  const int64_t t128x256 = tile_count(s, 128, 256);
+  const int64_t t128 = tile_count(s, 128, 128);
   const int64_t t192 = ceil_div(s.M, 256) * ceil_div(s.N, 192) * (int64_t)s.batch * s.groups;
   const bool full192 = s.M % 256 == 0 && s.N % 192 == 0 && t192 > 0 && t192 % 256 == 0;
   if (s.lpt) return launch_mfma<128, 128, 64, 2, 4, 3, AK, BKC>(A, B, s, epi, alt, st);
