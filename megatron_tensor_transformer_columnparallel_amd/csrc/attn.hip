@@ -625,18 +625,12 @@ static tps_status flash_bwd_core(const bf16_t* qkv, const bf16_t* dO, const floa
     TPS_TRY(check_launch("attn_bwd_dkv_kernel"));
   }
   const int mq = flash::work_merges_per_z(wq), mk = flash::work_merges_per_z(wk);
-  if (mq > 0) {
+  const int nq_wg = mq > 0 ? flash::merge_workgroups(wq, mq, flash::merge_rows<D>()) : 0;
+  const int nk_wg = mk > 0 ? flash::merge_workgroups(wk, mk, flash::merge_rows<2 * D>()) : 0;
+  if (nq_wg + nk_wg > 0) {
     TraceScope trace_(st, "attn_bwd_merge_kernel");
-    constexpr int rows = flash::kMergeThreads / (D / 4) >= 1 ? flash::kMergeThreads / (D / 4) : 1;
-    hipLaunchKernelGGL((flash::attn_bwd_merge_kernel<D, false>), dim3((unsigned)(mq * wq.nz * (wq.bb / rows))),
-                       dim3(flash::kMergeThreads), 0, st, qpart, dqkv, p, wq, mq);
-    TPS_TRY(check_launch("attn_bwd_merge_kernel"));
-  }
-  if (mk > 0) {
-    TraceScope trace_(st, "attn_bwd_merge_kernel");
-    constexpr int rows = flash::kMergeThreads / (D / 2) >= 1 ? flash::kMergeThreads / (D / 2) : 1;
-    hipLaunchKernelGGL((flash::attn_bwd_merge_kernel<D, true>), dim3((unsigned)(mk * wk.nz * (wk.bb / rows))),
-                       dim3(flash::kMergeThreads), 0, st, kvpart, dqkv, p, wk, mk);
+    hipLaunchKernelGGL((flash::attn_bwd_merge_kernel<D>), dim3((unsigned)(nq_wg + nk_wg)), dim3(flash::kMergeThreads),
+                       0, st, qpart, kvpart, dqkv, p, wq, mq, wk, mk, nq_wg);
     TPS_TRY(check_launch("attn_bwd_merge_kernel"));
   }
   return TPS_OK;

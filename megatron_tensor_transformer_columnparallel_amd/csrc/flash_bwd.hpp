@@ -703,20 +703,29 @@ attn_bwd_kv_kernel(const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ dO
 }
 
 // ---------------------------------------------------------------- merge
+// Rows of one split block that a merge workgroup covers: one thread per
+// (row, 4 of the W columns), W = D (dQ) or 2 D (dK then dV).
+template <int W>
+constexpr int merge_rows() {
+  return kMergeThreads / (W / 4) >= 1 ? kMergeThreads / (W / 4) : 1;
+}
+// Workgroups of a merge: every split block of every (batch, head).
+inline int merge_workgroups(const BwdWork& wk, int merges_per_z, int rows) {
+  return merges_per_z * wk.nz * (wk.bb / rows);
+}
+
 // Sum of a split block's chunk partials in chunk order, rounded once to
-// bf16 into dQKV: W = D columns (dQ of head zi) or 2 D (dK then dV).  One
-// thread per (row, 4 columns); a workgroup covers kMergeThreads / (W / 4)
-// rows of one split block.
+// bf16 into dQKV: W = D columns (dQ of head zi) or 2 D (dK then dV).  Merge
+// workgroup `wg` covers merge_rows<W>() rows of one split block.
 template <int D, bool KV>
-__global__ void __launch_bounds__(kMergeThreads) attn_bwd_merge_kernel(const float* __restrict__ part,
-                                                                       bf16_t* __restrict__ dqkv, BwdPlan p,
-                                                                       BwdWork wk, int merges_per_z) {
+__device__ __forceinline__ void bwd_merge_block(const float* __restrict__ part, bf16_t* __restrict__ dqkv,
+                                                const BwdPlan& p, const BwdWork& wk, int merges_per_z, int wg) {
   constexpr int W = KV ? 2 * D : D;
   constexpr int CH = W / 4;
-  constexpr int ROWS = kMergeThreads / CH >= 1 ? kMergeThreads / CH : 1;
+  constexpr int ROWS = merge_rows<W>();
   const int groups = wk.bb / ROWS;
-  const int blk = blockIdx.x / groups;
-  const int rg = blockIdx.x - blk * groups;
+  const int blk = wg / groups;
+  const int rg = wg - blk * groups;
   const int z = blk / merges_per_z;
   const int k = blk - z * merges_per_z;   // k-th split block of this (batch, head), in slot order
   const Located l = wave_locate(wk.nb, k, [&](int s) {
@@ -754,6 +763,21 @@ __global__ void __launch_bounds__(kMergeThreads) attn_bwd_merge_kernel(const flo
     bf16_t* dst = dqkv + ((int64_t)zo * p.sq + row) * p.ld + dcol;
     *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
   }
+}
+
+// Both merges in one launch: workgroups [0, nq_wg) merge the dQ partials
+// (split query blocks), the rest the dK/dV partials (split key blocks).  The
+// two write disjoint columns of dQKV, and each is latency-bound on its own
+// (a few 16-byte loads per thread), so one grid lets them overlap.
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads) attn_bwd_merge_kernel(const float* __restrict__ qpart,
+                                                                       const float* __restrict__ kvpart,
+                                                                       bf16_t* __restrict__ dqkv, BwdPlan p,
+                                                                       BwdWork wq, int mq, BwdWork wk, int mk,
+                                                                       int nq_wg) {
+  const int wg = (int)blockIdx.x;
+  if (wg < nq_wg) bwd_merge_block<D, false>(qpart, dqkv, p, wq, mq, wg);
+  else bwd_merge_block<D, true>(kvpart, dqkv, p, wk, mk, wg - nq_wg);
 }
 
 }  // namespace flash
